@@ -1,0 +1,81 @@
+"""Algorithmic work and traffic of the projected-attention forward (host-side arithmetic).
+
+Work per head, following the cost model of the Sparse Projection Attention page (Sec. 4.1.1,
+dense projection, s = 1) and the time-complexity list of the Projection-Decomposition
+Attention page (Sec. 4.1, steps 1-3 and 5 without the low-rank step):
+
+    project Q and K : 2 * (2 N d m)        = 4 N d m
+    scores          : c * 2 N^2 m
+    weights x V     : c * 2 N^2 dv
+    exponentials    : c * N^2
+
+with c = 1/2 under a causal mask (the N^2 terms are halved; the projection term is not).
+
+Bytes per head of the whole path: read Q, K, V and P once, write O once, and one round trip
+(write plus read) of the projected keys and queries that the projection launch hands to the
+attention launch. The exact-score work the method avoids is never counted.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+
+@dataclass(frozen=True)
+class Work:
+    project_flops: float
+    score_flops: float
+    pv_flops: float
+    exps: float
+
+    @property
+    def attn_flops(self) -> float:
+        """Flops of the attention launch (scores and weights x V)."""
+        return self.score_flops + self.pv_flops
+
+    @property
+    def total_flops(self) -> float:
+        return self.project_flops + self.score_flops + self.pv_flops
+
+
+def work(B: int, H: int, N: int, d: int, m: int, dv: int, causal: bool) -> Work:
+    heads = B * H
+    c = 0.5 if causal else 1.0
+    return Work(project_flops=heads * 4.0 * N * d * m,
+                score_flops=heads * c * 2.0 * N * N * m,
+                pv_flops=heads * c * 2.0 * N * N * dv,
+                exps=heads * c * float(N) * N)
+
+
+def path_bytes(B: int, H: int, N: int, d: int, m: int, dv: int, elem: int = 2,
+               out_elem: int = 2) -> dict[str, float]:
+    """Algorithmic HBM bytes of each launch and of the whole path (see module docstring)."""
+    heads = B * H
+    qk = 2.0 * heads * N * d * elem
+    v = 1.0 * heads * N * dv * elem
+    o = 1.0 * heads * N * dv * out_elem
+    p = 1.0 * H * d * m * elem
+    tilde = 2.0 * heads * N * m * elem  # projected queries and keys
+    project = qk + p + tilde  # read Q, K, P; write Qt, Kt
+    attn = tilde + v + o  # read Qt, Kt, V; write O
+    return {"project": project, "attn": attn, "total": project + attn}
+
+
+def score_speedup(d: int, m: int) -> float:
+    """Score-computation ratio of exact to projected attention, d/m (SPA page Sec. 3.1.3)."""
+    return d / m
+
+
+def asymptotic_speedup(d: int, m: int, dv: int) -> float:
+    """End-to-end ratio as N grows, (d + dv)/(m + dv) (SPA page Sec. 4.1.1)."""
+    return (d + dv) / (m + dv)
+
+
+def materialised_logits_bytes(N: int, bytes_per_logit: int = 4) -> int:
+    """Bytes of one head's N x N logit matrix, which this path never writes."""
+    return N * N * bytes_per_logit
+
+
+# MI355X published peaks used as roofline denominators.
+PEAK_BF16_DENSE_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_FP32_MATRIX_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
