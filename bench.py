@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the projected-attention forward on one MI355X.
+
+One step = one spa_attn_fwd call (projection launch + attention launch) over the headline
+workload, B=2 H=16 N=8192 d=128 m=32 dv=128, causal, bf16 inputs and output, with the inputs
+resident in HBM. Prints one JSON line (see the keys below).
+
+  python bench.py [--steps K] [--warmup W] [--workload c3] [--no-cpu-baseline]
+  python bench.py --calibrate-copy      # a plain 1 GiB device copy, for counter scaling
+
+Flops are algorithmic (the projection 4 N d m, scores 2 N^2 m, weights x V 2 N^2 dv per head,
+the N^2 terms halved under the causal mask); the exact-attention work the method avoids is
+not counted. The dominant kernel's duration comes from HIP events recorded by the library
+around each launch on the launch stream during the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import jl_feature_projected_amd as spa  # noqa: E402
+from jl_feature_projected_amd import accounting, inputs  # noqa: E402
+
+METRIC = "projected-attention fwd TFLOP/s and % bf16 MFMA peak at N=8192,d=128,m=32"
+ATTN_SRC = os.path.join(ROOT, "jl_feature_projected_amd", "csrc", "spa_attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_c3_hbm_traffic.md")
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per attention launch from the committed counter summary, if it was taken on
+    this exact kernel source and workload; otherwise None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel source sha256\[:16\]:\s*`?([0-9a-f]{16})", text)
+    m_wl = re.search(r"workload:\s*`?([\w.-]+)", text)
+    m_b = re.search(r"hbm bytes per launch:\s*`?([0-9.eE+]+)", text)
+    if not (m_hash and m_wl and m_b):
+        return None
+    if m_hash.group(1) != source_hash(ATTN_SRC) or m_wl.group(1) != workload_name:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w: inputs.Workload, x: inputs.Inputs, budget_s: float = 12.0) -> dict:
+    """The CPU oracle timed on a bounded sample of the same workload: whole heads, all rows."""
+    import numpy as np
+
+    import oracle
+
+    BH = w.B * w.H
+    Q = x.Q.reshape(BH, 1, w.N, w.d)
+    K = x.K.reshape(BH, 1, w.N, w.d)
+    V = x.V.reshape(BH, 1, w.N, w.dv)
+    P = x.P.double().numpy()
+
+    def heads(n):
+        # heads 0..n-1 of the flattened (batch, head) axis, each with its own P[h]
+        idx = list(range(n))
+        q = np.concatenate([Q[i:i + 1].double().numpy() for i in idx], axis=1)
+        k = np.concatenate([K[i:i + 1].double().numpy() for i in idx], axis=1)
+        v = np.concatenate([V[i:i + 1].double().numpy() for i in idx], axis=1)
+        p = np.stack([P[i % w.H] for i in idx])
+        return q, k, v, p
+
+    q, k, v, p = heads(1)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, p, w.scale, w.causal)
+    t1 = time.perf_counter() - t0
+    n = max(1, min(BH, int(budget_s / max(t1, 1e-3))))
+    if n > 1:
+        q, k, v, p = heads(n)
+        t0 = time.perf_counter()
+        oracle.attn_fwd(q, k, v, p, w.scale, w.causal)
+        t1 = time.perf_counter() - t0
+    flops = accounting.work(1, n, w.N, w.d, w.m, w.dv, w.causal).total_flops
+    return {"value": round(flops / t1 / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{n} of {BH} heads, all {w.N} rows each ({flops / 1e9:.1f} GFLOP, "
+                      f"{t1:.2f} s, float64)"}
+
+
+def calibrate_copy(dev) -> None:
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "copies": 3}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every (batch, head) is independent and this build "
+              "has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(dev)
+        return 0
+
+    w = inputs.WORKLOADS[args.workload]
+    x = inputs.draw(w)
+    Q, K, V, P = (t.to(dev) for t in (x.Q, x.K, x.V, x.P))
+    out_dtype = w.torch_dtype
+    O = torch.empty((w.B, w.H, w.N, w.dv), dtype=out_dtype, device=dev)
+    ws = torch.empty(spa.spa_attn_fwd_workspace_bytes(w.B, w.H, w.N, w.d, w.m, w.dv, w.torch_dtype),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        spa.spa_attn_fwd(Q, K, V, P, w.scale, w.causal, out=O, workspace=ws, out_dtype=out_dtype)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spa.profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    proj_ms, attn_ms, calls = spa.profile_end()
+    ev_ms = ev0.elapsed_time(ev1)
+
+    work = accounting.work(w.B, w.H, w.N, w.d, w.m, w.dv, w.causal)
+    ms_per_step = max(wall * 1e3, ev_ms) / args.steps
+    value = work.total_flops / (ms_per_step * 1e-3) / 1e12
+    peak = accounting.PEAK_BF16_DENSE_TFLOPS if w.dtype == "bf16" else accounting.PEAK_FP32_MATRIX_TFLOPS
+    attn_avg_ms = attn_ms / calls
+    achieved = work.attn_flops / (attn_avg_ms * 1e-3) / 1e12
+    bytes_ = accounting.path_bytes(w.B, w.H, w.N, w.d, w.m, w.dv,
+                                   elem=2 if w.dtype == "bf16" else 4,
+                                   out_elem=2 if w.dtype == "bf16" else 4)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "m": w.m,
+                   "dv": w.dv, "causal": w.causal, "out_dtype": w.dtype,
+                   "flops_per_step": work.total_flops},
+        "pct_of_bf16_peak": round(100.0 * value / accounting.PEAK_BF16_DENSE_TFLOPS, 2),
+        "launch_ms": {"project": round(proj_ms / calls, 5), "attn": round(attn_avg_ms, 5)},
+        "roofline": {
+            "kernel": "attn_bf16_kernel" if w.dtype == "bf16" else "attn_f32_kernel",
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(w.name),
+            "algorithmic_bytes": bytes_["attn"],
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,135 @@
+/*
+ * spa.h -- C ABI of libspa: feature-axis projected softmax attention on MI355X (gfx950).
+ *
+ * The operation (per batch b and head h, with one projection P_h in R^{d x m} shared by
+ * queries and keys):
+ *
+ *     Qt = Q P_h,  Kt = K P_h                                   (projection)
+ *     O  = softmax_rows( scale * Qt Kt^T  [+ causal mask] ) V   (attention)
+ *
+ * Sources: "Sparse Projection Attention: A Computationally Efficient Framework for Long
+ * Sequence Modeling", Sec. 3.1.2-3.1.3 and Algorithm 1 (project queries and keys with one
+ * shared matrix, score in the projected space, softmax, multiply by V); "Projection-
+ * Decomposition Attention (PDA)", Algorithm 2.1 steps 1-3 and 5 (Gaussian P with N(0, 1/m)
+ * entries; the low-rank step 4 is not part of this library) and Sec. 4.2 (the score matrix
+ * can be streamed and is never stored). The N x N score matrix is never written to memory.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, contiguous and row-major. Q, K: [B,H,N,d]; V, O: [B,H,N,dv];
+ *     P: [H,d,m] (one d x m matrix per head; a projection shared by all heads is passed as H
+ *     identical copies); projected tensors: [B,H,N,m]; lse: [B,H,N].
+ *   - Tensor pointers are DEVICE pointers. Base addresses must be 16-byte aligned (lse:
+ *     4-byte aligned). The caller owns every buffer; the library keeps no pointer after a
+ *     call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls are asynchronous and
+ *     stream-ordered: a returned SPA_OK means the work was enqueued, not that it finished.
+ *   - Errors are reported only through the returned status; nothing aborts or throws.
+ *     Arguments are validated on the host before any HIP call, so an invalid call touches
+ *     neither the device nor the stream. spa_last_error() gives a readable reason.
+ *   - Non-finite values in the tensors are not checked; they propagate to the outputs.
+ *   - The library is reentrant. Concurrent calls must use distinct outputs and workspaces.
+ */
+#ifndef SPA_H
+#define SPA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spa_status {
+    SPA_OK = 0,
+    SPA_ERR_INVALID_ARGUMENT = 1, /* null pointer, dim < 1, bad flag, non-finite scale,
+                                     misaligned or overlapping buffers */
+    SPA_ERR_UNSUPPORTED = 2,      /* a valid shape or dtype with no compiled kernel */
+    SPA_ERR_WORKSPACE = 3,        /* workspace given but smaller than required */
+    SPA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} spa_status_t;
+
+typedef enum spa_dtype {
+    SPA_F32 = 0, /* IEEE binary32 */
+    SPA_BF16 = 1 /* bfloat16 (8-bit exponent, 7-bit stored mantissa) */
+} spa_dtype_t;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int spa_version(void);
+
+/* Readable name of a status code (static string). */
+const char* spa_status_string(spa_status_t status);
+
+/* Reason for the calling thread's last failed call ("" if none); valid until its next call. */
+const char* spa_last_error(void);
+
+/*
+ * spa_project -- the projection step on its own: Xt[b,h,n,:] = X[b,h,n,:] P[h].
+ * (SPA page Sec. 3.1.2 and Algorithm 1 steps 2-3; PDA page Algorithm 2.1 step 1.)
+ *
+ *   X  [B,H,N,d]  input rows, in `dtype`.
+ *   P  [H,d,m]    projection, in `dtype`.
+ *   Xt [B,H,N,m]  output, written in `dtype`; must not overlap X or P.
+ *
+ * Accumulation is fp32 (bf16 path: bf16 MFMA products with fp32 accumulation, the result
+ * rounded to nearest-even bf16). Supported: SPA_BF16 with d in {64, 128} and 1 <= m <= 128;
+ * SPA_F32 with 1 <= d <= 256 and 1 <= m <= 128.
+ */
+spa_status_t spa_project(const void* X, const void* P, void* Xt, int B, int H, int N, int d,
+                         int m, spa_dtype_t dtype, void* stream);
+
+/*
+ * Workspace bytes spa_attn_fwd needs for these sizes (it holds the projected queries and
+ * keys). Returns 0 for arguments spa_attn_fwd would reject.
+ */
+size_t spa_attn_fwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
+                                    spa_dtype_t dtype);
+
+/*
+ * spa_attn_fwd -- the projected attention forward:
+ *
+ *   O[b,h,i,:] = sum_j softmax_j( scale * <Q[b,h,i,:] P[h], K[b,h,j,:] P[h]> ) V[b,h,j,:]
+ *
+ * over j in 0..N-1, or j in 0..i when causal = 1 (square self-attention; the diagonal is
+ * kept, so no row is ever empty). (SPA page Sec. 3.1.3 and Algorithm 1 steps 4-6; PDA page
+ * Algorithm 2.1 steps 2, 3 and 5.) The scale is the caller's: the pages use 1/sqrt(m)
+ * (SPA Sec. 3.1.3, PDA Algorithm 2.1) and 1/sqrt(d) (PDA revised proof Sec. 2.1, which keeps
+ * projected scores on the exact-score scale).
+ *
+ *   Q, K  [B,H,N,d], V [B,H,N,dv], P [H,d,m]: inputs in `dtype`.
+ *   scale finite float (any sign, zero allowed); causal 0 or 1.
+ *   O     [B,H,N,dv] output in `o_dtype`: SPA_BF16 or SPA_F32 on the bf16 path, SPA_F32 on
+ *         the fp32 path. Must not overlap any input, lse or the workspace.
+ *   lse   optional [B,H,N] fp32 output (NULL to skip): the natural log of each row's
+ *         softmax normaliser, log(sum_j exp(score_ij)).
+ *   workspace / workspace_bytes: device scratch of at least
+ *         spa_attn_fwd_workspace_bytes(...) bytes, 16-byte aligned, used for the projected
+ *         queries and keys. If workspace is NULL the library allocates and frees it
+ *         stream-ordered (hipMallocAsync / hipFreeAsync) inside the call.
+ *
+ * The bf16 path runs two launches on `stream`: a projection launch (bf16 MFMA, fp32
+ * accumulation, projected values rounded to bf16) and the attention launch (bf16 MFMA for
+ * both contractions, fp32 accumulation and an fp32 online softmax; the softmax weights are
+ * rounded to bf16 before they meet V). Supported: d in {64, 128}, dv in {64, 128},
+ * 1 <= m <= 128. The fp32 path computes in fp32 throughout: 1 <= d <= 256, 1 <= m <= 128,
+ * 1 <= dv <= 128. N may be any size from 1 to 2^22; tails are masked.
+ */
+spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const void* P,
+                          float scale, int causal, int B, int H, int N, int d, int m, int dv,
+                          spa_dtype_t dtype, void* O, spa_dtype_t o_dtype, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-launch timing for benchmarks. spa_profile_begin(max_calls) starts recording HIP
+ * events around the projection and attention launches of the next max_calls spa_attn_fwd
+ * calls (1 <= max_calls <= 65536; fails with SPA_ERR_INVALID_ARGUMENT if a recording is
+ * already open). spa_profile_end() waits for the last recorded event and returns the summed
+ * milliseconds of each launch and the number of calls recorded; any output pointer may be
+ * NULL. Timing is process-wide state: do not record from several threads at once.
+ */
+spa_status_t spa_profile_begin(int max_calls);
+spa_status_t spa_profile_end(double* project_ms, double* attn_ms, int* calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPA_H */

@@ -1,1 +1,186 @@
-"""Feature-axis projected softmax attention (SPA / PDA style) for MI355X (gfx950)."""
+"""Feature-axis projected softmax attention (SPA / PDA style) on MI355X (gfx950).
+
+A thin binding over the C ABI of ``libspa.so`` (declared in ``include/spa.h``). It only
+marshals arguments: every step of the computation runs in the library's HIP kernels on the
+caller's current torch stream. PyTorch provides device memory and streams. There is no
+fallback: without the built library, or on tensors that are not on a ROCm device, calls raise.
+
+    O = spa_attn_fwd(Q, K, V, P, scale, causal)      # Q,K [B,H,N,d], V [B,H,N,dv], P [H,d,m]
+    Qt = spa_project(Q, P)                           # [B,H,N,m]
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspa.so")
+
+SPA_OK = 0
+SPA_ERR_INVALID_ARGUMENT = 1
+SPA_ERR_UNSUPPORTED = 2
+SPA_ERR_WORKSPACE = 3
+SPA_ERR_HIP = 4
+SPA_F32 = 0
+SPA_BF16 = 1
+
+EXPORTS = ("spa_version", "spa_status_string", "spa_last_error", "spa_project",
+           "spa_attn_fwd_workspace_bytes", "spa_attn_fwd", "spa_profile_begin",
+           "spa_profile_end")
+
+
+class SpaError(RuntimeError):
+    """A libspa call returned a status other than SPA_OK."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_STATUS_NAMES = {0: "SPA_OK", 1: "SPA_ERR_INVALID_ARGUMENT", 2: "SPA_ERR_UNSUPPORTED",
+                 3: "SPA_ERR_WORKSPACE", 4: "SPA_ERR_HIP"}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libspa.so with its C signatures declared; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m jl_feature_projected_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, z, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_int
+    L.spa_version.restype = i
+    L.spa_version.argtypes = []
+    L.spa_status_string.restype = ctypes.c_char_p
+    L.spa_status_string.argtypes = [st]
+    L.spa_last_error.restype = ctypes.c_char_p
+    L.spa_last_error.argtypes = []
+    L.spa_project.restype = st
+    L.spa_project.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
+    L.spa_attn_fwd_workspace_bytes.restype = z
+    L.spa_attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.spa_attn_fwd.restype = st
+    L.spa_attn_fwd.argtypes = [vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, vp, i, vp, vp, z, vp]
+    L.spa_profile_begin.restype = st
+    L.spa_profile_begin.argtypes = [i]
+    dp = ctypes.POINTER(ctypes.c_double)
+    L.spa_profile_end.restype = st
+    L.spa_profile_end.argtypes = [dp, dp, ctypes.POINTER(ctypes.c_int)]
+    _lib = L
+    return L
+
+
+def check(status: int) -> None:
+    if status != SPA_OK:
+        raise SpaError(status, lib().spa_last_error().decode())
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t == torch.bfloat16:
+        return SPA_BF16
+    if t == torch.float32:
+        return SPA_F32
+    raise TypeError(f"unsupported dtype {t}: use torch.bfloat16 or torch.float32")
+
+
+def _device_tensor(x, name: str):
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a ROCm device tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return x
+
+
+def _stream_ptr(device) -> int:
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def spa_project(X, P):
+    """Xt[b,h,n,:] = X[b,h,n,:] @ P[h] on the current stream. X [B,H,N,d], P [H,d,m]."""
+    torch = _torch()
+    _device_tensor(X, "X")
+    _device_tensor(P, "P")
+    if X.dim() != 4 or P.dim() != 3:
+        raise ValueError("X must be [B,H,N,d] and P [H,d,m]")
+    B, H, N, d = X.shape
+    if P.shape[0] != H or P.shape[1] != d or P.dtype != X.dtype or P.device != X.device:
+        raise ValueError("P must be [H,d,m] with X's dtype and device")
+    m = P.shape[2]
+    Xt = torch.empty((B, H, N, m), dtype=X.dtype, device=X.device)
+    check(lib().spa_project(X.data_ptr(), P.data_ptr(), Xt.data_ptr(), B, H, N, d, m,
+                            _dtype_code(X.dtype), _stream_ptr(X.device)))
+    return Xt
+
+
+def spa_attn_fwd_workspace_bytes(B, H, N, d, m, dv, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().spa_attn_fwd_workspace_bytes(B, H, N, d, m, dv, code))
+
+
+def spa_attn_fwd(Q, K, V, P, scale: float | None = None, causal: bool = False,
+                 out_dtype=None, return_lse: bool = False, workspace=None, out=None):
+    """O = softmax(scale (Q P)(K P)^T [+causal]) V, per batch and head, on the current stream.
+
+    Q, K [B,H,N,d], V [B,H,N,dv], P [H,d,m], all bf16 or all fp32 on one device.
+    scale defaults to 1/sqrt(d). out_dtype: torch.float32 or torch.bfloat16 (bf16 inputs
+    only); default is the input dtype. workspace: optional uint8 device tensor of at least
+    spa_attn_fwd_workspace_bytes(...) bytes (otherwise the library allocates one
+    stream-ordered). out: optional preallocated output. Returns O, or (O, lse) with lse the
+    natural log of each row's softmax normaliser, fp32 [B,H,N].
+    """
+    torch = _torch()
+    for name, x in (("Q", Q), ("K", K), ("V", V), ("P", P)):
+        _device_tensor(x, name)
+    if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3]:
+        raise ValueError("Q, K must be [B,H,N,d] and V [B,H,N,dv]")
+    B, H, N, d = Q.shape
+    dv = V.shape[3]
+    if P.dim() != 3 or P.shape[0] != H or P.shape[1] != d:
+        raise ValueError("P must be [H,d,m]")
+    m = P.shape[2]
+    dt = Q.dtype
+    if any(x.dtype != dt for x in (K, V, P)) or any(x.device != Q.device for x in (K, V, P)):
+        raise ValueError("Q, K, V and P must share dtype and device")
+    odt = dt if out_dtype is None else out_dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=odt, device=Q.device)
+    else:
+        _device_tensor(out, "out")
+        if out.shape != (B, H, N, dv) or out.dtype != odt:
+            raise ValueError("out has the wrong shape or dtype")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=Q.device) if return_lse else None
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _device_tensor(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().spa_attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), P.data_ptr(),
+                             float(scale), int(bool(causal)), B, H, N, d, m, dv,
+                             _dtype_code(dt), out.data_ptr(), _dtype_code(odt),
+                             lse.data_ptr() if lse is not None else None, ws_ptr, ws_bytes,
+                             _stream_ptr(Q.device)))
+    return (out, lse) if return_lse else out
+
+
+def profile_begin(max_calls: int) -> None:
+    """Start recording per-launch HIP events for the next max_calls spa_attn_fwd calls."""
+    check(lib().spa_profile_begin(int(max_calls)))
+
+
+def profile_end() -> tuple[float, float, int]:
+    """(projection ms summed, attention ms summed, calls recorded); waits for the events."""
+    p, a, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+    check(lib().spa_profile_end(ctypes.byref(p), ctypes.byref(a), ctypes.byref(n)))
+    return p.value, a.value, n.value

@@ -1,0 +1,334 @@
+// spa_api.cpp -- the C ABI of libspa: argument validation, workspace handling, dispatch to
+// the HIP kernels, status codes and per-launch timing.
+//
+// Every argument check runs on the host before the first HIP call, so a rejected call
+// leaves the device and the stream untouched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/spa.h"
+#include "spa_internal.h"
+
+namespace {
+
+constexpr int kMaxN = 1 << 22;
+constexpr long long kMaxRows = 1LL << 31;  // B*H*N bound on every path
+
+thread_local char g_err[512] = "";
+
+spa_status_t fail(spa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+spa_status_t fail(spa_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+spa_status_t hip_fail(const char* where, hipError_t e) {
+    return fail(SPA_ERR_HIP, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+Range range(const void* p, size_t bytes) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return {b, b + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+size_t elem_size(spa_dtype_t t) { return t == SPA_BF16 ? 2 : 4; }
+
+// Workspace layout: projected queries then projected keys, each 256-byte aligned.
+struct WorkspaceLayout {
+    size_t tilde_bytes;  // one projected tensor
+    size_t k_offset;
+    size_t total;
+};
+WorkspaceLayout workspace_layout(long long rows, int m, spa_dtype_t dtype) {
+    const int cols = dtype == SPA_BF16 ? spa::padded_m(m) : m;
+    WorkspaceLayout w;
+    w.tilde_bytes = (size_t)rows * cols * elem_size(dtype);
+    w.k_offset = (w.tilde_bytes + 255) & ~(size_t)255;
+    w.total = w.k_offset + w.tilde_bytes;
+    return w;
+}
+
+spa_status_t check_dims(const char* fn, int B, int H, int N, int d, int m, int dv) {
+    if (B < 1 || H < 1 || N < 1 || d < 1 || m < 1 || dv < 1)
+        return fail(SPA_ERR_INVALID_ARGUMENT,
+                    "%s: every dimension must be >= 1 (B=%d H=%d N=%d d=%d m=%d dv=%d)", fn, B,
+                    H, N, d, m, dv);
+    if (N > kMaxN) return fail(SPA_ERR_UNSUPPORTED, "%s: N=%d exceeds %d", fn, N, kMaxN);
+    if ((long long)B * H * N >= kMaxRows)
+        return fail(SPA_ERR_UNSUPPORTED, "%s: B*H*N=%lld exceeds 2^31", fn,
+                    (long long)B * H * N);
+    return SPA_OK;
+}
+
+spa_status_t check_shape_support(const char* fn, spa_dtype_t dtype, int d, int m, int dv) {
+    if (dtype == SPA_BF16) {
+        if (d != 64 && d != 128)
+            return fail(SPA_ERR_UNSUPPORTED, "%s: bf16 path needs d in {64,128}, got %d", fn, d);
+        if (m > 128)
+            return fail(SPA_ERR_UNSUPPORTED, "%s: bf16 path needs m <= 128, got %d", fn, m);
+        if (dv != 64 && dv != 128)
+            return fail(SPA_ERR_UNSUPPORTED, "%s: bf16 path needs dv in {64,128}, got %d", fn,
+                        dv);
+        return SPA_OK;
+    }
+    if (dtype == SPA_F32) {
+        if (d > 256 || m > 128 || dv > 128)
+            return fail(SPA_ERR_UNSUPPORTED,
+                        "%s: fp32 path needs d <= 256, m <= 128, dv <= 128 (d=%d m=%d dv=%d)",
+                        fn, d, m, dv);
+        return SPA_OK;
+    }
+    return fail(SPA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+}
+
+// ---- launch timing ----------------------------------------------------------------------
+struct Profile {
+    std::mutex mu;
+    bool on = false;
+    int max_calls = 0;
+    int calls = 0;
+    std::vector<hipEvent_t> ev;  // 3 per call: before projection, between, after attention
+} g_prof;
+
+}  // namespace
+
+extern "C" {
+
+int spa_version(void) { return 100; }
+
+const char* spa_status_string(spa_status_t s) {
+    switch (s) {
+        case SPA_OK: return "SPA_OK";
+        case SPA_ERR_INVALID_ARGUMENT: return "SPA_ERR_INVALID_ARGUMENT";
+        case SPA_ERR_UNSUPPORTED: return "SPA_ERR_UNSUPPORTED";
+        case SPA_ERR_WORKSPACE: return "SPA_ERR_WORKSPACE";
+        case SPA_ERR_HIP: return "SPA_ERR_HIP";
+    }
+    return "SPA_ERR_UNKNOWN";
+}
+
+const char* spa_last_error(void) { return g_err; }
+
+spa_status_t spa_project(const void* X, const void* P, void* Xt, int B, int H, int N, int d,
+                         int m, spa_dtype_t dtype, void* stream) {
+    g_err[0] = '\0';
+    const char* fn = "spa_project";
+    if (!X || !P || !Xt) return fail(SPA_ERR_INVALID_ARGUMENT, "%s: null tensor pointer", fn);
+    spa_status_t st = check_dims(fn, B, H, N, d, m, 1);
+    if (st != SPA_OK) return st;
+    if (dtype != SPA_BF16 && dtype != SPA_F32)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+    if (dtype == SPA_BF16 ? (d != 64 && d != 128) || m > 128 : d > 256 || m > 128)
+        return fail(SPA_ERR_UNSUPPORTED, "%s: unsupported d=%d m=%d for %s", fn, d, m,
+                    dtype == SPA_BF16 ? "bf16" : "fp32");
+    if (!aligned(X, 16) || !aligned(P, 16) || !aligned(Xt, 16))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: tensor base not 16-byte aligned", fn);
+    const size_t es = elem_size(dtype);
+    const long long rows = (long long)B * H * N;
+    const Range rx = range(X, rows * d * es), rp = range(P, (size_t)H * d * m * es),
+                ry = range(Xt, rows * m * es);
+    if (overlap(ry, rx) || overlap(ry, rp))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: output overlaps an input", fn);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dtype == SPA_BF16)
+        e = spa::launch_project_bf16(X, nullptr, P, Xt, nullptr, 1, B * H, H, N, d, m, m, m,
+                                     1.0f, 1.0f, s);
+    else
+        e = spa::launch_project_f32(static_cast<const float*>(X), static_cast<const float*>(P),
+                                    static_cast<float*>(Xt), B * H, H, N, d, m, 1.0f, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return SPA_OK;
+}
+
+size_t spa_attn_fwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
+                                    spa_dtype_t dtype) {
+    char saved[sizeof(g_err)];
+    memcpy(saved, g_err, sizeof(g_err));
+    size_t out = 0;
+    if (check_dims("spa_attn_fwd_workspace_bytes", B, H, N, d, m, dv) == SPA_OK &&
+        check_shape_support("spa_attn_fwd_workspace_bytes", dtype, d, m, dv) == SPA_OK)
+        out = workspace_layout((long long)B * H * N, m, dtype).total;
+    memcpy(g_err, saved, sizeof(g_err));
+    return out;
+}
+
+spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const void* P,
+                          float scale, int causal, int B, int H, int N, int d, int m, int dv,
+                          spa_dtype_t dtype, void* O, spa_dtype_t o_dtype, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    const char* fn = "spa_attn_fwd";
+    if (!Q || !K || !V || !P || !O)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: null tensor pointer", fn);
+    spa_status_t st = check_dims(fn, B, H, N, d, m, dv);
+    if (st != SPA_OK) return st;
+    if (causal != 0 && causal != 1)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1, got %d", fn, causal);
+    if (!std::isfinite(scale))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: scale must be finite", fn);
+    st = check_shape_support(fn, dtype, d, m, dv);
+    if (st != SPA_OK) return st;
+    if (o_dtype != SPA_F32 && o_dtype != SPA_BF16)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: unknown o_dtype %d", fn, (int)o_dtype);
+    if (dtype == SPA_F32 && o_dtype != SPA_F32)
+        return fail(SPA_ERR_UNSUPPORTED, "%s: the fp32 path writes fp32 outputs only", fn);
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(P, 16) ||
+        !aligned(O, 16))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: tensor base not 16-byte aligned", fn);
+    if (lse && !aligned(lse, 4))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: lse not 4-byte aligned", fn);
+    if (workspace && !aligned(workspace, 16))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace not 16-byte aligned", fn);
+
+    const long long rows = (long long)B * H * N;
+    const size_t es = elem_size(dtype);
+    const WorkspaceLayout wl = workspace_layout(rows, m, dtype);
+    if (workspace && workspace_bytes < wl.total)
+        return fail(SPA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn,
+                    workspace_bytes, wl.total);
+    const Range ro = range(O, rows * dv * elem_size(o_dtype));
+    const Range ins[4] = {range(Q, rows * d * es), range(K, rows * d * es),
+                          range(V, rows * dv * es), range(P, (size_t)H * d * m * es)};
+    for (const Range& r : ins)
+        if (overlap(ro, r)) return fail(SPA_ERR_INVALID_ARGUMENT, "%s: O overlaps an input", fn);
+    if (lse) {
+        const Range rl = range(lse, rows * sizeof(float));
+        if (overlap(rl, ro)) return fail(SPA_ERR_INVALID_ARGUMENT, "%s: lse overlaps O", fn);
+        for (const Range& r : ins)
+            if (overlap(rl, r))
+                return fail(SPA_ERR_INVALID_ARGUMENT, "%s: lse overlaps an input", fn);
+    }
+    if (workspace) {
+        const Range rw = range(workspace, wl.total);
+        if (overlap(rw, ro) || (lse && overlap(rw, range(lse, rows * sizeof(float)))))
+            return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace overlaps an output", fn);
+        for (const Range& r : ins)
+            if (overlap(rw, r))
+                return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace overlaps an input", fn);
+    }
+
+    // ---- validated: HIP work starts here ------------------------------------------------
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    if (!ws) {
+        hipError_t e = hipMallocAsync(&ws, wl.total, s);
+        if (e != hipSuccess) return hip_fail("spa_attn_fwd: hipMallocAsync", e);
+    }
+    char* wsb = static_cast<char*>(ws);
+    void* Qt = wsb;
+    void* Kt = wsb + wl.k_offset;
+
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    {
+        std::lock_guard<std::mutex> lock(g_prof.mu);
+        if (g_prof.on && g_prof.calls < g_prof.max_calls) {
+            for (int i = 0; i < 3; ++i) ev[i] = g_prof.ev[3 * g_prof.calls + i];
+            ++g_prof.calls;
+        }
+    }
+    hipError_t e = hipSuccess;
+    if (ev[0]) e = hipEventRecord(ev[0], s);
+    if (e == hipSuccess) {
+        if (dtype == SPA_BF16) {
+            const int mp = spa::padded_m(m);
+            // Queries carry scale*log2(e) so that scores come out in base-2 exponent units.
+            const float qscale = scale * 1.44269504088896340736f;
+            e = spa::launch_project_bf16(Q, K, P, Qt, Kt, 2, B * H, H, N, d, m, mp, mp, qscale,
+                                         1.0f, s);
+            if (e == hipSuccess && ev[1]) e = hipEventRecord(ev[1], s);
+            if (e == hipSuccess)
+                e = spa::launch_attn_bf16(Qt, Kt, V, O, lse, B * H, N, mp, dv, causal == 1,
+                                          o_dtype == SPA_F32, s);
+        } else {
+            e = spa::launch_project_f32(static_cast<const float*>(Q),
+                                        static_cast<const float*>(P), static_cast<float*>(Qt),
+                                        B * H, H, N, d, m, 1.0f, s);
+            if (e == hipSuccess)
+                e = spa::launch_project_f32(static_cast<const float*>(K),
+                                            static_cast<const float*>(P),
+                                            static_cast<float*>(Kt), B * H, H, N, d, m, 1.0f,
+                                            s);
+            if (e == hipSuccess && ev[1]) e = hipEventRecord(ev[1], s);
+            if (e == hipSuccess)
+                e = spa::launch_attn_f32(static_cast<const float*>(Qt),
+                                         static_cast<const float*>(Kt),
+                                         static_cast<const float*>(V), static_cast<float*>(O),
+                                         lse, B * H, N, m, dv, causal == 1, scale, s);
+        }
+    }
+    if (e == hipSuccess && ev[2]) e = hipEventRecord(ev[2], s);
+    if (!workspace) {
+        hipError_t e2 = hipFreeAsync(ws, s);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return SPA_OK;
+}
+
+spa_status_t spa_profile_begin(int max_calls) {
+    g_err[0] = '\0';
+    if (max_calls < 1 || max_calls > 65536)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "spa_profile_begin: max_calls=%d", max_calls);
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    if (g_prof.on) return fail(SPA_ERR_INVALID_ARGUMENT, "spa_profile_begin: already recording");
+    g_prof.ev.assign(3 * (size_t)max_calls, nullptr);
+    for (auto& e : g_prof.ev) {
+        hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) {
+            for (auto& x : g_prof.ev)
+                if (x) (void)hipEventDestroy(x);
+            g_prof.ev.clear();
+            return hip_fail("spa_profile_begin: hipEventCreate", r);
+        }
+    }
+    g_prof.max_calls = max_calls;
+    g_prof.calls = 0;
+    g_prof.on = true;
+    return SPA_OK;
+}
+
+spa_status_t spa_profile_end(double* project_ms, double* attn_ms, int* calls) {
+    g_err[0] = '\0';
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    if (!g_prof.on) return fail(SPA_ERR_INVALID_ARGUMENT, "spa_profile_end: not recording");
+    double pt = 0.0, at = 0.0;
+    hipError_t err = hipSuccess;
+    if (g_prof.calls > 0) err = hipEventSynchronize(g_prof.ev[3 * g_prof.calls - 1]);
+    for (int c = 0; c < g_prof.calls && err == hipSuccess; ++c) {
+        float a = 0.0f, b = 0.0f;
+        err = hipEventElapsedTime(&a, g_prof.ev[3 * c], g_prof.ev[3 * c + 1]);
+        if (err == hipSuccess) err = hipEventElapsedTime(&b, g_prof.ev[3 * c + 1], g_prof.ev[3 * c + 2]);
+        pt += a;
+        at += b;
+    }
+    const int n = g_prof.calls;
+    for (auto& e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.on = false;
+    g_prof.calls = 0;
+    if (err != hipSuccess) return hip_fail("spa_profile_end", err);
+    if (project_ms) *project_ms = pt;
+    if (attn_ms) *attn_ms = at;
+    if (calls) *calls = n;
+    return SPA_OK;
+}
+
+}  // extern "C"

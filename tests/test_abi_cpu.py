@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: libspa.so loads, exports every symbol include/spa.h declares, and
+rejects invalid calls on the host before any HIP call (so these run anywhere)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import jl_feature_projected_amd as spa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spa.h")
+
+# Fake, aligned, non-null device addresses far apart: every call below is rejected by host
+# validation before a pointer could be used.
+A, B_, C, D, E, F = (0x10000000 * k for k in range(1, 7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return spa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(spa.EXPORTS)
+
+
+def test_version_and_status_strings(L):
+    assert L.spa_version() >= 100
+    for code, name in ((0, "SPA_OK"), (1, "SPA_ERR_INVALID_ARGUMENT"), (2, "SPA_ERR_UNSUPPORTED"),
+                       (3, "SPA_ERR_WORKSPACE"), (4, "SPA_ERR_HIP")):
+        assert L.spa_status_string(code).decode() == name
+
+
+def _attn(L, **kw):
+    a = dict(Q=A, K=B_, V=C, P=D, scale=0.125, causal=1, B=1, H=2, N=256, d=128, m=32, dv=128,
+             dtype=spa.SPA_BF16, O=E, o_dtype=spa.SPA_F32, lse=None, ws=F, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return L.spa_attn_fwd(a["Q"], a["K"], a["V"], a["P"], a["scale"], a["causal"], a["B"],
+                          a["H"], a["N"], a["d"], a["m"], a["dv"], a["dtype"], a["O"],
+                          a["o_dtype"], a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(O=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(N=0), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(B=-1), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(m=0), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(causal=2), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(o_dtype=9), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(Q=A + 2), spa.SPA_ERR_INVALID_ARGUMENT),           # misaligned
+    (dict(lse=E + 2), spa.SPA_ERR_INVALID_ARGUMENT),         # misaligned lse
+    (dict(O=A + 64), spa.SPA_ERR_INVALID_ARGUMENT),          # O overlaps Q
+    (dict(lse=E + 16), spa.SPA_ERR_INVALID_ARGUMENT),        # lse overlaps O
+    (dict(ws=E), spa.SPA_ERR_INVALID_ARGUMENT),              # workspace overlaps O
+    (dict(ws_bytes=1024), spa.SPA_ERR_WORKSPACE),
+    (dict(d=96), spa.SPA_ERR_UNSUPPORTED),
+    (dict(dv=32), spa.SPA_ERR_UNSUPPORTED),
+    (dict(m=129), spa.SPA_ERR_UNSUPPORTED),
+    (dict(N=(1 << 22) + 1), spa.SPA_ERR_UNSUPPORTED),
+    (dict(dtype=spa.SPA_F32, o_dtype=spa.SPA_BF16), spa.SPA_ERR_UNSUPPORTED),
+    (dict(dtype=spa.SPA_F32, d=512), spa.SPA_ERR_UNSUPPORTED),
+])
+def test_attn_fwd_rejects_on_host(L, kw, code):
+    assert _attn(L, **kw) == code
+    assert len(L.spa_last_error()) > 0
+
+
+def test_project_rejects_on_host(L):
+    P = L.spa_project
+    assert P(None, B_, C, 1, 1, 8, 64, 16, spa.SPA_BF16, None) == spa.SPA_ERR_INVALID_ARGUMENT
+    assert P(A, B_, C, 1, 1, 0, 64, 16, spa.SPA_BF16, None) == spa.SPA_ERR_INVALID_ARGUMENT
+    assert P(A, B_, C, 1, 1, 8, 80, 16, spa.SPA_BF16, None) == spa.SPA_ERR_UNSUPPORTED
+    assert P(A, B_, C, 1, 1, 8, 64, 200, spa.SPA_BF16, None) == spa.SPA_ERR_UNSUPPORTED
+    assert P(A, B_, A + 32, 1, 1, 8, 64, 16, spa.SPA_BF16, None) == spa.SPA_ERR_INVALID_ARGUMENT
+    assert P(A + 4, B_, C, 1, 1, 8, 64, 16, spa.SPA_BF16, None) == spa.SPA_ERR_INVALID_ARGUMENT
+    assert P(A, B_, C, 1, 1, 8, 64, 16, 5, None) == spa.SPA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_bytes(L):
+    # bf16: projected queries and keys at the padded width (m=8 -> 16 columns)
+    n = L.spa_attn_fwd_workspace_bytes(2, 3, 100, 64, 8, 64, spa.SPA_BF16)
+    one = 2 * 3 * 100 * 16 * 2
+    assert n == ((one + 255) // 256) * 256 + one
+    n32 = L.spa_attn_fwd_workspace_bytes(1, 1, 512, 64, 16, 64, spa.SPA_F32)
+    assert n32 == 2 * 512 * 16 * 4
+    assert L.spa_attn_fwd_workspace_bytes(1, 1, 512, 96, 16, 64, spa.SPA_BF16) == 0
+    assert L.spa_attn_fwd_workspace_bytes(0, 1, 512, 64, 16, 64, spa.SPA_BF16) == 0
+
+
+def test_profile_api_state(L):
+    assert L.spa_profile_begin(0) == spa.SPA_ERR_INVALID_ARGUMENT
+    d, e, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+    assert L.spa_profile_end(ctypes.byref(d), ctypes.byref(e), ctypes.byref(n)) == \
+        spa.SPA_ERR_INVALID_ARGUMENT
+
+
+def test_binding_fails_loudly_without_device_tensors():
+    import torch
+
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    p = torch.zeros(1, 64, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        spa.spa_attn_fwd(x, x, x, p, 0.125, True)
+    with pytest.raises(ValueError):
+        spa.spa_project(x, p)

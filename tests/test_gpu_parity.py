@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path against the CPU oracle on identical seeded inputs (MI355X only).
+
+Tolerances: bf16 path max-abs error <= 2e-2 on fp32 outputs (bf16 outputs are additionally
+allowed their own rounding, half a bf16 ulp of the reference value); fp32 path max-abs error
+<= 1e-4 relative to max |O|. Small cases compare every output; the full-size workloads
+compare a stratified row sample (tile boundaries, first and last rows, random rows, and
+whole heads where the oracle finishes in seconds) plus properties that hold at any size.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import jl_feature_projected_amd as spa
+import oracle
+from jl_feature_projected_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+TOL_F32_REL = 1e-4
+
+
+def note(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "the gpu tests need a ROCm GPU"
+    spa.lib()
+    return torch.device("cuda:0")
+
+
+def to_dev(x: inputs.Inputs, dev):
+    return [t.to(dev) for t in (x.Q, x.K, x.V, x.P)]
+
+
+def run(x, dev, out_dtype=torch.float32, return_lse=False, scale=None):
+    w = x.w
+    Q, K, V, P = to_dev(x, dev)
+    res = spa.spa_attn_fwd(Q, K, V, P, w.scale if scale is None else scale, w.causal,
+                           out_dtype=out_dtype, return_lse=return_lse)
+    torch.cuda.synchronize()
+    return res
+
+
+def np64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def bf16_half_ulp(x):
+    """Half a bf16 ulp at |x|: the rounding a bf16 output may add."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 8)
+
+
+def assert_bf16_close(got, ref, out_bf16=False, what=""):
+    err = np.abs(got - ref)
+    allow = TOL_BF16 + (bf16_half_ulp(ref) if out_bf16 else 0.0)
+    worst = np.unravel_index(np.argmax(err - allow), err.shape)
+    note(f"{what}: max-abs {err.max():.3e} (at {tuple(int(i) for i in worst)})")
+    assert np.all(err <= allow), (what, float(err.max()), worst)
+
+
+# ---- the projection step on its own ------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("m", [1, 5, 8, 16, 32, 48, 64, 128])
+def test_project_parity(dev, oracle_mod, dtype, m):
+    d = 128 if m % 2 == 0 else 64
+    w = inputs.Workload("proj", 2, 3, 333, d, m, 64, False, dtype=dtype, seed=m)
+    x = inputs.draw(w)
+    Xt = spa.spa_project(x.Q.to(dev), x.P.to(dev))
+    ref = oracle_mod.project(x.Q, x.P)
+    got = np64(Xt)
+    if dtype == "bf16":
+        # fp32 accumulation, one rounding to bf16
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5)
+    else:
+        assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+# ---- small workloads: every output -------------------------------------------------------
+
+def test_c1_fp32_full(dev, oracle_mod):
+    w = inputs.WORKLOADS["c1"]
+    x = inputs.draw(w)
+    note(f"c1 {w.name}")
+    O, lse = run(x, dev, out_dtype=torch.float32, return_lse=True)
+    Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, w.causal, with_lse=True)
+    rel = np.max(np.abs(np64(O) - Or)) / np.max(np.abs(Or))
+    note(f"c1 relative error {rel:.3e}")
+    assert rel <= TOL_F32_REL
+    assert np.max(np.abs(np64(lse) - lr)) <= 1e-4 * max(1.0, np.max(np.abs(lr)))
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_c2_full(dev, oracle_mod, out):
+    w = inputs.WORKLOADS["c2"]
+    x = inputs.draw(w)
+    note(f"c2 {w.name} out={out}")
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    O = run(x, dev, out_dtype=odt)
+    Or = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, w.causal)
+    assert_bf16_close(np64(O), Or, out_bf16=(out == "bf16"), what=f"c2/{out}")
+
+
+SMALL = [
+    # (N, d, m, dv, causal)
+    (1, 64, 16, 64, True), (1, 128, 8, 128, False), (7, 64, 16, 64, False),
+    (64, 128, 32, 128, True), (100, 64, 8, 128, True), (129, 128, 48, 64, False),
+    (300, 128, 64, 128, True), (300, 64, 5, 64, False), (513, 128, 128, 128, True),
+    (1000, 128, 32, 128, False), (1000, 64, 16, 64, True), (777, 128, 100, 64, True),
+]
+
+
+@pytest.mark.parametrize("N,d,m,dv,causal", SMALL)
+def test_small_shapes_full(dev, oracle_mod, N, d, m, dv, causal):
+    w = inputs.Workload(f"small-n{N}-d{d}-m{m}-dv{dv}-c{int(causal)}", 2, 3, N, d, m, dv,
+                        causal, seed=1000 + N + m)
+    x = inputs.draw(w)
+    note(w.name)
+    O, lse = run(x, dev, return_lse=True)
+    Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, causal, with_lse=True)
+    assert_bf16_close(np64(O), Or, what=w.name)
+    assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
+
+
+@pytest.mark.parametrize("N,m,dv,causal", [(200, 16, 64, True), (333, 40, 128, False)])
+def test_fp32_path_other_shapes(dev, oracle_mod, N, m, dv, causal):
+    w = inputs.Workload(f"f32-n{N}-m{m}", 1, 2, N, 96, m, dv, causal, dtype="f32", seed=7)
+    x = inputs.draw(w)
+    note(w.name)
+    O = run(x, dev)
+    Or = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, causal)
+    assert np.max(np.abs(np64(O) - Or)) / np.max(np.abs(Or)) <= TOL_F32_REL
+
+
+# ---- full-size workloads: stratified row samples ----------------------------------------
+
+FULL = {  # workload -> (random rows per head, heads compared in full)
+    "c3": (96, (0, 31)),
+    "c4": (24, ()),
+    "c5_m8": (48, (15,)),
+    "c5_m16": (48, ()),
+    "c5_m32": (48, ()),
+    "c5_m64": (48, ()),
+    "c5_m128": (48, ()),
+    "c5_identity": (48, (15,)),
+}
+
+
+def sample_rows(w, per_head, full_heads, seed=0):
+    rng = np.random.default_rng(seed)
+    N, BH = w.N, w.B * w.H
+    edges = [0, 1, 31, 32, 63, 64, 65, 127, 128, 129, N // 2, N - 129, N - 128, N - 65,
+             N - 64, N - 1]
+    bh, ri = [], []
+    for h in range(BH):
+        rows = set(e for e in edges if 0 <= e < N) | set(rng.integers(0, N, per_head).tolist())
+        if h in full_heads:
+            rows = set(range(N))
+        rows = sorted(rows)
+        bh += [h] * len(rows)
+        ri += rows
+    return np.array(bh), np.array(ri)
+
+
+@pytest.mark.parametrize("key", list(FULL))
+def test_full_size_sampled(dev, oracle_mod, key):
+    w = inputs.WORKLOADS[key]
+    per_head, full_heads = FULL[key]
+    note(f"{key} {w.name}: drawing inputs")
+    x = inputs.draw(w)
+    note(f"{key}: GPU run")
+    O = run(x, dev, out_dtype=torch.float32)
+    assert bool(torch.isfinite(O).all())
+    bh, ri = sample_rows(w, per_head, full_heads)
+    note(f"{key}: oracle on {len(bh)} rows")
+    Or = oracle_mod.attn_rows(x.Q, x.K, x.V, x.P, w.scale, w.causal, bh, ri)
+    Og = O.reshape(w.B * w.H, w.N, w.dv)[torch.from_numpy(bh).to(dev), torch.from_numpy(ri).to(dev)]
+    assert_bf16_close(np64(Og), Or, what=key)
+    if w.causal:
+        # row 0 of every head sees only key 0: the output is exactly that value row
+        assert torch.equal(O[:, :, 0].float(), x.V[:, :, 0].float().to(dev))
+
+
+def test_identity_projection_matches_exact_attention(dev):
+    """m = d with P = I: the path computes exact softmax(Q K^T / sqrt(d)) V."""
+    w = inputs.WORKLOADS["c5_identity"].replace(H=2, N=1500)
+    x = inputs.draw(w)
+    O = run(x, dev)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        x.Q.double(), x.K.double(), x.V.double(), is_causal=True, scale=w.scale)
+    assert_bf16_close(np64(O), ref.numpy(), what="identity-vs-sdpa")
+
+
+# ---- properties that need no oracle ------------------------------------------------------
+
+def test_closed_forms_on_gpu(dev):
+    w = inputs.Workload("closed", 1, 2, 700, 128, 32, 128, True, seed=5)
+    x = inputs.draw(w)
+    Q, K, V, P = to_dev(x, dev)
+    # V = 1 -> O = 1
+    ones = torch.ones_like(V)
+    O = spa.spa_attn_fwd(Q, K, ones, P, w.scale, True, out_dtype=torch.float32)
+    assert torch.max(torch.abs(O - 1.0)).item() <= 2 ** -7
+    # Q = 0 -> uniform weights -> causal prefix means
+    O = spa.spa_attn_fwd(torch.zeros_like(Q), K, V, P, w.scale, True, out_dtype=torch.float32)
+    prefix = torch.cumsum(V.double(), dim=2) / torch.arange(1, w.N + 1, device=dev,
+                                                            dtype=torch.float64)[None, None, :, None]
+    assert torch.max(torch.abs(O.double() - prefix)).item() <= 1e-2
+    # non-causal permutation of keys and values together leaves O unchanged
+    perm = torch.randperm(w.N, generator=torch.Generator().manual_seed(0)).to(dev)
+    O1 = spa.spa_attn_fwd(Q, K, V, P, w.scale, False, out_dtype=torch.float32)
+    O2 = spa.spa_attn_fwd(Q, K[:, :, perm].contiguous(), V[:, :, perm].contiguous(), P, w.scale,
+                          False, out_dtype=torch.float32)
+    assert torch.max(torch.abs(O1 - O2)).item() <= 1e-2
+
+
+def test_deterministic_bits(dev):
+    w = inputs.WORKLOADS["c2"].replace(B=1)
+    x = inputs.draw(w)
+    a = run(x, dev, out_dtype=torch.bfloat16)
+    b = run(x, dev, out_dtype=torch.bfloat16)
+    assert torch.equal(a, b)
+
+
+def test_workspace_paths_agree(dev):
+    w = inputs.WORKLOADS["c2"].replace(B=1, H=4)
+    x = inputs.draw(w)
+    Q, K, V, P = to_dev(x, dev)
+    n = spa.spa_attn_fwd_workspace_bytes(w.B, w.H, w.N, w.d, w.m, w.dv, torch.bfloat16)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    a = spa.spa_attn_fwd(Q, K, V, P, w.scale, True, workspace=ws)
+    b = spa.spa_attn_fwd(Q, K, V, P, w.scale, True)
+    assert torch.equal(a, b)
+    with pytest.raises(spa.SpaError) as e:
+        spa.spa_attn_fwd(Q, K, V, P, w.scale, True, workspace=ws[: n // 2])
+    assert e.value.status == spa.SPA_ERR_WORKSPACE
+    # a side stream gives the same bits
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = spa.spa_attn_fwd(Q, K, V, P, w.scale, True, workspace=ws)
+    s.synchronize()
+    assert torch.equal(a, c)
+
+
+def test_profile_records_launch_times(dev):
+    w = inputs.WORKLOADS["c2"].replace(B=1)
+    x = inputs.draw(w)
+    Q, K, V, P = to_dev(x, dev)
+    spa.profile_begin(4)
+    for _ in range(3):
+        spa.spa_attn_fwd(Q, K, V, P, w.scale, True)
+    proj_ms, attn_ms, calls = spa.profile_end()
+    assert calls == 3 and proj_ms > 0 and attn_ms > 0
