@@ -150,7 +150,7 @@ spa_status_t spa_project(const void* X, const void* P, void* Xt, int B, int H, i
     hipError_t e;
     if (dtype == SPA_BF16)
         e = spa::launch_project_bf16(X, nullptr, P, Xt, nullptr, 1, B * H, H, N, d, m, m, m,
-                                     1.0f, 1.0f, s);
+                                     1.0f, 1.0f, /*out_f16=*/false, s);
     else
         e = spa::launch_project_f32(static_cast<const float*>(X), static_cast<const float*>(P),
                                     static_cast<float*>(Xt), B * H, H, N, d, m, 1.0f, s);
@@ -250,9 +250,12 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
         if (dtype == SPA_BF16) {
             const int mp = spa::padded_m(m);
             // Queries carry scale*log2(e) so that scores come out in base-2 exponent units.
+            // The projected operands of the score MFMA are kept in fp16: its 11-bit
+            // significand holds the score error well inside the bf16 path's tolerance where
+            // bf16 operands (8 bits) do not, at the same MFMA rate.
             const float qscale = scale * 1.44269504088896340736f;
             e = spa::launch_project_bf16(Q, K, P, Qt, Kt, 2, B * H, H, N, d, m, mp, mp, qscale,
-                                         1.0f, s);
+                                         1.0f, /*out_f16=*/true, s);
             if (e == hipSuccess && ev[1]) e = hipEventRecord(ev[1], s);
             if (e == hipSuccess)
                 e = spa::launch_attn_bf16(Qt, Kt, V, O, lse, B * H, N, mp, dv, causal == 1,

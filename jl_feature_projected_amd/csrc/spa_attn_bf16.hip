@@ -1,5 +1,5 @@
-// spa_attn_bf16.hip -- projected softmax attention on bf16 MFMA (gfx950), streamed over key
-// tiles so the N x N score matrix never reaches memory.
+// spa_attn_bf16.hip -- projected softmax attention for bf16 inputs on gfx950 MFMA, streamed
+// over key tiles so the N x N score matrix never reaches memory.
 //
 // What it computes: "Sparse Projection Attention" page, Sec. 3.1.3 and Algorithm 1 steps 4-6
 // (scores of projected queries and keys, row softmax, weights times V); "Projection-
@@ -23,7 +23,9 @@
 //     score accumulator straight into the B operand: the k-order of the contraction is the
 //     key order the score layout already has, and V^T is read from LDS in that same order.
 // Queries arrive pre-scaled by scale*log2(e), so exp2 of the MFMA output is the softmax
-// numerator.
+// numerator. The projected queries and keys are fp16 (the score MFMA runs in fp16, whose
+// 11-bit significand keeps the score error small); V and the weights are bf16. The
+// normaliser is summed from the bf16-rounded weights, the same values the PV MFMA consumes.
 #include "spa_device.h"
 #include "spa_internal.h"
 
@@ -37,10 +39,10 @@ constexpr float kTau = 8.0f;
 
 template <int MP, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
-    const bf16_t* __restrict__ Qt, const bf16_t* __restrict__ Kt, const bf16_t* __restrict__ V,
+    const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Kt, const bf16_t* __restrict__ V,
     void* __restrict__ O, float* __restrict__ lse, int N, int nqb, int out_f32) {
     constexpr int KS = MP / 16;          // score MFMA k-steps
-    constexpr int KROW = MP + 8;         // LDS pitch of a projected-key row (bf16)
+    constexpr int KROW = MP + 8;         // LDS pitch of a projected-key row (fp16)
     constexpr int VROW = kBC + 4;        // LDS pitch of a V^T row (bf16)
     constexpr int K_ELEMS = kBC * KROW;  // one K tile
     constexpr int V_ELEMS = DV * VROW;   // one V^T tile
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     constexpr int VSLOTS = (kBC / 4) * (DV / 8);           // 4 keys x 8 dv per slot
     constexpr int DB = DV / 32;                            // 32-row blocks of V^T / O^T
 
-    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (K_ELEMS + V_ELEMS)];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (K_ELEMS + V_ELEMS)];
 
     // Workgroup -> (head, query block). Workgroups are handed to the 8 XCDs round-robin;
     // when the grid divides evenly, XCD x gets a contiguous range of (head, block) pairs so
@@ -68,17 +70,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const int qw0 = q0 + wave * 32;
     const int myq = qw0 + col;
 
-    const bf16_t* Qh = Qt + (size_t)bh * N * MP;
-    const bf16_t* Kh = Kt + (size_t)bh * N * MP;
+    const uint16_t* Qh = Qt + (size_t)bh * N * MP;
+    const uint16_t* Kh = Kt + (size_t)bh * N * MP;
     const bf16_t* Vh = V + (size_t)bh * N * DV;
 
     // This lane's query as the B operand of the score MFMA (zero past N).
-    bf16x8 qf[KS];
+    f16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (myq < N) v = load16(Qh + (size_t)myq * MP + ks * 16 + half * 8);
-        qf[ks] = as_bf16x8(v);
+        qf[ks] = as_f16x8(v);
     }
 
     const int kend = CAUSAL ? min(N, q0 + kBR) : N;
@@ -107,8 +109,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         }
     };
     auto store_tile = [&](int buf) {
-        bf16_t* Ks = lds + buf * (K_ELEMS + V_ELEMS);
-        bf16_t* Vs = Ks + K_ELEMS;
+        uint16_t* Ks = lds + buf * (K_ELEMS + V_ELEMS);
+        uint16_t* Vs = Ks + K_ELEMS;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int c = tid + i * kThreads;
@@ -155,8 +157,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         const bool more = t + 1 < ntiles;
         if (more) load_tile(k0 + kBC);
 
-        const bf16_t* Ks = lds + (t & 1) * (K_ELEMS + V_ELEMS);
-        const bf16_t* Vs = Ks + K_ELEMS;
+        const uint16_t* Ks = lds + (t & 1) * (K_ELEMS + V_ELEMS);
+        const uint16_t* Vs = Ks + K_ELEMS;
 
         // Causal: a wave whose queries all precede the tile has nothing to do in it.
         if (!CAUSAL || k0 <= qw0 + 31) {
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 s[kb] = cinit;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 a = as_bf16x8(load16(Ks + (kb * 32 + col) * KROW + ks * 16 + half * 8));
+                    const f16x8 a = as_f16x8(load16(Ks + (kb * 32 + col) * KROW + ks * 16 + half * 8));
                     s[kb] = mfma32x32x16(a, qf[ks], s[kb]);
                 }
             }
@@ -219,8 +221,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                     for (int j = 0; j < 4; ++j) {
                         const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j]);
                         const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j + 1]);
-                        lsum += p0 + p1;
                         wp[j] = pack_bf16x2(p0, p1);
+                        lsum = add_bf16x2(wp[j], lsum);
                     }
                     pf[kb][tt] = as_bf16x8(w);
                 }
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt) {
-                        const bf16_t* vp = Vs + (db * 32 + col) * VROW + kb * 32 + tt * 16 + half * 4;
+                        const uint16_t* vp = Vs + (db * 32 + col) * VROW + kb * 32 + tt * 16 + half * 4;
                         const uint2 lo = *reinterpret_cast<const uint2*>(vp);
                         const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
                         const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -280,7 +282,7 @@ hipError_t launch(const void* Qt, const void* Kt, const void* V, void* O, float*
                   int N, bool out_f32, hipStream_t stream) {
     const int nqb = (N + kBR - 1) / kBR;
     attn_bf16_kernel<MP, DV, CAUSAL><<<dim3(nqb * BH), kThreads, 0, stream>>>(
-        static_cast<const bf16_t*>(Qt), static_cast<const bf16_t*>(Kt),
+        static_cast<const uint16_t*>(Qt), static_cast<const uint16_t*>(Kt),
         static_cast<const bf16_t*>(V), O, lse, N, nqb, out_f32 ? 1 : 0);
     return hipGetLastError();
 }

@@ -16,13 +16,18 @@ namespace spa {
 
 typedef __bf16 bf16_t;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ uint4 as_uint4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
 
 __device__ __forceinline__ uint4 load16(const void* p) {
@@ -34,6 +39,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
     bf16x2 v = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two floats rounded to nearest-even fp16, packed low/high into one dword.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc + lo + hi of a packed bf16 pair, in fp32 (one v_dot2 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), ones, acc, false);
 }
 
 __device__ __forceinline__ f32x16 f32x16_fill(float x) {

@@ -8,7 +8,8 @@
 // Each wave computes X~^T for 32 tokens: D[c][t] = sum_k P^T[c][k] X^T[k][t], with P^T
 // staged once per workgroup in LDS as the A operand and 16-byte loads of X rows as the B
 // operand. In the D layout a lane owns one token and 4 consecutive output columns per
-// group, so every store is one 8-byte write of 4 bf16.
+// group, so every store is one 8-byte write of 4 values. The result is rounded once, to
+// bf16 for the exported projection or to fp16 for the attention path's score operands.
 #include "spa_device.h"
 #include "spa_internal.h"
 
@@ -20,11 +21,17 @@ constexpr int kProjTokensPerWave = 32;
 constexpr int kProjIters = 2;  // token blocks per wave: amortises the P^T staging
 constexpr int kProjTokensPerBlock = kProjThreads / 64 * kProjTokensPerWave * kProjIters;
 
-template <int D, int MB>
+// Round-to-nearest-even of two floats to the output type, packed into one dword.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_out(float lo, float hi) {
+    return F16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+}
+
+template <int D, int MB, bool F16>
 __global__ __launch_bounds__(kProjThreads) void project_bf16_kernel(
     const bf16_t* __restrict__ X0, const bf16_t* __restrict__ X1, const bf16_t* __restrict__ P,
-    bf16_t* __restrict__ Y0, bf16_t* __restrict__ Y1, int N, int BH, int H, int m, int out_stride,
-    int out_cols, float out_scale0, float out_scale1) {
+    uint16_t* __restrict__ Y0, uint16_t* __restrict__ Y1, int N, int BH, int H, int m,
+    int out_stride, int out_cols, float out_scale0, float out_scale1) {
     constexpr int PROW = D + 8;  // LDS row pitch in bf16: 16 bytes of padding per row
     constexpr int KS = D / 16;   // MFMA k-steps over the input features
     __shared__ __attribute__((aligned(16))) bf16_t Pt[MB * 32 * PROW];
@@ -36,7 +43,7 @@ __global__ __launch_bounds__(kProjThreads) void project_bf16_kernel(
     const int z = zbh / BH;
     const int bh = zbh - z * BH;
     const bf16_t* X = z ? X1 : X0;
-    bf16_t* Y = z ? Y1 : Y0;
+    uint16_t* Y = z ? Y1 : Y0;
     const float out_scale = z ? out_scale1 : out_scale0;
     const int h = bh % H;
     const int tid = threadIdx.x;
@@ -51,7 +58,7 @@ __global__ __launch_bounds__(kProjThreads) void project_bf16_kernel(
 
     const int wave = tid / 64, lane = tid % 64, col = lane % 32, half = lane / 32;
     const bf16_t* Xh = X + (size_t)bh * N * D;
-    bf16_t* Yh = Y + (size_t)bh * N * out_stride;
+    uint16_t* Yh = Y + (size_t)bh * N * out_stride;
     const bool vec_store = (out_stride % 4) == 0;
 
 #pragma unroll 1
@@ -78,49 +85,59 @@ __global__ __launch_bounds__(kProjThreads) void project_bf16_kernel(
             for (int g = 0; g < 4; ++g) {
                 const int c0 = mb * 32 + 8 * g + 4 * half;
                 if (c0 >= out_cols) continue;
-                bf16_t* dst = Yh + (size_t)tok * out_stride + c0;
+                uint16_t* dst = Yh + (size_t)tok * out_stride + c0;
+                uint2 w;
+                w.x = pack_out<F16>(acc[4 * g + 0] * out_scale, acc[4 * g + 1] * out_scale);
+                w.y = pack_out<F16>(acc[4 * g + 2] * out_scale, acc[4 * g + 3] * out_scale);
                 if (vec_store && c0 + 4 <= out_cols) {
-                    uint2 w;
-                    w.x = pack_bf16x2(acc[4 * g + 0] * out_scale, acc[4 * g + 1] * out_scale);
-                    w.y = pack_bf16x2(acc[4 * g + 2] * out_scale, acc[4 * g + 3] * out_scale);
                     *reinterpret_cast<uint2*>(dst) = w;
                 } else {
+                    const uint16_t v[4] = {(uint16_t)(w.x & 0xffffu), (uint16_t)(w.x >> 16),
+                                           (uint16_t)(w.y & 0xffffu), (uint16_t)(w.y >> 16)};
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (c0 + r < out_cols) dst[r] = (bf16_t)(acc[4 * g + r] * out_scale);
+                        if (c0 + r < out_cols) dst[r] = v[r];
                 }
             }
         }
     }
 }
 
-template <int D, int MB>
+template <int D, int MB, bool F16>
 hipError_t launch(const void* X0, const void* X1, const void* P, void* Y0, void* Y1, int nz,
                   int BH, int H, int N, int m, int out_stride, int out_cols, float s0, float s1,
                   hipStream_t stream) {
     const long long nblk = (N + kProjTokensPerBlock - 1) / kProjTokensPerBlock;
     const long long blocks = nblk * BH * nz;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    project_bf16_kernel<D, MB><<<dim3((unsigned)blocks), kProjThreads, 0, stream>>>(
+    project_bf16_kernel<D, MB, F16><<<dim3((unsigned)blocks), kProjThreads, 0, stream>>>(
         static_cast<const bf16_t*>(X0), static_cast<const bf16_t*>(X1),
-        static_cast<const bf16_t*>(P), static_cast<bf16_t*>(Y0), static_cast<bf16_t*>(Y1), N,
-        BH, H, m, out_stride, out_cols, s0, s1);
+        static_cast<const bf16_t*>(P), static_cast<uint16_t*>(Y0), static_cast<uint16_t*>(Y1),
+        N, BH, H, m, out_stride, out_cols, s0, s1);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool F16>
 hipError_t launch_d(const void* X0, const void* X1, const void* P, void* Y0, void* Y1, int nz,
                     int BH, int H, int N, int m, int out_stride, int out_cols, float s0,
                     float s1, hipStream_t stream) {
     const int cols = out_cols > m ? out_cols : m;
     const int mb = (cols + 31) / 32;
     switch (mb) {
-        case 1: return launch<D, 1>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, s0, s1, stream);
-        case 2: return launch<D, 2>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, s0, s1, stream);
+        case 1: return launch<D, 1, F16>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, s0, s1, stream);
+        case 2: return launch<D, 2, F16>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, s0, s1, stream);
         case 3:
-        case 4: return launch<D, 4>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, s0, s1, stream);
+        case 4: return launch<D, 4, F16>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, s0, s1, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int D>
+hipError_t launch_t(const void* X0, const void* X1, const void* P, void* Y0, void* Y1, int nz,
+                    int BH, int H, int N, int m, int out_stride, int out_cols, float s0,
+                    float s1, bool out_f16, hipStream_t stream) {
+    return out_f16 ? launch_d<D, true>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, s0, s1, stream)
+                   : launch_d<D, false>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, s0, s1, stream);
 }
 
 }  // namespace
@@ -128,10 +145,10 @@ hipError_t launch_d(const void* X0, const void* X1, const void* P, void* Y0, voi
 hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, void* Y0,
                                void* Y1, int nz, int BH, int H, int N, int d, int m,
                                int out_stride, int out_cols, float out_scale0,
-                               float out_scale1, hipStream_t stream) {
+                               float out_scale1, bool out_f16, hipStream_t stream) {
     switch (d) {
-        case 64: return launch_d<64>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, out_scale0, out_scale1, stream);
-        case 128: return launch_d<128>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, out_scale0, out_scale1, stream);
+        case 64: return launch_t<64>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, out_scale0, out_scale1, out_f16, stream);
+        case 128: return launch_t<128>(X0, X1, P, Y0, Y1, nz, BH, H, N, m, out_stride, out_cols, out_scale0, out_scale1, out_f16, stream);
         default: return hipErrorInvalidValue;
     }
 }
