@@ -37,6 +37,79 @@ constexpr int kBR = 128;  // queries per workgroup (4 waves x 32)
 constexpr int kBC = 64;   // keys per tile
 constexpr float kTau = 8.0f;
 
+template <int BYTES>
+struct VecOf;
+template <>
+struct VecOf<16> {
+    using T = u32x4;
+};
+template <>
+struct VecOf<8> {
+    using T = u32x2;
+};
+
+// Global -> register -> LDS staging of one key tile: 64 projected-key rows (fp16, LDS rows
+// of MP + 8) and the matching 64 V rows, transposed to V^T (bf16, LDS rows of kBC + 4).
+// Every thread moves the same number of bytes, so the loads need no branches: rows past N
+// are clamped to row N-1 (their scores are masked, so their weights are exactly 0).
+template <int MP, int DV>
+struct Stage {
+    static constexpr int KROW = MP + 8;
+    static constexpr int VROW = kBC + 4;
+    static constexpr int KBYTES = kBC * MP * 2 / kThreads;  // projected-key bytes per thread
+    static constexpr int KVEC = KBYTES < 16 ? KBYTES : 16;  // bytes per load
+    static constexpr int KLD = KBYTES / KVEC;               // loads per thread (1, 2 or 4)
+    static constexpr int KPR = MP * 2 / KVEC;               // loads per key row
+    static constexpr int VCOLS = DV / 16;                   // V columns per thread (x 4 keys)
+    static constexpr int VCG = DV / VCOLS;                  // column groups (16)
+    using KVec = typename VecOf<KVEC>::T;
+    using VVec = typename VecOf<VCOLS * 2>::T;
+
+    __device__ __forceinline__ static void load(KVec (&kreg)[KLD], VVec (&vreg)[4],
+                                                const uint16_t* Kh, const bf16_t* Vh, int k0,
+                                                int N, int tid, int vcg, int vkg) {
+#pragma unroll
+        for (int i = 0; i < KLD; ++i) {
+            const int c = tid + i * kThreads;
+            const int key = min(k0 + c / KPR, N - 1);
+            kreg[i] = *reinterpret_cast<const KVec*>(Kh + (size_t)key * MP + (c % KPR) * (KVEC / 2));
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = min(k0 + vkg * 4 + r, N - 1);
+            vreg[r] = *reinterpret_cast<const VVec*>(Vh + (size_t)key * DV + vcg * VCOLS);
+        }
+    }
+
+    __device__ __forceinline__ static void store(const KVec (&kreg)[KLD], const VVec (&vreg)[4],
+                                                 uint16_t* Ks, uint16_t* Vs, int tid, int vcg,
+                                                 int vkg) {
+#pragma unroll
+        for (int i = 0; i < KLD; ++i) {
+            const int c = tid + i * kThreads;
+            *reinterpret_cast<KVec*>(Ks + (c / KPR) * KROW + (c % KPR) * (KVEC / 2)) = kreg[i];
+        }
+        // 4 keys x VCOLS columns -> VCOLS rows of V^T holding 4 keys (8 bytes) each.
+#pragma unroll
+        for (int a = 0; a < VCOLS / 2; ++a) {
+            const uint32_t w0 = dword(vreg[0], a), w1 = dword(vreg[1], a);
+            const uint32_t w2 = dword(vreg[2], a), w3 = dword(vreg[3], a);
+            uint2 lo, hi;
+            lo.x = (w0 & 0xffffu) | (w1 << 16);
+            lo.y = (w2 & 0xffffu) | (w3 << 16);
+            hi.x = (w0 >> 16) | (w1 & 0xffff0000u);
+            hi.y = (w2 >> 16) | (w3 & 0xffff0000u);
+            *reinterpret_cast<uint2*>(Vs + (vcg * VCOLS + 2 * a) * VROW + vkg * 4) = lo;
+            *reinterpret_cast<uint2*>(Vs + (vcg * VCOLS + 2 * a + 1) * VROW + vkg * 4) = hi;
+        }
+    }
+
+    template <typename Vec>
+    __device__ __forceinline__ static uint32_t dword(const Vec& v, int a) {
+        return v[a];
+    }
+};
+
 template <int MP, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Kt, const bf16_t* __restrict__ V,
@@ -46,10 +119,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     constexpr int VROW = kBC + 4;        // LDS pitch of a V^T row (bf16)
     constexpr int K_ELEMS = kBC * KROW;  // one K tile
     constexpr int V_ELEMS = DV * VROW;   // one V^T tile
-    constexpr int KCHUNKS = kBC * MP / 8;                  // 16-byte chunks per K tile
-    constexpr int KPT = (KCHUNKS + kThreads - 1) / kThreads;
-    constexpr int VSLOTS = (kBC / 4) * (DV / 8);           // 4 keys x 8 dv per slot
-    constexpr int DB = DV / 32;                            // 32-row blocks of V^T / O^T
+    constexpr int DB = DV / 32;          // 32-row blocks of V^T / O^T
 
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (K_ELEMS + V_ELEMS)];
 
@@ -87,57 +157,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const int ntiles = (kend + kBC - 1) / kBC;
 
     // ---- global -> register -> LDS staging --------------------------------------------
-    uint4 kreg[KPT];
-    uint4 vreg[4];
-    auto load_tile = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + i * kThreads;
-            kreg[i] = make_uint4(0, 0, 0, 0);
-            if (c < KCHUNKS) {
-                const int key = c / (MP / 8), cc = c % (MP / 8);
-                if (k0 + key < N) kreg[i] = load16(Kh + (size_t)(k0 + key) * MP + cc * 8);
-            }
-        }
-        if (tid < VSLOTS) {
-            const int c8 = tid % (DV / 8), kg = tid / (DV / 8);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = k0 + kg * 4 + r;
-                vreg[r] = key < N ? load16(Vh + (size_t)key * DV + c8 * 8) : make_uint4(0, 0, 0, 0);
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        uint16_t* Ks = lds + buf * (K_ELEMS + V_ELEMS);
-        uint16_t* Vs = Ks + K_ELEMS;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + i * kThreads;
-            if (c < KCHUNKS) {
-                const int key = c / (MP / 8), cc = c % (MP / 8);
-                *reinterpret_cast<uint4*>(Ks + key * KROW + cc * 8) = kreg[i];
-            }
-        }
-        if (tid < VSLOTS) {
-            // 4 keys x 8 dv in registers -> 8 rows of V^T, 4 keys (8 bytes) each.
-            const int c8 = tid % (DV / 8), kg = tid / (DV / 8);
-            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-            const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-            const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-            const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                uint2 lo, hi;
-                lo.x = (w0[a] & 0xffffu) | (w1[a] << 16);
-                lo.y = (w2[a] & 0xffffu) | (w3[a] << 16);
-                hi.x = (w0[a] >> 16) | (w1[a] & 0xffff0000u);
-                hi.y = (w2[a] >> 16) | (w3[a] & 0xffff0000u);
-                *reinterpret_cast<uint2*>(Vs + (c8 * 8 + 2 * a) * VROW + kg * 4) = lo;
-                *reinterpret_cast<uint2*>(Vs + (c8 * 8 + 2 * a + 1) * VROW + kg * 4) = hi;
-            }
-        }
-    };
+    using St = Stage<MP, DV>;
+    typename St::KVec kreg[St::KLD];
+    typename St::VVec vreg[4];
+    const int vcg = tid % St::VCG, vkg = tid / St::VCG;
 
     // ---- per-lane softmax state (query myq) --------------------------------------------
     f32x16 acc[DB];
@@ -147,15 +170,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     float lsum = 0.0f;   // partial normaliser over this half-wave's keys
     f32x16 cinit = f32x16_fill(0.0f);  // -mu, the score accumulator's start value
 
-    load_tile(0);
-    store_tile(0);
+    St::load(kreg, vreg, Kh, Vh, 0, N, tid, vcg, vkg);
+    St::store(kreg, vreg, lds, lds + K_ELEMS, tid, vcg, vkg);
     __syncthreads();
 
 #pragma unroll 1
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * kBC;
         const bool more = t + 1 < ntiles;
-        if (more) load_tile(k0 + kBC);
+        if (more) St::load(kreg, vreg, Kh, Vh, k0 + kBC, N, tid, vcg, vkg);
 
         const uint16_t* Ks = lds + (t & 1) * (K_ELEMS + V_ELEMS);
         const uint16_t* Vs = Ks + K_ELEMS;
@@ -188,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
-            tmax = fmaxf(tmax, swap_halves(tmax));
+            tmax = halves_max(tmax);
             // The first tile sets mu to its maximum (key 0 is unmasked for every query, so
             // that maximum is finite, and nothing has been accumulated yet); later tiles move
             // mu only past the kTau slack, rescaling what was accumulated by 2^-delta <= 1.
@@ -228,29 +251,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 }
             }
             // O^T += V^T . p^T. Slot 8*half + j of k-step tt in key block kb holds key
-            // kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, as in the score accumulator.
+            // kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, as in the score accumulator. The V^T
+            // fragments of block db+1 are read while block db's MFMAs run.
+            uint4 vf[2][4];
+            auto read_vfrags = [&](int db, uint4* f) {
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    const uint16_t* vp = Vs + (db * 32 + col) * VROW + (kt >> 1) * 32 + (kt & 1) * 16 + half * 4;
+                    const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+                    const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
+                    f[kt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+            };
+            read_vfrags(0, vf[0]);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
+                if (db + 1 < DB) read_vfrags(db + 1, vf[(db + 1) & 1]);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const uint16_t* vp = Vs + (db * 32 + col) * VROW + kb * 32 + tt * 16 + half * 4;
-                        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-                        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-                        const bf16x8 a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-                        acc[db] = mfma32x32x16(a, pf[kb][tt], acc[db]);
-                    }
-                }
+                for (int kt = 0; kt < 4; ++kt)
+                    acc[db] = mfma32x32x16(as_bf16x8(vf[db & 1][kt]), pf[kt >> 1][kt & 1], acc[db]);
             }
         }
 
-        if (more) store_tile((t + 1) & 1);
+        if (more) {
+            uint16_t* Kn = lds + ((t + 1) & 1) * (K_ELEMS + V_ELEMS);
+            St::store(kreg, vreg, Kn, Kn + K_ELEMS, tid, vcg, vkg);
+        }
         __syncthreads();
     }
 
     // ---- epilogue: O = O_acc / l (both half-waves' key subsets summed) ------------------
-    const float ltot = lsum + swap_halves(lsum);
+    const float ltot = halves_sum(lsum);
     const float inv = 1.0f / ltot;
     if (myq < N) {
         const size_t row = (size_t)bh * N + myq;

@@ -18,6 +18,10 @@ typedef __bf16 bf16_t;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+// Native vectors for raw 16- and 8-byte moves (copies of HIP's uint4 struct lower to memcpy,
+// which keeps arrays of them out of registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -62,7 +66,15 @@ __device__ __forceinline__ f32x16 f32x16_fill(float x) {
     return v;
 }
 
-// Value of the other half-wave's lane (l xor 32).
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+// max / sum of x over lanes l and l xor 32, in every lane (one v_permlane32_swap: the two
+// results hold the low and the high half-wave's values side by side).
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace spa
