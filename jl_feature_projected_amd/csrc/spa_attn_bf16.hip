@@ -49,19 +49,30 @@ struct VecOf<8> {
 };
 
 // Global -> register -> LDS staging of one key tile: 64 projected-key rows (fp16, LDS rows
-// of MP + 8) and the matching 64 V rows, transposed to V^T (bf16, LDS rows of kBC + 4).
+// of MP + 8) and the matching 64 V rows, transposed to V^T (bf16, LDS rows of kVRow).
 // Every thread moves the same number of bytes, so the loads need no branches: rows past N
 // are clamped to row N-1 (their scores are masked, so their weights are exactly 0).
+//
+// V^T layout. A thread loads 4 consecutive keys (one key group) x VCOLS columns and writes
+// VCOLS rows of V^T, 8 bytes each. Consecutive lanes take consecutive key groups, so the 16
+// lanes of one LDS write cycle hit one row at 16 different 8-byte slots (no bank conflict).
+// Inside a row, key group g is stored at slot kgslot(g), which swaps bits 0 and 1 of g: the
+// two key groups one PV MFMA lane needs (g and g + 2, see the PV step) become adjacent, so
+// the operand is a single 16-byte read; rows are 144 bytes apart, so 8 lanes reading 8
+// consecutive rows cover the 32 banks once.
+constexpr int kVRow = kBC + 8;  // V^T row pitch in bf16 elements (144 bytes)
+
+__device__ __forceinline__ int kgslot(int g) { return (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1); }
+
 template <int MP, int DV>
 struct Stage {
     static constexpr int KROW = MP + 8;
-    static constexpr int VROW = kBC + 4;
     static constexpr int KBYTES = kBC * MP * 2 / kThreads;  // projected-key bytes per thread
     static constexpr int KVEC = KBYTES < 16 ? KBYTES : 16;  // bytes per load
     static constexpr int KLD = KBYTES / KVEC;               // loads per thread (1, 2 or 4)
     static constexpr int KPR = MP * 2 / KVEC;               // loads per key row
     static constexpr int VCOLS = DV / 16;                   // V columns per thread (x 4 keys)
-    static constexpr int VCG = DV / VCOLS;                  // column groups (16)
+    static constexpr int KG = kBC / 4;                      // key groups per tile (16)
     using KVec = typename VecOf<KVEC>::T;
     using VVec = typename VecOf<VCOLS * 2>::T;
 
@@ -89,24 +100,19 @@ struct Stage {
             const int c = tid + i * kThreads;
             *reinterpret_cast<KVec*>(Ks + (c / KPR) * KROW + (c % KPR) * (KVEC / 2)) = kreg[i];
         }
-        // 4 keys x VCOLS columns -> VCOLS rows of V^T holding 4 keys (8 bytes) each.
+        // 4 keys x VCOLS columns -> VCOLS rows of V^T holding these 4 keys (8 bytes) each.
+        uint16_t* dst = Vs + vcg * VCOLS * kVRow + kgslot(vkg) * 4;
 #pragma unroll
         for (int a = 0; a < VCOLS / 2; ++a) {
-            const uint32_t w0 = dword(vreg[0], a), w1 = dword(vreg[1], a);
-            const uint32_t w2 = dword(vreg[2], a), w3 = dword(vreg[3], a);
-            uint2 lo, hi;
+            const uint32_t w0 = vreg[0][a], w1 = vreg[1][a], w2 = vreg[2][a], w3 = vreg[3][a];
+            u32x2 lo, hi;
             lo.x = (w0 & 0xffffu) | (w1 << 16);
             lo.y = (w2 & 0xffffu) | (w3 << 16);
             hi.x = (w0 >> 16) | (w1 & 0xffff0000u);
             hi.y = (w2 >> 16) | (w3 & 0xffff0000u);
-            *reinterpret_cast<uint2*>(Vs + (vcg * VCOLS + 2 * a) * VROW + vkg * 4) = lo;
-            *reinterpret_cast<uint2*>(Vs + (vcg * VCOLS + 2 * a + 1) * VROW + vkg * 4) = hi;
+            *reinterpret_cast<u32x2*>(dst + (2 * a) * kVRow) = lo;
+            *reinterpret_cast<u32x2*>(dst + (2 * a + 1) * kVRow) = hi;
         }
-    }
-
-    template <typename Vec>
-    __device__ __forceinline__ static uint32_t dword(const Vec& v, int a) {
-        return v[a];
     }
 };
 
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     void* __restrict__ O, float* __restrict__ lse, int N, int nqb, int out_f32) {
     constexpr int KS = MP / 16;          // score MFMA k-steps
     constexpr int KROW = MP + 8;         // LDS pitch of a projected-key row (fp16)
-    constexpr int VROW = kBC + 4;        // LDS pitch of a V^T row (bf16)
+    constexpr int VROW = kVRow;          // LDS pitch of a V^T row (bf16)
     constexpr int K_ELEMS = kBC * KROW;  // one K tile
     constexpr int V_ELEMS = DV * VROW;   // one V^T tile
     constexpr int DB = DV / 32;          // 32-row blocks of V^T / O^T
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     using St = Stage<MP, DV>;
     typename St::KVec kreg[St::KLD];
     typename St::VVec vreg[4];
-    const int vcg = tid % St::VCG, vkg = tid / St::VCG;
+    const int vkg = tid % St::KG, vcg = tid / St::KG;  // key group, column group
 
     // ---- per-lane softmax state (query myq) --------------------------------------------
     f32x16 acc[DB];
@@ -253,14 +259,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
             // O^T += V^T . p^T. Slot 8*half + j of k-step tt in key block kb holds key
             // kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, as in the score accumulator. The V^T
             // fragments of block db+1 are read while block db's MFMAs run.
-            uint4 vf[2][4];
-            auto read_vfrags = [&](int db, uint4* f) {
+            u32x4 vf[2][4];
+            auto read_vfrags = [&](int db, u32x4* f) {
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
-                    const uint16_t* vp = Vs + (db * 32 + col) * VROW + (kt >> 1) * 32 + (kt & 1) * 16 + half * 4;
-                    const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-                    f[kt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    // key groups g = 8*kb + 4*tt + half (slots 0-3) and g + 2 (slots 4-7)
+                    const int g = 8 * (kt >> 1) + 4 * (kt & 1) + half;
+                    f[kt] = *reinterpret_cast<const u32x4*>(Vs + (db * 32 + col) * VROW + kgslot(g) * 4);
                 }
             };
             read_vfrags(0, vf[0]);
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 if (db + 1 < DB) read_vfrags(db + 1, vf[(db + 1) & 1]);
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
-                    acc[db] = mfma32x32x16(as_bf16x8(vf[db & 1][kt]), pf[kt >> 1][kt & 1], acc[db]);
+                    acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, vf[db & 1][kt]), pf[kt >> 1][kt & 1], acc[db]);
             }
         }
 
