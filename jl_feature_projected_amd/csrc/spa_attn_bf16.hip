@@ -10,9 +10,9 @@
 // design 3, with the dense projected contraction in place of the sparse intersection.
 //
 // Work decomposition: a workgroup of 4 waves owns 128 queries of one (batch, head); each
-// wave owns 32 of them. Key tiles of 64 are staged in LDS (projected keys as rows, V
-// transposed), double buffered, with the next tile's global loads issued before the current
-// tile's math. Per tile and wave:
+// wave owns 32 of them. Key tiles of 64 are copied HBM -> LDS by buffer loads that write LDS
+// directly (no registers, no VALU; rows past N read as zero), double buffered: the next
+// tile's copy is issued before the current tile's math. Per tile and wave:
 //   scores^T (64 keys x 32 queries) = Kt_tile . Qt^T on 32x32x16 MFMA. The accumulator starts
 //     at -mu (the running row maximum), so the MFMA output is already score - mu; a lane
 //     owns one query and 16 keys per 32-key block, so row reductions are in-lane plus one
@@ -21,7 +21,13 @@
 //     (base-2 units), which keeps every weight below 2^kTau; all else is exp2 on the VALU.
 //   O^T (dv x 32 queries) += V^T_tile . p^T on 32x32x16 MFMA. The weights p go from the
 //     score accumulator straight into the B operand: the k-order of the contraction is the
-//     key order the score layout already has, and V^T is read from LDS in that same order.
+//     key order the score layout already has. The V tile stays row-major in LDS and the
+//     A operand is read with ds_read_b64_tr_b16: within each 16-lane group, lane 4a+b
+//     receives element b of the 8-byte rows that lanes a, a+4, a+8, a+12 address, so lane s
+//     addressing V[r0 + s/4][c0 + 4(s%4)] gives lane i the keys r0..r0+3 of column c0 + i.
+// LDS tiles are XOR-swizzled in 16-byte chunks (the copy picks, per lane, which global chunk
+// lands in its LDS slot), so neither the score-operand reads nor the transposed reads hit
+// a bank twice.
 // Queries arrive pre-scaled by scale*log2(e), so exp2 of the MFMA output is the softmax
 // numerator. The projected queries and keys are fp16 (the score MFMA runs in fp16, whose
 // 11-bit significand keeps the score error small); V and the weights are bf16. The
@@ -33,101 +39,56 @@ namespace spa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int kBR = 128;  // queries per workgroup (4 waves x 32)
 constexpr int kBC = 64;   // keys per tile
 constexpr float kTau = 8.0f;
 
-template <int BYTES>
-struct VecOf;
-template <>
-struct VecOf<16> {
-    using T = u32x4;
-};
-template <>
-struct VecOf<8> {
-    using T = u32x2;
-};
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// Global -> register -> LDS staging of one key tile: 64 projected-key rows (fp16, LDS rows
-// of MP + 8) and the matching 64 V rows, transposed to V^T (bf16, LDS rows of kVRow).
-// Every thread moves the same number of bytes, so the loads need no branches: rows past N
-// are clamped to row N-1 (their scores are masked, so their weights are exactly 0).
-//
-// V^T layout. A thread loads 4 consecutive keys (one key group) x VCOLS columns and writes
-// VCOLS rows of V^T, 8 bytes each. Consecutive lanes take consecutive key groups, so the 16
-// lanes of one LDS write cycle hit one row at 16 different 8-byte slots (no bank conflict).
-// Inside a row, key group g is stored at slot kgslot(g), which swaps bits 0 and 1 of g: the
-// two key groups one PV MFMA lane needs (g and g + 2, see the PV step) become adjacent, so
-// the operand is a single 16-byte read; rows are 144 bytes apart, so 8 lanes reading 8
-// consecutive rows cover the 32 banks once.
-constexpr int kVRow = kBC + 8;  // V^T row pitch in bf16 elements (144 bytes)
+// Buffer descriptor over [base, base + bytes): loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
 
-__device__ __forceinline__ int kgslot(int g) { return (g & ~3) | ((g & 1) << 1) | ((g >> 1) & 1); }
+// 16 bytes per lane from buffer offset voff straight into LDS at dst + 16 * lane (dst is
+// wave-uniform). The body exists in the device pass only: the host pass cannot parse this
+// builtin, and a kernel that calls it directly loses its host-side launch stub.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+#endif
+}
 
-template <int MP, int DV>
-struct Stage {
-    static constexpr int KROW = MP + 8;
-    static constexpr int KBYTES = kBC * MP * 2 / kThreads;  // projected-key bytes per thread
-    static constexpr int KVEC = KBYTES < 16 ? KBYTES : 16;  // bytes per load
-    static constexpr int KLD = KBYTES / KVEC;               // loads per thread (1, 2 or 4)
-    static constexpr int KPR = MP * 2 / KVEC;               // loads per key row
-    static constexpr int VCOLS = DV / 16;                   // V columns per thread (x 4 keys)
-    static constexpr int KG = kBC / 4;                      // key groups per tile (16)
-    using KVec = typename VecOf<KVEC>::T;
-    using VVec = typename VecOf<VCOLS * 2>::T;
-
-    __device__ __forceinline__ static void load(KVec (&kreg)[KLD], VVec (&vreg)[4],
-                                                const uint16_t* Kh, const bf16_t* Vh, int k0,
-                                                int N, int tid, int vcg, int vkg) {
-#pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int c = tid + i * kThreads;
-            const int key = min(k0 + c / KPR, N - 1);
-            kreg[i] = *reinterpret_cast<const KVec*>(Kh + (size_t)key * MP + (c % KPR) * (KVEC / 2));
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = min(k0 + vkg * 4 + r, N - 1);
-            vreg[r] = *reinterpret_cast<const VVec*>(Vh + (size_t)key * DV + vcg * VCOLS);
-        }
-    }
-
-    __device__ __forceinline__ static void store(const KVec (&kreg)[KLD], const VVec (&vreg)[4],
-                                                 uint16_t* Ks, uint16_t* Vs, int tid, int vcg,
-                                                 int vkg) {
-#pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int c = tid + i * kThreads;
-            *reinterpret_cast<KVec*>(Ks + (c / KPR) * KROW + (c % KPR) * (KVEC / 2)) = kreg[i];
-        }
-        // 4 keys x VCOLS columns -> VCOLS rows of V^T holding these 4 keys (8 bytes) each.
-        uint16_t* dst = Vs + vcg * VCOLS * kVRow + kgslot(vkg) * 4;
-#pragma unroll
-        for (int a = 0; a < VCOLS / 2; ++a) {
-            const uint32_t w0 = vreg[0][a], w1 = vreg[1][a], w2 = vreg[2][a], w3 = vreg[3][a];
-            u32x2 lo, hi;
-            lo.x = (w0 & 0xffffu) | (w1 << 16);
-            lo.y = (w2 & 0xffffu) | (w3 << 16);
-            hi.x = (w0 >> 16) | (w1 & 0xffff0000u);
-            hi.y = (w2 >> 16) | (w3 & 0xffff0000u);
-            *reinterpret_cast<u32x2*>(dst + (2 * a) * kVRow) = lo;
-            *reinterpret_cast<u32x2*>(dst + (2 * a + 1) * kVRow) = hi;
-        }
-    }
-};
+// 16-byte chunk swizzles. K tile: rows of MP*2 bytes; 8 lanes reading chunk q of 8
+// consecutive rows must land on 8 different 4-bank windows. V tile: rows of DV*2 bytes (a
+// multiple of 128); the 4 rows x 2 chunks one 16-lane transposed read touches must land on
+// 8 different windows.
+template <int MP>
+__device__ __forceinline__ int kswz(int row) {
+    constexpr int rows_per_128 = MP >= 64 ? 1 : 64 / MP;
+    constexpr int span = MP / 8 < 8 ? MP / 8 : 8;
+    return (row / rows_per_128) % span;
+}
+__device__ __forceinline__ int vswz(int row) { return 2 * (row & 3); }
 
 template <int MP, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Kt, const bf16_t* __restrict__ V,
     void* __restrict__ O, float* __restrict__ lse, int N, int nqb, int out_f32) {
-    constexpr int KS = MP / 16;          // score MFMA k-steps
-    constexpr int KROW = MP + 8;         // LDS pitch of a projected-key row (fp16)
-    constexpr int VROW = kVRow;          // LDS pitch of a V^T row (bf16)
-    constexpr int K_ELEMS = kBC * KROW;  // one K tile
-    constexpr int V_ELEMS = DV * VROW;   // one V^T tile
-    constexpr int DB = DV / 32;          // 32-row blocks of V^T / O^T
+    constexpr int KS = MP / 16;              // score MFMA k-steps
+    constexpr int KCH = MP / 8;              // 16-byte chunks per projected-key row
+    constexpr int VCH = DV / 8;              // 16-byte chunks per V row
+    constexpr int K_BYTES = kBC * MP * 2;    // one K tile
+    constexpr int V_BYTES = kBC * DV * 2;    // one V tile
+    constexpr int BUF = K_BYTES + V_BYTES;   // one LDS buffer
+    constexpr int KINS = K_BYTES / 1024;     // 64-lane x 16-byte copies per K tile (2 .. 16)
+    constexpr int VINS = V_BYTES / 1024;     // ... per V tile (8 or 16)
+    constexpr int DB = DV / 32;              // 32-row blocks of V^T / O^T
+    static_assert(KINS >= 2 && VINS % kWaves == 0, "tile copy split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * (K_ELEMS + V_ELEMS)];
+    __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
     // Workgroup -> (head, query block). Workgroups are handed to the 8 XCDs round-robin;
     // when the grid divides evenly, XCD x gets a contiguous range of (head, block) pairs so
@@ -154,19 +115,72 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     f16x8 qf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (myq < N) v = load16(Qh + (size_t)myq * MP + ks * 16 + half * 8);
-        qf[ks] = as_f16x8(v);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (myq < N) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)myq * MP + ks * 16 + half * 8);
+        qf[ks] = __builtin_bit_cast(f16x8, v);
     }
 
     const int kend = CAUSAL ? min(N, q0 + kBR) : N;
     const int ntiles = (kend + kBC - 1) / kBC;
 
-    // ---- global -> register -> LDS staging --------------------------------------------
-    using St = Stage<MP, DV>;
-    typename St::KVec kreg[St::KLD];
-    typename St::VVec vreg[4];
-    const int vkg = tid % St::KG, vcg = tid / St::KG;  // key group, column group
+    // ---- HBM -> LDS tile copy ---------------------------------------------------------
+    // Copy j (64 lanes x 16 bytes) fills LDS chunks 64j .. 64j+63 of the tile; lane l writes
+    // chunk c = 64j + l, which holds global chunk (c % CH) ^ swizzle(row) of row c / CH.
+    // Copies are dealt round-robin to the waves (wave w issues j = w, w + 4, ...); the
+    // global byte offsets are fixed per lane, a tile only moves the descriptor's base.
+    constexpr int KPW = (KINS + kWaves - 1) / kWaves;  // K copies per wave (the last may idle)
+    constexpr int VPW = VINS / kWaves;                 // V copies per wave
+    uint32_t koff[KPW], voff[VPW];
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+        const int c = 64 * (wave + kWaves * i) + lane;
+        const int row = c / KCH;
+        koff[i] = row * MP * 2 + 16 * ((c % KCH) ^ kswz<MP>(row));
+    }
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+        const int c = 64 * (wave + kWaves * i) + lane;
+        const int row = c / VCH;
+        voff[i] = row * DV * 2 + 16 * ((c % VCH) ^ vswz(row));
+    }
+    auto copy_tile = [&](int k0, int buf) {
+        char* kdst = lds + buf * BUF;
+        char* vdst = kdst + K_BYTES;
+        const uint32_t rows_left = (uint32_t)(N - k0);
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kh + (size_t)k0 * MP, rows_left * MP * 2);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vh + (size_t)k0 * DV, rows_left * DV * 2);
+#pragma unroll
+        for (int i = 0; i < KPW; ++i) {
+            const int j = wave + kWaves * i;
+            if (j < KINS) copy16_to_lds(kr, kdst + 1024 * j, koff[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < VPW; ++i)
+            copy16_to_lds(vr, vdst + 1024 * (wave + kWaves * i), voff[i]);
+    };
+
+    // Per-lane LDS read offsets, fixed across tiles.
+    // Score operand: key row kb*32 + col, global chunk 2*ks + half.
+    int kread[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int row = kb * 32 + col;
+            kread[kb][ks] = row * MP * 2 + 16 * ((2 * ks + half) ^ kswz<MP>(row));
+        }
+    // PV operand (transposed read): lane s of 16-lane group (half, gc) addresses key row
+    // r0 + s/4 at column 32*db + 16*gc + 4*(s%4); r0 = kb*32 + 16*tt + 4*half, plus 8 for the
+    // second half of the k-slots. Every such row has row % 4 == s/4, so the row's swizzle is
+    // the same for all of this lane's reads: the swizzled chunk of each column block is
+    // precomputed, and (kb, tt, lo/hi) only add a row offset.
+    const int s16 = lane & 15, gc = (lane >> 4) & 1;
+    const int vrow0 = 4 * half + (s16 >> 2);
+    const int vbase = vrow0 * DV * 2 + 8 * (s16 & 1);  // + 2 * ((4*(s%4)) & 7)
+    int vchunk[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        vchunk[db] = vbase + 16 * ((4 * db + 2 * gc + ((s16 & 3) >> 1)) ^ vswz(vrow0));
 
     // ---- per-lane softmax state (query myq) --------------------------------------------
     f32x16 acc[DB];
@@ -176,18 +190,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     float lsum = 0.0f;   // partial normaliser over this half-wave's keys
     f32x16 cinit = f32x16_fill(0.0f);  // -mu, the score accumulator's start value
 
-    St::load(kreg, vreg, Kh, Vh, 0, N, tid, vcg, vkg);
-    St::store(kreg, vreg, lds, lds + K_ELEMS, tid, vcg, vkg);
+    copy_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
 #pragma unroll 1
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * kBC;
-        const bool more = t + 1 < ntiles;
-        if (more) St::load(kreg, vreg, Kh, Vh, k0 + kBC, N, tid, vcg, vkg);
+        if (t + 1 < ntiles) copy_tile(k0 + kBC, (t + 1) & 1);
 
-        const uint16_t* Ks = lds + (t & 1) * (K_ELEMS + V_ELEMS);
-        const uint16_t* Vs = Ks + K_ELEMS;
+        const char* Ks = lds + (t & 1) * BUF;
+        const char* Vs = Ks + K_BYTES;
 
         // Causal: a wave whose queries all precede the tile has nothing to do in it.
         if (!CAUSAL || k0 <= qw0 + 31) {
@@ -197,7 +210,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 s[kb] = cinit;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const f16x8 a = as_f16x8(load16(Ks + (kb * 32 + col) * KROW + ks * 16 + half * 8));
+                    const f16x8 a = __builtin_bit_cast(
+                        f16x8, *reinterpret_cast<const u32x4*>(Ks + kread[kb][ks]));
                     s[kb] = mfma32x32x16(a, qf[ks], s[kb]);
                 }
             }
@@ -244,44 +258,41 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    uint4 w;
-                    uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
+                    u32x4 w;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j]);
                         const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j + 1]);
-                        wp[j] = pack_bf16x2(p0, p1);
-                        lsum = add_bf16x2(wp[j], lsum);
+                        w[j] = pack_bf16x2(p0, p1);
+                        lsum = add_bf16x2(w[j], lsum);
                     }
-                    pf[kb][tt] = as_bf16x8(w);
+                    pf[kb][tt] = __builtin_bit_cast(bf16x8, w);
                 }
             }
             // O^T += V^T . p^T. Slot 8*half + j of k-step tt in key block kb holds key
-            // kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, as in the score accumulator. The V^T
-            // fragments of block db+1 are read while block db's MFMAs run.
-            u32x4 vf[2][4];
-            auto read_vfrags = [&](int db, u32x4* f) {
-#pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    // key groups g = 8*kb + 4*tt + half (slots 0-3) and g + 2 (slots 4-7)
-                    const int g = 8 * (kt >> 1) + 4 * (kt & 1) + half;
-                    f[kt] = *reinterpret_cast<const u32x4*>(Vs + (db * 32 + col) * VROW + kgslot(g) * 4);
-                }
-            };
-            read_vfrags(0, vf[0]);
+            // kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, as in the score accumulator.
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                if (db + 1 < DB) read_vfrags(db + 1, vf[(db + 1) & 1]);
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt)
-                    acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, vf[db & 1][kt]), pf[kt >> 1][kt & 1], acc[db]);
+                for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const char* vp = Vs + vchunk[db] + (kb * 32 + tt * 16) * DV * 2;
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4*)(vp));
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4*)(vp + 8 * DV * 2));
+                        const bf16x8 a = __builtin_bit_cast(
+                            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                        acc[db] = mfma32x32x16(a, pf[kb][tt], acc[db]);
+                    }
+                }
             }
         }
 
-        if (more) {
-            uint16_t* Kn = lds + ((t + 1) & 1) * (K_ELEMS + V_ELEMS);
-            St::store(kreg, vreg, Kn, Kn + K_ELEMS, tid, vcg, vkg);
-        }
+        // This wave's copies into the other buffer are done, and (barrier) everyone's are,
+        // and everyone has finished reading this buffer.
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
@@ -302,10 +313,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                     *reinterpret_cast<float4*>(dst) = make_float4(o0, o1, o2, o3);
                 } else {
                     bf16_t* dst = static_cast<bf16_t*>(O) + row * DV + c0;
-                    uint2 w;
+                    u32x2 w;
                     w.x = pack_bf16x2(o0, o1);
                     w.y = pack_bf16x2(o2, o3);
-                    *reinterpret_cast<uint2*>(dst) = w;
+                    *reinterpret_cast<u32x2*>(dst) = w;
                 }
             }
         }
