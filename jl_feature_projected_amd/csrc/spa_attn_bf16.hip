@@ -61,17 +61,26 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, char* ds
 #endif
 }
 
-// 16-byte chunk swizzles. K tile: rows of MP*2 bytes; 8 lanes reading chunk q of 8
-// consecutive rows must land on 8 different 4-bank windows. V tile: rows of DV*2 bytes (a
-// multiple of 128); the 4 rows x 2 chunks one 16-lane transposed read touches must land on
-// 8 different windows.
+// 16-byte chunk swizzles: LDS slot = global chunk ^ swizzle(row), a GF(2)-linear function of
+// the row's low bits. The tables were chosen (by exhaustive search over such functions) so
+// that every read pattern below touches each LDS bank once per service cycle, whether the
+// LDS serves 128 bytes per cycle over 32 banks or 256 bytes over 64:
+//   K tile (rows of MP*2 bytes), score operand: 8 or 16 consecutive rows, one chunk each;
+//   V tile (rows of DV*2 bytes), transposed read: 4 rows x 2 or 4 chunks.
 template <int MP>
 __device__ __forceinline__ int kswz(int row) {
-    constexpr int rows_per_128 = MP >= 64 ? 1 : 64 / MP;
-    constexpr int span = MP / 8 < 8 ? MP / 8 : 8;
-    return (row / rows_per_128) % span;
+    constexpr int b0 = MP == 16 ? 0 : MP == 32 ? 0 : 1;
+    constexpr int b1 = MP == 16 ? 0 : MP == 32 ? 1 : 2;
+    constexpr int b2 = MP == 16 ? 1 : MP == 32 ? 2 : 4;
+    constexpr int b3 = MP == 16 ? 1 : MP == 32 ? 1 : MP == 64 ? 1 : 8;
+    return (row & 1 ? b0 : 0) ^ (row & 2 ? b1 : 0) ^ (row & 4 ? b2 : 0) ^ (row & 8 ? b3 : 0);
 }
-__device__ __forceinline__ int vswz(int row) { return 2 * (row & 3); }
+template <int DV>
+__device__ __forceinline__ int vswz(int row) {
+    constexpr int b0 = DV == 64 ? 2 : 4;
+    constexpr int b1 = DV == 64 ? 4 : 10;
+    return (row & 1 ? b0 : 0) ^ (row & 2 ? b1 : 0);
+}
 
 template <int MP, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
@@ -141,7 +150,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     for (int i = 0; i < VPW; ++i) {
         const int c = 64 * (wave + kWaves * i) + lane;
         const int row = c / VCH;
-        voff[i] = row * DV * 2 + 16 * ((c % VCH) ^ vswz(row));
+        voff[i] = row * DV * 2 + 16 * ((c % VCH) ^ vswz<DV>(row));
     }
     auto copy_tile = [&](int k0, int buf) {
         char* kdst = lds + buf * BUF;
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     int vchunk[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-        vchunk[db] = vbase + 16 * ((4 * db + 2 * gc + ((s16 & 3) >> 1)) ^ vswz(vrow0));
+        vchunk[db] = vbase + 16 * ((4 * db + 2 * gc + ((s16 & 3) >> 1)) ^ vswz<DV>(vrow0));
 
     // ---- per-lane softmax state (query myq) --------------------------------------------
     f32x16 acc[DB];
