@@ -17,8 +17,14 @@
 //     at -mu (the running row maximum), so the MFMA output is already score - mu; a lane
 //     owns one query and 16 keys per 32-key block, so row reductions are in-lane plus one
 //     exchange with lane l xor 32.
-//   lazy online softmax: mu only moves when a tile's maximum exceeds it by more than kTau
-//     (base-2 units), which keeps every weight below 2^kTau; all else is exp2 on the VALU.
+//   softmax without a running maximum: by Cauchy-Schwarz every score of a row is at most
+//     M = |q_i| * max_j |k_j| (the key norm maxima come from the projection launch), so the
+//     accumulator starts at -M and exp2 of the MFMA output is a weight in (0, 1]: no max,
+//     no cross-lane exchange, no rescale, no branch in the tile loop. If M overshoots a
+//     row's true maximum so far that its normaliser falls below 2^-64 (weights would start
+//     to underflow), the whole workgroup recomputes its rows with an exact online softmax
+//     (lazy: the running maximum only moves when a tile exceeds it by more than kTau base-2
+//     units, rescaling what was accumulated).
 //   O^T (dv x 32 queries) += V^T_tile . p^T on 32x32x16 MFMA. The weights p go from the
 //     score accumulator straight into the B operand: the k-order of the contraction is the
 //     key order the score layout already has. The V tile stays row-major in LDS and the
@@ -32,6 +38,8 @@
 // numerator. The projected queries and keys are fp16 (the score MFMA runs in fp16, whose
 // 11-bit significand keeps the score error small); V and the weights are bf16. The
 // normaliser is summed from the bf16-rounded weights, the same values the PV MFMA consumes.
+#include <type_traits>
+
 #include "spa_device.h"
 #include "spa_internal.h"
 
@@ -44,20 +52,34 @@ constexpr int kBR = 128;  // queries per workgroup (4 waves x 32)
 constexpr int kBC = 64;   // keys per tile
 constexpr float kTau = 8.0f;
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// Buffer descriptor over [base, base + bytes): loads past the end return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+// Buffer descriptor over [base, base + bytes): loads past the end return zero. Raw buffer
+// (stride 0), 32-bit data format.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 r;
+    r.x = (uint32_t)a;
+    r.y = (uint32_t)(a >> 32) & 0xffffu;
+    r.z = bytes;
+    r.w = 0x00020000u;
+    return r;
 }
 
 // 16 bytes per lane from buffer offset voff straight into LDS at dst + 16 * lane (dst is
-// wave-uniform). The body exists in the device pass only: the host pass cannot parse this
-// builtin, and a kernel that calls it directly loses its host-side launch stub.
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t voff) {
+// wave-uniform). Issued as inline assembly so the compiler does not track it: it cannot
+// tell that the LDS it writes (the other buffer) is disjoint from the LDS the tile loop
+// reads, and would otherwise wait for the copy before the first read. The copy's completion
+// is awaited explicitly (vmcnt) before the barrier that hands the buffer over. Device pass
+// only: the host pass does not parse AMDGPU assembly constraints.
+__device__ __forceinline__ void copy16_to_lds(u32x4 rsrc, char* dst, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rsrc)
+                 : "m0");
 #endif
 }
 
@@ -85,7 +107,8 @@ __device__ __forceinline__ int vswz(int row) {
 template <int MP, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Kt, const bf16_t* __restrict__ V,
-    void* __restrict__ O, float* __restrict__ lse, int N, int nqb, int out_f32) {
+    const float* __restrict__ kmax, void* __restrict__ O, float* __restrict__ lse, int N, int nqb,
+    int out_f32) {
     constexpr int KS = MP / 16;              // score MFMA k-steps
     constexpr int KCH = MP / 8;              // 16-byte chunks per projected-key row
     constexpr int VCH = DV / 8;              // 16-byte chunks per V row
@@ -156,8 +179,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         char* kdst = lds + buf * BUF;
         char* vdst = kdst + K_BYTES;
         const uint32_t rows_left = (uint32_t)(N - k0);
-        const __amdgpu_buffer_rsrc_t kr = make_rsrc(Kh + (size_t)k0 * MP, rows_left * MP * 2);
-        const __amdgpu_buffer_rsrc_t vr = make_rsrc(Vh + (size_t)k0 * DV, rows_left * DV * 2);
+        const u32x4 kr = make_rsrc(Kh + (size_t)k0 * MP, rows_left * MP * 2);
+        const u32x4 vr = make_rsrc(Vh + (size_t)k0 * DV, rows_left * DV * 2);
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
             const int j = wave + kWaves * i;
@@ -191,122 +214,157 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     for (int db = 0; db < DB; ++db)
         vchunk[db] = vbase + 16 * ((4 * db + 2 * gc + ((s16 & 3) >> 1)) ^ vswz<DV>(vrow0));
 
+    // ---- score bound: M = |q| * max |k| over the key blocks this workgroup reads -------
+    float kmx = 0.0f;
+    {
+        const int nkb = proj_blocks(N);
+        const int kblocks = (kend + kProjBlockTokens - 1) / kProjBlockTokens;
+        for (int b = lane; b < kblocks; b += 64) kmx = fmaxf(kmx, kmax[(size_t)bh * nkb + b]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o, 64));
+    }
+    float qn2 = 0.0f;  // squared norm of the query as the MFMA sees it (fp16 values)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = (float)qf[ks][i];
+            qn2 += v * v;
+        }
+    // The slack covers fp16 rounding of the keys and fp32 rounding of norms and sums.
+    const float bound = sqrtf(halves_sum(qn2)) * kmx * (1.0f + 0x1p-8f) + 0x1p-8f;
+
     // ---- per-lane softmax state (query myq) --------------------------------------------
     f32x16 acc[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db] = f32x16_fill(0.0f);
-    float mu = 0.0f;     // running maximum (base-2 units), identical in both half-waves
-    float lsum = 0.0f;   // partial normaliser over this half-wave's keys
-    f32x16 cinit = f32x16_fill(0.0f);  // -mu, the score accumulator's start value
+    float mu;        // the exponent offset (base-2 units), identical in both half-waves
+    float lsum;      // partial normaliser over this half-wave's keys
 
-    copy_tile(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    auto tile_loop = [&](auto exact_tag) {
+        constexpr bool EXACT = decltype(exact_tag)::value;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = f32x16_fill(0.0f);
+        lsum = 0.0f;
+        mu = EXACT ? 0.0f : bound;
+        f32x16 cinit = f32x16_fill(-mu);  // the score accumulator's start value
+
+        copy_tile(0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
 
 #pragma unroll 1
-    for (int t = 0; t < ntiles; ++t) {
-        const int k0 = t * kBC;
-        if (t + 1 < ntiles) copy_tile(k0 + kBC, (t + 1) & 1);
+        for (int t = 0; t < ntiles; ++t) {
+            const int k0 = t * kBC;
+            if (t + 1 < ntiles) copy_tile(k0 + kBC, (t + 1) & 1);
 
-        const char* Ks = lds + (t & 1) * BUF;
-        const char* Vs = Ks + K_BYTES;
+            const char* Ks = lds + (t & 1) * BUF;
+            const char* Vs = Ks + K_BYTES;
 
-        // Causal: a wave whose queries all precede the tile has nothing to do in it.
-        if (!CAUSAL || k0 <= qw0 + 31) {
-            f32x16 s[2];
+            // Causal: a wave whose queries all precede the tile has nothing to do in it.
+            if (!CAUSAL || k0 <= qw0 + 31) {
+                f32x16 s[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = cinit;
+                for (int kb = 0; kb < 2; ++kb) {
+                    s[kb] = cinit;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const f16x8 a = __builtin_bit_cast(
-                        f16x8, *reinterpret_cast<const u32x4*>(Ks + kread[kb][ks]));
-                    s[kb] = mfma32x32x16(a, qf[ks], s[kb]);
-                }
-            }
-            // Masks: keys past N, and keys after the query under the causal mask.
-            const bool edge = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > qw0);
-            if (edge) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                        if (key >= N || (CAUSAL && key > myq)) s[kb][i] = -INFINITY;
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const f16x8 a = __builtin_bit_cast(
+                            f16x8, *reinterpret_cast<const u32x4*>(Ks + kread[kb][ks]));
+                        s[kb] = mfma32x32x16(a, qf[ks], s[kb]);
                     }
-            }
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
-            tmax = halves_max(tmax);
-            // The first tile sets mu to its maximum (key 0 is unmasked for every query, so
-            // that maximum is finite, and nothing has been accumulated yet); later tiles move
-            // mu only past the kTau slack, rescaling what was accumulated by 2^-delta <= 1.
-            if (t == 0 || __any(tmax > kTau)) {
-                const float delta = (t == 0) ? tmax : fmaxf(tmax, 0.0f);
-                if (t != 0) {
-                    const float alpha = __builtin_amdgcn_exp2f(-delta);
-                    lsum *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
                 }
-                mu += delta;
+                // Masks: keys past N, and keys after the query under the causal mask.
+                const bool edge = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > qw0);
+                if (edge) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) s[kb][i] -= delta;
-                cinit = f32x16_fill(-mu);
-            }
-            // Weights, their partial sum, and the bf16 B operands of the PV MFMA.
-            bf16x8 pf[2][2];
+                        for (int i = 0; i < 16; ++i) {
+                            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                            if (key >= N || (CAUSAL && key > myq)) s[kb][i] = -INFINITY;
+                        }
+                }
+                if constexpr (EXACT) {
+                    float tmax = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+                    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    u32x4 w;
+                        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
+                    tmax = halves_max(tmax);
+                    // The first tile sets mu to its maximum (key 0 is unmasked for every
+                    // query, so that maximum is finite, and nothing has been accumulated
+                    // yet); later tiles move mu only past the kTau slack, rescaling what was
+                    // accumulated by 2^-delta <= 1.
+                    if (t == 0 || __any(tmax > kTau)) {
+                        const float delta = (t == 0) ? tmax : fmaxf(tmax, 0.0f);
+                        if (t != 0) {
+                            const float alpha = __builtin_amdgcn_exp2f(-delta);
+                            lsum *= alpha;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j]);
-                        const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j + 1]);
-                        w[j] = pack_bf16x2(p0, p1);
-                        lsum = add_bf16x2(w[j], lsum);
+                            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                                for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+                        }
+                        mu += delta;
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) s[kb][i] -= delta;
+                        cinit = f32x16_fill(-mu);
                     }
-                    pf[kb][tt] = __builtin_bit_cast(bf16x8, w);
                 }
-            }
-            // O^T += V^T . p^T. Slot 8*half + j of k-step tt in key block kb holds key
-            // kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, as in the score accumulator.
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
+                // Weights, their partial sum, and the bf16 B operands of the PV MFMA.
+                bf16x8 pf[2][2];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt) {
-                        const char* vp = Vs + vchunk[db] + (kb * 32 + tt * 16) * DV * 2;
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(vp));
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(vp + 8 * DV * 2));
-                        const bf16x8 a = __builtin_bit_cast(
-                            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                        acc[db] = mfma32x32x16(a, pf[kb][tt], acc[db]);
+                        u32x4 w;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j]);
+                            const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j + 1]);
+                            w[j] = pack_bf16x2(p0, p1);
+                            lsum = add_bf16x2(w[j], lsum);
+                        }
+                        pf[kb][tt] = __builtin_bit_cast(bf16x8, w);
+                    }
+                }
+                // O^T += V^T . p^T. Slot 8*half + j of k-step tt in key block kb holds key
+                // kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, as in the score accumulator.
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt) {
+                            const char* vp = Vs + vchunk[db] + (kb * 32 + tt * 16) * DV * 2;
+                            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) i16x4*)(vp));
+                            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) i16x4*)(vp + 8 * DV * 2));
+                            const bf16x8 a = __builtin_bit_cast(
+                                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                            acc[db] = mfma32x32x16(a, pf[kb][tt], acc[db]);
+                        }
                     }
                 }
             }
-        }
 
-        // This wave's copies into the other buffer are done, and (barrier) everyone's are,
-        // and everyone has finished reading this buffer.
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+            // This wave's copies into the other buffer are done, and (barrier) everyone's
+            // are, and everyone has finished reading this buffer.
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    };
+
+    tile_loop(std::false_type{});
+    float ltot = halves_sum(lsum);
+    if (__syncthreads_or(myq < N && ltot < 0x1p-64f)) {
+        tile_loop(std::true_type{});
+        ltot = halves_sum(lsum);
     }
 
     // ---- epilogue: O = O_acc / l (both half-waves' key subsets summed) ------------------
-    const float ltot = halves_sum(lsum);
     const float inv = 1.0f / ltot;
     if (myq < N) {
         const size_t row = (size_t)bh * N + myq;
@@ -334,42 +392,43 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 }
 
 template <int MP, int DV, bool CAUSAL>
-hipError_t launch(const void* Qt, const void* Kt, const void* V, void* O, float* lse, int BH,
-                  int N, bool out_f32, hipStream_t stream) {
+hipError_t launch(const void* Qt, const void* Kt, const void* V, const float* kmax, void* O,
+                  float* lse, int BH, int N, bool out_f32, hipStream_t stream) {
     const int nqb = (N + kBR - 1) / kBR;
     attn_bf16_kernel<MP, DV, CAUSAL><<<dim3(nqb * BH), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(Qt), static_cast<const uint16_t*>(Kt),
-        static_cast<const bf16_t*>(V), O, lse, N, nqb, out_f32 ? 1 : 0);
+        static_cast<const bf16_t*>(V), kmax, O, lse, N, nqb, out_f32 ? 1 : 0);
     return hipGetLastError();
 }
 
 template <int MP, int DV>
-hipError_t launch_c(const void* Qt, const void* Kt, const void* V, void* O, float* lse, int BH,
-                    int N, bool causal, bool out_f32, hipStream_t stream) {
-    return causal ? launch<MP, DV, true>(Qt, Kt, V, O, lse, BH, N, out_f32, stream)
-                  : launch<MP, DV, false>(Qt, Kt, V, O, lse, BH, N, out_f32, stream);
+hipError_t launch_c(const void* Qt, const void* Kt, const void* V, const float* kmax, void* O,
+                    float* lse, int BH, int N, bool causal, bool out_f32, hipStream_t stream) {
+    return causal ? launch<MP, DV, true>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream)
+                  : launch<MP, DV, false>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream);
 }
 
 template <int MP>
-hipError_t launch_dv(const void* Qt, const void* Kt, const void* V, void* O, float* lse,
-                     int BH, int N, int dv, bool causal, bool out_f32, hipStream_t stream) {
+hipError_t launch_dv(const void* Qt, const void* Kt, const void* V, const float* kmax, void* O,
+                     float* lse, int BH, int N, int dv, bool causal, bool out_f32,
+                     hipStream_t stream) {
     switch (dv) {
-        case 64: return launch_c<MP, 64>(Qt, Kt, V, O, lse, BH, N, causal, out_f32, stream);
-        case 128: return launch_c<MP, 128>(Qt, Kt, V, O, lse, BH, N, causal, out_f32, stream);
+        case 64: return launch_c<MP, 64>(Qt, Kt, V, kmax, O, lse, BH, N, causal, out_f32, stream);
+        case 128: return launch_c<MP, 128>(Qt, Kt, V, kmax, O, lse, BH, N, causal, out_f32, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* V, void* O,
-                            float* lse, int BH, int N, int mp, int dv, bool causal,
+hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* V, const float* kmax,
+                            void* O, float* lse, int BH, int N, int mp, int dv, bool causal,
                             bool out_f32, hipStream_t stream) {
     switch (mp) {
-        case 16: return launch_dv<16>(Qt, Kt, V, O, lse, BH, N, dv, causal, out_f32, stream);
-        case 32: return launch_dv<32>(Qt, Kt, V, O, lse, BH, N, dv, causal, out_f32, stream);
-        case 64: return launch_dv<64>(Qt, Kt, V, O, lse, BH, N, dv, causal, out_f32, stream);
-        case 128: return launch_dv<128>(Qt, Kt, V, O, lse, BH, N, dv, causal, out_f32, stream);
+        case 16: return launch_dv<16>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, stream);
+        case 32: return launch_dv<32>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, stream);
+        case 64: return launch_dv<64>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, stream);
+        case 128: return launch_dv<128>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, stream);
         default: return hipErrorInvalidValue;
     }
 }

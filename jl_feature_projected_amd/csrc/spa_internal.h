@@ -10,21 +10,29 @@ namespace spa {
 // or 128 (the contraction depth of one 32x32x16 MFMA is 16).
 inline int padded_m(int m) { return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 : 128; }
 
+// Tokens per projection workgroup, and the number of such blocks per head.
+constexpr int kProjBlockTokens = 256;
+__host__ __device__ inline int proj_blocks(int N) { return (N + kProjBlockTokens - 1) / kProjBlockTokens; }
+
 // Projection of bf16 inputs on bf16 MFMA: Y_z[bh, n, c] = out_scale_z * sum_k X_z[bh, n, k]
 // P[h, k, c] for z < nz (nz = 1 or 2, e.g. queries and keys in one launch), accumulated in
 // fp32 and rounded once to fp16 (out_f16) or bf16. P is [H, d, m]; columns m <= c <
-// out_cols are written as zeros. Output rows are out_stride elements apart.
+// out_cols are written as zeros. Output rows are out_stride elements apart. If kmax is not
+// null, kmax[bh * proj_blocks(N) + b] receives the largest row norm (fp32, before rounding)
+// of Y1 over tokens b*256 .. b*256+255 of head bh.
 hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, void* Y0,
                                void* Y1, int nz, int BH, int H, int N, int d, int m,
                                int out_stride, int out_cols, float out_scale0,
-                               float out_scale1, bool out_f16, hipStream_t stream);
+                               float out_scale1, bool out_f16, float* kmax,
+                               hipStream_t stream);
 
 // Attention over projected inputs. Qt and Kt are fp16 [BH, N, mp] with zero columns past m
 // (score MFMA in fp16); Qt is pre-scaled by scale*log2(e) so the scores come out in base-2
 // exponent units. V is bf16 (weights x V MFMA in bf16). O is [BH, N, dv] in fp32 (out_f32)
-// or bf16; lse [BH, N] optional.
-hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* V, void* O,
-                            float* lse, int BH, int N, int mp, int dv, bool causal,
+// or bf16; lse [BH, N] optional. kmax holds the per-block key norm maxima written by the
+// projection launch.
+hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* V, const float* kmax,
+                            void* O, float* lse, int BH, int N, int mp, int dv, bool causal,
                             bool out_f32, hipStream_t stream);
 
 // fp32 projection: Y[bh, n, c] = out_scale * sum_k X[bh, n, k] P[h, k, c], fp32 FMAs.

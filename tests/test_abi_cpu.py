@@ -93,10 +93,15 @@ def test_project_rejects_on_host(L):
 
 
 def test_workspace_bytes(L):
-    # bf16: projected queries and keys at the padded width (m=8 -> 16 columns)
+    # bf16: projected queries and keys at the padded width (m=8 -> 16 columns), then one
+    # float per (head, 256-key block) for the key norm maxima
     n = L.spa_attn_fwd_workspace_bytes(2, 3, 100, 64, 8, 64, spa.SPA_BF16)
     one = 2 * 3 * 100 * 16 * 2
-    assert n == ((one + 255) // 256) * 256 + one
+    a256 = lambda x: ((x + 255) // 256) * 256
+    assert n == a256(a256(one) + one) + 2 * 3 * 1 * 4
+    n2 = L.spa_attn_fwd_workspace_bytes(1, 2, 1000, 128, 32, 128, spa.SPA_BF16)
+    one2 = 2 * 1000 * 32 * 2
+    assert n2 == a256(a256(one2) + one2) + 2 * 4 * 4
     n32 = L.spa_attn_fwd_workspace_bytes(1, 1, 512, 64, 16, 64, spa.SPA_F32)
     assert n32 == 2 * 512 * 16 * 4
     assert L.spa_attn_fwd_workspace_bytes(1, 1, 512, 96, 16, 64, spa.SPA_BF16) == 0
