@@ -77,8 +77,11 @@ spa_status_t spa_project(const void* X, const void* P, void* Xt, int B, int H, i
                          int m, spa_dtype_t dtype, void* stream);
 
 /*
- * Workspace bytes spa_attn_fwd needs for these sizes (it holds the projected queries and
- * keys). Returns 0 for arguments spa_attn_fwd would reject.
+ * Workspace bytes spa_attn_fwd needs for these sizes. Returns 0 for arguments spa_attn_fwd
+ * would reject. Contents (each region 256-byte aligned): the projected queries and keys
+ * (bf16 path: fp16 at m rounded up to 16, 32, 64 or 128 columns; fp32 path: fp32 at m
+ * columns) and, on the bf16 path only, one fp32 per (head, 256-key block) with that block's
+ * largest projected key norm, and V transposed per head ([dv, N rounded up to 64] bf16).
  */
 size_t spa_attn_fwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
                                     spa_dtype_t dtype);
@@ -101,15 +104,19 @@ size_t spa_attn_fwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
  *   lse   optional [B,H,N] fp32 output (NULL to skip): the natural log of each row's
  *         softmax normaliser, log(sum_j exp(score_ij)).
  *   workspace / workspace_bytes: device scratch of at least
- *         spa_attn_fwd_workspace_bytes(...) bytes, 16-byte aligned, used for the projected
- *         queries and keys. If workspace is NULL the library allocates and frees it
- *         stream-ordered (hipMallocAsync / hipFreeAsync) inside the call.
+ *         spa_attn_fwd_workspace_bytes(...) bytes, 16-byte aligned (contents above). If
+ *         workspace is NULL the library allocates and frees it stream-ordered
+ *         (hipMallocAsync / hipFreeAsync) inside the call.
  *
- * The bf16 path runs two launches on `stream`: a projection launch (bf16 MFMA, fp32
- * accumulation, projected values rounded to bf16) and the attention launch (bf16 MFMA for
- * both contractions, fp32 accumulation and an fp32 online softmax; the softmax weights are
- * rounded to bf16 before they meet V). Supported: d in {64, 128}, dv in {64, 128},
- * 1 <= m <= 128. The fp32 path computes in fp32 throughout: 1 <= d <= 256, 1 <= m <= 128,
+ * The bf16 path runs three launches on `stream`: the projection of Q and K (bf16 MFMA, fp32
+ * accumulation, projected values rounded once to fp16, queries pre-multiplied by
+ * scale*log2(e); it also records the per-block key norm maxima), the transpose of V, and
+ * the attention launch (fp16 MFMA for the scores and bf16 MFMA for weights x V, both with
+ * fp32 accumulation; the softmax weights are rounded to bf16 before they meet V and the
+ * normaliser sums those rounded weights). Each row's exponent offset is the Cauchy-Schwarz
+ * bound |q| * max |k| rather than a running maximum; rows for which that bound is so loose
+ * that the normaliser would fall below 2^-64 are recomputed with an exact online maximum.
+ * Supported: d in {64, 128}, dv in {64, 128}, 1 <= m <= 128. The fp32 path computes in fp32 throughout: 1 <= d <= 256, 1 <= m <= 128,
  * 1 <= dv <= 128. N may be any size from 1 to 2^22; tails are masked.
  */
 spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const void* P,

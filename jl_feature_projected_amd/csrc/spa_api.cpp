@@ -50,24 +50,29 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 size_t elem_size(spa_dtype_t t) { return t == SPA_BF16 ? 2 : 4; }
 
 // Workspace layout: projected queries, projected keys, and (bf16 path) the per-block key
-// norm maxima, each 256-byte aligned.
+// norm maxima and V^T, each 256-byte aligned.
 struct WorkspaceLayout {
     size_t tilde_bytes;  // one projected tensor
     size_t k_offset;
     size_t kmax_offset;
+    size_t vt_offset;
     size_t total;
 };
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-WorkspaceLayout workspace_layout(int BH, int N, int m, spa_dtype_t dtype) {
+WorkspaceLayout workspace_layout(int BH, int N, int m, int dv, spa_dtype_t dtype) {
     const long long rows = (long long)BH * N;
     const int cols = dtype == SPA_BF16 ? spa::padded_m(m) : m;
     WorkspaceLayout w;
     w.tilde_bytes = (size_t)rows * cols * elem_size(dtype);
     w.k_offset = align256(w.tilde_bytes);
     w.kmax_offset = align256(w.k_offset + w.tilde_bytes);
-    const size_t kmax_bytes =
-        dtype == SPA_BF16 ? (size_t)BH * spa::proj_blocks(N) * sizeof(float) : 0;
-    w.total = w.kmax_offset + kmax_bytes;
+    if (dtype == SPA_BF16) {
+        w.vt_offset = align256(w.kmax_offset + (size_t)BH * spa::proj_blocks(N) * sizeof(float));
+        w.total = w.vt_offset + (size_t)BH * dv * spa::vt_padded_keys(N) * 2;
+    } else {
+        w.vt_offset = w.kmax_offset;
+        w.total = w.kmax_offset;
+    }
     return w;
 }
 
@@ -172,7 +177,7 @@ size_t spa_attn_fwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
     size_t out = 0;
     if (check_dims("spa_attn_fwd_workspace_bytes", B, H, N, d, m, dv) == SPA_OK &&
         check_shape_support("spa_attn_fwd_workspace_bytes", dtype, d, m, dv) == SPA_OK)
-        out = workspace_layout(B * H, N, m, dtype).total;
+        out = workspace_layout(B * H, N, m, dv, dtype).total;
     memcpy(g_err, saved, sizeof(g_err));
     return out;
 }
@@ -207,7 +212,7 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
 
     const long long rows = (long long)B * H * N;
     const size_t es = elem_size(dtype);
-    const WorkspaceLayout wl = workspace_layout(B * H, N, m, dtype);
+    const WorkspaceLayout wl = workspace_layout(B * H, N, m, dv, dtype);
     if (workspace && workspace_bytes < wl.total)
         return fail(SPA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn,
                     workspace_bytes, wl.total);
@@ -243,6 +248,7 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
     void* Qt = wsb;
     void* Kt = wsb + wl.k_offset;
     float* kmax = reinterpret_cast<float*>(wsb + wl.kmax_offset);
+    void* Vt = wsb + wl.vt_offset;
 
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
     {
@@ -264,9 +270,10 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
             const float qscale = scale * 1.44269504088896340736f;
             e = spa::launch_project_bf16(Q, K, P, Qt, Kt, 2, B * H, H, N, d, m, mp, mp, qscale,
                                          1.0f, /*out_f16=*/true, kmax, s);
+            if (e == hipSuccess) e = spa::launch_vt_bf16(V, Vt, B * H, N, dv, s);
             if (e == hipSuccess && ev[1]) e = hipEventRecord(ev[1], s);
             if (e == hipSuccess)
-                e = spa::launch_attn_bf16(Qt, Kt, V, kmax, O, lse, B * H, N, mp, dv,
+                e = spa::launch_attn_bf16(Qt, Kt, Vt, kmax, O, lse, B * H, N, mp, dv,
                                           causal == 1, o_dtype == SPA_F32, s);
         } else {
             e = spa::launch_project_f32(static_cast<const float*>(Q),

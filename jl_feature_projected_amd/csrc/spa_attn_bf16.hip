@@ -10,9 +10,10 @@
 // design 3, with the dense projected contraction in place of the sparse intersection.
 //
 // Work decomposition: a workgroup of 4 waves owns 128 queries of one (batch, head); each
-// wave owns 32 of them. Key tiles of 64 are copied HBM -> LDS by buffer loads that write LDS
-// directly (no registers, no VALU; rows past N read as zero), double buffered: the next
-// tile's copy is issued before the current tile's math. Per tile and wave:
+// wave owns 32 of them. Key tiles of 64 (projected keys, and the matching 64 columns of
+// V^T) are copied HBM -> LDS by buffer loads that write LDS directly (no registers, no VALU;
+// rows past the end read as zero), double buffered: a copy is issued one step before the
+// step that reads it. Per tile and wave:
 //   scores^T (64 keys x 32 queries) = Kt_tile . Qt^T on 32x32x16 MFMA. The accumulator starts
 //     at -mu (the running row maximum), so the MFMA output is already score - mu; a lane
 //     owns one query and 16 keys per 32-key block, so row reductions are in-lane plus one
@@ -27,18 +28,17 @@
 //     units, rescaling what was accumulated).
 //   O^T (dv x 32 queries) += V^T_tile . p^T on 32x32x16 MFMA. The weights p go from the
 //     score accumulator straight into the B operand: the k-order of the contraction is the
-//     key order the score layout already has. The V tile stays row-major in LDS and the
-//     A operand is read with ds_read_b64_tr_b16: within each 16-lane group, lane 4a+b
-//     receives element b of the 8-byte rows that lanes a, a+4, a+8, a+12 address, so lane s
-//     addressing V[r0 + s/4][c0 + 4(s%4)] gives lane i the keys r0..r0+3 of column c0 + i.
+//     key order the score layout already has. V arrives transposed (a separate launch
+//     writes V^T with the keys of each 16-key group in that same order), so each A operand
+//     is one 16-byte LDS read: 8 keys of one V column.
 // LDS tiles are XOR-swizzled in 16-byte chunks (the copy picks, per lane, which global chunk
-// lands in its LDS slot), so neither the score-operand reads nor the transposed reads hit
-// a bank twice.
+// lands in its LDS slot), so no read of the score or PV operands hits a bank twice.
 // Queries arrive pre-scaled by scale*log2(e), so exp2 of the MFMA output is the softmax
 // numerator. The projected queries and keys are fp16 (the score MFMA runs in fp16, whose
 // 11-bit significand keeps the score error small); V and the weights are bf16. The
 // normaliser is summed from the bf16-rounded weights, the same values the PV MFMA consumes.
 #include <type_traits>
+#include <utility>
 
 #include "spa_device.h"
 #include "spa_internal.h"
@@ -52,43 +52,42 @@ constexpr int kBR = 128;  // queries per workgroup (4 waves x 32)
 constexpr int kBC = 64;   // keys per tile
 constexpr float kTau = 8.0f;
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
 // Buffer descriptor over [base, base + bytes): loads past the end return zero. Raw buffer
-// (stride 0), 32-bit data format.
+// (stride 0), 32-bit data format. The fields go through readfirstlane so they are SGPRs
+// (the asm operand needs them there) even where the compiler cannot prove them uniform.
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     u32x4 r;
-    r.x = (uint32_t)a;
-    r.y = (uint32_t)(a >> 32) & 0xffffu;
-    r.z = bytes;
+    r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r.z = __builtin_amdgcn_readfirstlane(bytes);
     r.w = 0x00020000u;
     return r;
 }
 
-// 16 bytes per lane from buffer offset voff straight into LDS at dst + 16 * lane (dst is
-// wave-uniform). Issued as inline assembly so the compiler does not track it: it cannot
+// 16 bytes per lane from buffer offset voff straight into LDS at byte address m0 + 16 * lane
+// (m0 wave-uniform; readfirstlane keeps it in an SGPR where the compiler cannot prove that). Issued as inline assembly so the compiler does not track it: it cannot
 // tell that the LDS it writes (the other buffer) is disjoint from the LDS the tile loop
 // reads, and would otherwise wait for the copy before the first read. The copy's completion
 // is awaited explicitly (vmcnt) before the barrier that hands the buffer over. Device pass
 // only: the host pass does not parse AMDGPU assembly constraints.
-__device__ __forceinline__ void copy16_to_lds(u32x4 rsrc, char* dst, uint32_t voff) {
+__device__ __forceinline__ void copy16_to_lds(u32x4 rsrc, uint32_t m0, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
-                 : "s"(m0), "v"(voff), "s"(rsrc)
+                 : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(rsrc)
                  : "m0");
 #endif
 }
 
 // 16-byte chunk swizzles: LDS slot = global chunk ^ swizzle(row), a GF(2)-linear function of
-// the row's low bits. The tables were chosen (by exhaustive search over such functions) so
-// that every read pattern below touches each LDS bank once per service cycle, whether the
-// LDS serves 128 bytes per cycle over 32 banks or 256 bytes over 64:
+// the row's low bits, chosen so that every operand read touches each LDS bank once per
+// service cycle, whether the LDS serves 128 bytes per cycle over 32 banks or 256 bytes over
+// 64 (the K-tile tables were found by exhaustive search over such functions):
 //   K tile (rows of MP*2 bytes), score operand: 8 or 16 consecutive rows, one chunk each;
-//   V tile (rows of DV*2 bytes), transposed read: 4 rows x 2 or 4 chunks.
+//   V^T tile (rows of 128 bytes = 64 keys), PV operand: 8 or 16 consecutive rows, one chunk
+//   each. Rows r and r+8 share their position in a 256-byte bank row pair only if they differ
+//   in bit 0 after the swizzle, hence the extra bit-3 term.
 template <int MP>
 __device__ __forceinline__ int kswz(int row) {
     constexpr int b0 = MP == 16 ? 0 : MP == 32 ? 0 : 1;
@@ -97,23 +96,35 @@ __device__ __forceinline__ int kswz(int row) {
     constexpr int b3 = MP == 16 ? 1 : MP == 32 ? 1 : MP == 64 ? 1 : 8;
     return (row & 1 ? b0 : 0) ^ (row & 2 ? b1 : 0) ^ (row & 4 ? b2 : 0) ^ (row & 8 ? b3 : 0);
 }
-template <int DV>
-__device__ __forceinline__ int vswz(int row) {
-    constexpr int b0 = DV == 64 ? 2 : 4;
-    constexpr int b1 = DV == 64 ? 4 : 10;
-    return (row & 1 ? b0 : 0) ^ (row & 2 ? b1 : 0);
+__device__ __forceinline__ int vtswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Scheduling groups for the PV MFMAs of a pipelined step (see pipelined_step): PV MFMA i
+// preceded by one DS read while any remain, followed from WSTART on by its share of the 16
+// weight pairs (4 VALU instructions each).
+template <int NPV, int PF, int WSTART, int... I>
+__device__ __forceinline__ void sched_pv_groups(std::integer_sequence<int, I...>) {
+    constexpr int NW = NPV - WSTART;
+    auto one = [](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i + PF < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (i >= WSTART) {
+            constexpr int pairs = (i - WSTART + 1) * 16 / NW - (i - WSTART) * 16 / NW;
+            if constexpr (pairs > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4 * pairs, 0);
+        }
+    };
+    (one(std::integral_constant<int, I>{}), ...);
 }
 
 template <int MP, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
-    const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Kt, const bf16_t* __restrict__ V,
+    const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Kt, const bf16_t* __restrict__ Vt,
     const float* __restrict__ kmax, void* __restrict__ O, float* __restrict__ lse, int N, int nqb,
     int out_f32) {
     constexpr int KS = MP / 16;              // score MFMA k-steps
     constexpr int KCH = MP / 8;              // 16-byte chunks per projected-key row
-    constexpr int VCH = DV / 8;              // 16-byte chunks per V row
     constexpr int K_BYTES = kBC * MP * 2;    // one K tile
-    constexpr int V_BYTES = kBC * DV * 2;    // one V tile
+    constexpr int V_BYTES = kBC * DV * 2;    // one V^T tile (DV rows of 64 keys)
     constexpr int BUF = K_BYTES + V_BYTES;   // one LDS buffer
     constexpr int KINS = K_BYTES / 1024;     // 64-lane x 16-byte copies per K tile (2 .. 16)
     constexpr int VINS = V_BYTES / 1024;     // ... per V tile (8 or 16)
@@ -141,7 +152,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 
     const uint16_t* Qh = Qt + (size_t)bh * N * MP;
     const uint16_t* Kh = Kt + (size_t)bh * N * MP;
-    const bf16_t* Vh = V + (size_t)bh * N * DV;
+    const int Np = vt_padded_keys(N);  // row length of V^T
+    const bf16_t* Vh = Vt + (size_t)bh * DV * Np;
 
     // This lane's query as the B operand of the score MFMA (zero past N).
     f16x8 qf[KS];
@@ -157,7 +169,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 
     // ---- HBM -> LDS tile copy ---------------------------------------------------------
     // Copy j (64 lanes x 16 bytes) fills LDS chunks 64j .. 64j+63 of the tile; lane l writes
-    // chunk c = 64j + l, which holds global chunk (c % CH) ^ swizzle(row) of row c / CH.
+    // chunk c = 64j + l, which holds global chunk (c % CH) ^ swizzle(row) of row c / CH (CH
+    // chunks per row: MP/8 for a K row, 8 for a V^T row of 64 keys).
     // Copies are dealt round-robin to the waves (wave w issues j = w, w + 4, ...); the
     // global byte offsets are fixed per lane, a tile only moves the descriptor's base.
     constexpr int KPW = (KINS + kWaves - 1) / kWaves;  // K copies per wave (the last may idle)
@@ -172,23 +185,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < VPW; ++i) {
         const int c = 64 * (wave + kWaves * i) + lane;
-        const int row = c / VCH;
-        voff[i] = row * DV * 2 + 16 * ((c % VCH) ^ vswz<DV>(row));
+        const int row = c >> 3;  // V column
+        voff[i] = row * Np * 2 + 16 * ((c & 7) ^ vtswz(row));
     }
-    auto copy_tile = [&](int k0, int buf) {
-        char* kdst = lds + buf * BUF;
-        char* vdst = kdst + K_BYTES;
-        const uint32_t rows_left = (uint32_t)(N - k0);
-        const u32x4 kr = make_rsrc(Kh + (size_t)k0 * MP, rows_left * MP * 2);
-        const u32x4 vr = make_rsrc(Vh + (size_t)k0 * DV, rows_left * DV * 2);
+    // LDS byte address of this wave's first copy slot in buffer 0 (wave-uniform; the M0
+    // values below are this plus constants).
+    const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds + 1024 * wave);
+    auto copy_k = [&](int k0, int buf) {
+        const u32x4 kr = make_rsrc(Kh + (size_t)k0 * MP, (uint32_t)(N - k0) * MP * 2);
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
             const int j = wave + kWaves * i;
-            if (j < KINS) copy16_to_lds(kr, kdst + 1024 * j, koff[i]);
+            if (j < KINS) copy16_to_lds(kr, lds_wave + buf * BUF + 1024 * kWaves * i, koff[i]);
         }
+    };
+    auto copy_v = [&](int k0, int buf) {
+        const u32x4 vr = make_rsrc(Vh + k0, (uint32_t)(DV * Np - k0) * 2);
 #pragma unroll
         for (int i = 0; i < VPW; ++i)
-            copy16_to_lds(vr, vdst + 1024 * (wave + kWaves * i), voff[i]);
+            copy16_to_lds(vr, lds_wave + buf * BUF + K_BYTES + 1024 * kWaves * i, voff[i]);
     };
 
     // Per-lane LDS read offsets, fixed across tiles.
@@ -201,18 +217,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
             const int row = kb * 32 + col;
             kread[kb][ks] = row * MP * 2 + 16 * ((2 * ks + half) ^ kswz<MP>(row));
         }
-    // PV operand (transposed read): lane s of 16-lane group (half, gc) addresses key row
-    // r0 + s/4 at column 32*db + 16*gc + 4*(s%4); r0 = kb*32 + 16*tt + 4*half, plus 8 for the
-    // second half of the k-slots. Every such row has row % 4 == s/4, so the row's swizzle is
-    // the same for all of this lane's reads: the swizzled chunk of each column block is
-    // precomputed, and (kb, tt, lo/hi) only add a row offset.
-    const int s16 = lane & 15, gc = (lane >> 4) & 1;
-    const int vrow0 = 4 * half + (s16 >> 2);
-    const int vbase = vrow0 * DV * 2 + 8 * (s16 & 1);  // + 2 * ((4*(s%4)) & 7)
-    int vchunk[DB];
+    // PV operand: V^T row db*32 + col (a V column), 16-byte chunk 4*kb + 2*tt + half (keys
+    // kb*32 + 16*tt + {4*half .. 4*half+3, 8+4*half .. 8+4*half+3}, in the slot order of the
+    // score accumulator). The swizzle of row db*32 + col does not depend on db.
+    int vread[2][2];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-        vchunk[db] = vbase + 16 * ((4 * db + 2 * gc + ((s16 & 3) >> 1)) ^ vswz<DV>(vrow0));
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+            vread[kb][tt] = col * 128 + 16 * ((4 * kb + 2 * tt + half) ^ vtswz(col));
 
     // ---- score bound: M = |q| * max |k| over the key blocks this workgroup reads -------
     float kmx = 0.0f;
@@ -238,41 +251,133 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     f32x16 acc[DB];
     float mu;        // the exponent offset (base-2 units), identical in both half-waves
     float lsum;      // partial normaliser over this half-wave's keys
+    f32x16 cinit;    // the score accumulator's start value, -mu
 
-    auto tile_loop = [&](auto exact_tag) {
-        constexpr bool EXACT = decltype(exact_tag)::value;
+    // Scores^T of one key tile (64 keys x this wave's 32 queries), minus mu.
+    auto scores = [&](const char* Ks, f32x16 (&s)[2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = cinit;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const f16x8 a = __builtin_bit_cast(
+                    f16x8, *reinterpret_cast<const u32x4*>(Ks + kread[kb][ks]));
+                s[kb] = mfma32x32x16(a, qf[ks], s[kb]);
+            }
+        }
+    };
+    // Weights of k-step tt of key block kb, pair j (keys 2j, 2j+1 of the lane's 8 slots):
+    // exp2, rounded to bf16, packed, and added to the normaliser.
+    auto weight_pair = [&](const f32x16 (&s)[2], int kb, int tt, int j) -> uint32_t {
+        const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j]);
+        const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j + 1]);
+        const uint32_t w = pack_bf16x2(p0, p1);
+        lsum = add_bf16x2(w, lsum);
+        return w;
+    };
+    // One PV MFMA: O^T block db += V^T_tile(key block kb, k-step tt) . p^T. Slot 8*half + j
+    // of k-step tt in key block kb holds key kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, in the
+    // score accumulator and in the V^T tile alike.
+    auto pv_step = [&](const char* Vs, const u32x4 (&p)[2][2], int db, int kb, int tt) {
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(Vs + db * 32 * 128 + vread[kb][tt]));
+        acc[db] = mfma32x32x16(a, __builtin_bit_cast(bf16x8, p[kb][tt]), acc[db]);
+    };
+    auto pv = [&](const char* Vs, const u32x4 (&p)[2][2]) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) pv_step(Vs, p, db, kb, tt);
+    };
+    auto weights = [&](const f32x16 (&s)[2], u32x4 (&p)[2][2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p[kb][tt][j] = weight_pair(s, kb, tt, j);
+    };
+    // One pipelined step: scores of the next tile (K tile Kn) and PV of this one (V^T tile
+    // Vs, weights p), with the next tile's weights (out pn) computed while the PV MFMAs run.
+    // The schedule is fixed explicitly, since the LDS reads and the MFMA -> exp dependency
+    // each take about three MFMA issue slots to come back:
+    //   all K operands and the first PF V operands are read up front; the score MFMAs
+    //   follow; PV MFMA i is preceded by the read of V operand i + PF; the weights start
+    //   WSTART PV MFMAs after the score MFMAs (their inputs are ready by then) and are spread
+    //   over the remaining PV MFMAs.
+    auto pipelined_step = [&](const char* Kn, const char* Vs, const u32x4 (&p)[2][2],
+                              u32x4 (&pn)[2][2]) {
+        constexpr int NPV = 4 * DB;  // PV MFMAs per tile
+        constexpr int PF = 4;        // V operand prefetch distance, in MFMAs
+        constexpr int WSTART = 3;    // first PV MFMA that weight work is placed after
+        constexpr int NW = NPV - WSTART;
+        u32x4 ka[2][KS];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                ka[kb][ks] = *reinterpret_cast<const u32x4*>(Kn + kread[kb][ks]);
+        u32x4 va[NPV];
+        auto vload = [&](int i) {
+            const int db = i / 4, kb = (i >> 1) & 1, tt = i & 1;
+            va[i] = *reinterpret_cast<const u32x4*>(Vs + db * 32 * 128 + vread[kb][tt]);
+        };
+#pragma unroll
+        for (int i = 0; i < PF; ++i) vload(i);
+        f32x16 sn[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sn[kb] = cinit;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                sn[kb] = mfma32x32x16(__builtin_bit_cast(f16x8, ka[kb][ks]), qf[ks], sn[kb]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // nothing below moves above the score MFMAs
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            if (i + PF < NPV) vload(i + PF);
+            const int db = i / 4, kb = (i >> 1) & 1, tt = i & 1;
+            acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, va[i]),
+                                   __builtin_bit_cast(bf16x8, p[kb][tt]), acc[db]);
+            if (i >= WSTART) {
+#pragma unroll
+                for (int u = (i - WSTART) * 16 / NW; u < (i - WSTART + 1) * 16 / NW; ++u)
+                    pn[u >> 3][(u >> 2) & 1][u & 3] =
+                        weight_pair(sn, u >> 3, (u >> 2) & 1, u & 3);
+            }
+        }
+        // The same order as scheduling groups (DS read 0x100, MFMA 0x008, VALU 0x002); a
+        // weight pair is four VALU instructions (two exps, a pack, a dot).
+        sched_pv_groups<NPV, PF, WSTART>(std::make_integer_sequence<int, NPV>{});
+    };
+    auto init_state = [&](float mu0) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] = f32x16_fill(0.0f);
         lsum = 0.0f;
-        mu = EXACT ? 0.0f : bound;
-        f32x16 cinit = f32x16_fill(-mu);  // the score accumulator's start value
+        mu = mu0;
+        cinit = f32x16_fill(-mu);
+    };
 
-        copy_tile(0, 0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-
+    // Tiles [t0, ntiles), one at a time: the next tile's copy is issued first; keys past N
+    // and after the query (causal) are masked; waves whose queries all precede a tile skip
+    // it. The exact variant keeps a lazy running maximum.
+    auto tile_loop = [&](auto exact_tag, int t0) {
+        constexpr bool EXACT = decltype(exact_tag)::value;
 #pragma unroll 1
-        for (int t = 0; t < ntiles; ++t) {
+        for (int t = t0; t < ntiles; ++t) {
             const int k0 = t * kBC;
-            if (t + 1 < ntiles) copy_tile(k0 + kBC, (t + 1) & 1);
-
+            if (t + 1 < ntiles) {
+                copy_k(k0 + kBC, (t + 1) & 1);
+                copy_v(k0 + kBC, (t + 1) & 1);
+            }
             const char* Ks = lds + (t & 1) * BUF;
             const char* Vs = Ks + K_BYTES;
 
-            // Causal: a wave whose queries all precede the tile has nothing to do in it.
             if (!CAUSAL || k0 <= qw0 + 31) {
                 f32x16 s[2];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    s[kb] = cinit;
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const f16x8 a = __builtin_bit_cast(
-                            f16x8, *reinterpret_cast<const u32x4*>(Ks + kread[kb][ks]));
-                        s[kb] = mfma32x32x16(a, qf[ks], s[kb]);
-                    }
-                }
-                // Masks: keys past N, and keys after the query under the causal mask.
+                scores(Ks, s);
                 const bool edge = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > qw0);
                 if (edge) {
 #pragma unroll
@@ -312,44 +417,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                         cinit = f32x16_fill(-mu);
                     }
                 }
-                // Weights, their partial sum, and the bf16 B operands of the PV MFMA.
-                bf16x8 pf[2][2];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        u32x4 w;
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j]);
-                            const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j + 1]);
-                            w[j] = pack_bf16x2(p0, p1);
-                            lsum = add_bf16x2(w[j], lsum);
-                        }
-                        pf[kb][tt] = __builtin_bit_cast(bf16x8, w);
-                    }
-                }
-                // O^T += V^T . p^T. Slot 8*half + j of k-step tt in key block kb holds key
-                // kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, as in the score accumulator.
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                        for (int tt = 0; tt < 2; ++tt) {
-                            const char* vp = Vs + vchunk[db] + (kb * 32 + tt * 16) * DV * 2;
-                            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (__attribute__((address_space(3))) i16x4*)(vp));
-                            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (__attribute__((address_space(3))) i16x4*)(vp + 8 * DV * 2));
-                            const bf16x8 a = __builtin_bit_cast(
-                                bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                            acc[db] = mfma32x32x16(a, pf[kb][tt], acc[db]);
-                        }
-                    }
-                }
+                u32x4 p[2][2];
+                weights(s, p);
+                pv(Vs, p);
             }
-
             // This wave's copies into the other buffer are done, and (barrier) everyone's
             // are, and everyone has finished reading this buffer.
             __builtin_amdgcn_s_waitcnt(0);
@@ -357,10 +428,91 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         }
     };
 
-    tile_loop(std::false_type{});
+    // Fast path, tiles [0, nfull): no key of them is masked for any query of the workgroup,
+    // so they are software pipelined: the score MFMAs of tile t+1 are issued, then the PV
+    // MFMAs of tile t run while the wave computes tile t+1's weights. K and V copies are
+    // issued separately, each one step before the step that reads it:
+    //   step t reads K[t+1] (buffer (t+1)&1) and V[t] (buffer t&1), and copies V[t+1] into
+    //   buffer (t+1)&1 and K[t+2] into buffer t&1.
+    // Returns nfull with tile nfull's K and V in buffer nfull&1, as tile_loop expects.
+    // (At MP = DV = 128 the pipelined loop does not fit the register budget of two
+    // workgroups per CU; that shape runs every tile through tile_loop.)
+    constexpr bool PIPELINED = !(MP == 128 && DV == 128);
+    const int nfull = !PIPELINED ? 0 : CAUSAL ? min(ntiles, q0 / kBC) : N / kBC;
+    auto fast_phase = [&]() -> int {
+        copy_k(0, 0);
+        copy_v(0, 0);
+        if (!PIPELINED || nfull == 0) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            return 0;
+        }
+        if constexpr (!PIPELINED) return 0;
+        if (ntiles > 1) copy_k(kBC, 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        u32x4 pa[2][2], pb[2][2];
+        {
+            f32x16 s[2];
+            scores(lds, s);
+            weights(s, pa);
+        }
+        __syncthreads();  // K[0] read by every wave before step 0 refills buffer 0
+        // Step t with the buffer parity t & 1 as a template constant, so every LDS offset of
+        // the step is an immediate. Weights p of tile t in, weights pn of tile t+1 out. Every
+        // step but the last is pipelined; the last (PV of tile nfull-1 only) is peeled off
+        // so the loop body has no branch around its MFMAs.
+        auto step = [&](auto parity, int t, const u32x4 (&p)[2][2], u32x4 (&pn)[2][2]) {
+            constexpr int PAR = decltype(parity)::value;
+            copy_v((t + 1) * kBC, 1 - PAR);  // t + 1 < nfull <= ntiles
+            if (t + 2 < ntiles) copy_k((t + 2) * kBC, PAR);
+            pipelined_step(lds + (1 - PAR) * BUF, lds + PAR * BUF + K_BYTES, p, pn);
+            // The weights are plain register arithmetic, which the compiler may sink past the
+            // barrier to their use in the next step; pin them here, beside the MFMAs they are
+            // meant to overlap.
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) asm volatile("" : "+v"(pn[kb][tt]));
+            asm volatile("" : "+v"(lsum));
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        };
+        auto last_step = [&](auto parity, int t, const u32x4 (&p)[2][2]) {
+            constexpr int PAR = decltype(parity)::value;
+            if (t + 1 < ntiles) copy_v((t + 1) * kBC, 1 - PAR);
+            if (t + 2 < ntiles) copy_k((t + 2) * kBC, PAR);
+            pv(lds + PAR * BUF + K_BYTES, p);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        };
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        int t = 0;
+#pragma unroll 1
+        for (; t + 2 < nfull; t += 2) {
+            step(P0{}, t, pa, pb);
+            step(P1{}, t + 1, pb, pa);
+        }
+        if (t + 1 < nfull) {
+            step(P0{}, t, pa, pb);
+            last_step(P1{}, t + 1, pb);
+        } else {
+            last_step(P0{}, t, pa);
+        }
+        return nfull;
+    };
+
+    init_state(bound);
+    tile_loop(std::false_type{}, fast_phase());
     float ltot = halves_sum(lsum);
     if (__syncthreads_or(myq < N && ltot < 0x1p-64f)) {
-        tile_loop(std::true_type{});
+        init_state(0.0f);
+        copy_k(0, 0);
+        copy_v(0, 0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        tile_loop(std::true_type{}, 0);
         ltot = halves_sum(lsum);
     }
 
@@ -392,12 +544,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 }
 
 template <int MP, int DV, bool CAUSAL>
-hipError_t launch(const void* Qt, const void* Kt, const void* V, const float* kmax, void* O,
+hipError_t launch(const void* Qt, const void* Kt, const void* Vt, const float* kmax, void* O,
                   float* lse, int BH, int N, bool out_f32, hipStream_t stream) {
     const int nqb = (N + kBR - 1) / kBR;
     attn_bf16_kernel<MP, DV, CAUSAL><<<dim3(nqb * BH), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(Qt), static_cast<const uint16_t*>(Kt),
-        static_cast<const bf16_t*>(V), kmax, O, lse, N, nqb, out_f32 ? 1 : 0);
+        static_cast<const bf16_t*>(Vt), kmax, O, lse, N, nqb, out_f32 ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -26,12 +26,19 @@ hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, vo
                                float out_scale1, bool out_f16, float* kmax,
                                hipStream_t stream);
 
+// V^T for the attention launch: Vt[bh, c, k] (bf16, [BH, dv, vt_padded_keys(N)]) holds
+// V[bh, k', c], keys permuted within each group of 16 (order 0-3, 8-11, 4-7, 12-15) and
+// zero past N.
+constexpr int kVtTileKeys = 64;
+__host__ __device__ inline int vt_padded_keys(int N) { return (N + kVtTileKeys - 1) / kVtTileKeys * kVtTileKeys; }
+hipError_t launch_vt_bf16(const void* V, void* Vt, int BH, int N, int dv, hipStream_t stream);
+
 // Attention over projected inputs. Qt and Kt are fp16 [BH, N, mp] with zero columns past m
 // (score MFMA in fp16); Qt is pre-scaled by scale*log2(e) so the scores come out in base-2
-// exponent units. V is bf16 (weights x V MFMA in bf16). O is [BH, N, dv] in fp32 (out_f32)
-// or bf16; lse [BH, N] optional. kmax holds the per-block key norm maxima written by the
-// projection launch.
-hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* V, const float* kmax,
+// exponent units. Vt is V^T as written by launch_vt_bf16 (weights x V MFMA in bf16). O is
+// [BH, N, dv] in fp32 (out_f32) or bf16; lse [BH, N] optional. kmax holds the per-block key
+// norm maxima written by the projection launch.
+hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* Vt, const float* kmax,
                             void* O, float* lse, int BH, int N, int mp, int dv, bool causal,
                             bool out_f32, hipStream_t stream);
 

@@ -93,15 +93,16 @@ def test_project_rejects_on_host(L):
 
 
 def test_workspace_bytes(L):
-    # bf16: projected queries and keys at the padded width (m=8 -> 16 columns), then one
-    # float per (head, 256-key block) for the key norm maxima
+    # bf16: projected queries and keys at the padded width (m=8 -> 16 columns), one float
+    # per (head, 256-key block) for the key norm maxima, then V^T in bf16 with rows padded
+    # to a multiple of 64 keys
     n = L.spa_attn_fwd_workspace_bytes(2, 3, 100, 64, 8, 64, spa.SPA_BF16)
     one = 2 * 3 * 100 * 16 * 2
     a256 = lambda x: ((x + 255) // 256) * 256
-    assert n == a256(a256(one) + one) + 2 * 3 * 1 * 4
+    assert n == a256(a256(a256(one) + one) + 2 * 3 * 1 * 4) + 2 * 3 * 64 * 128 * 2
     n2 = L.spa_attn_fwd_workspace_bytes(1, 2, 1000, 128, 32, 128, spa.SPA_BF16)
     one2 = 2 * 1000 * 32 * 2
-    assert n2 == a256(a256(one2) + one2) + 2 * 4 * 4
+    assert n2 == a256(a256(a256(one2) + one2) + 2 * 4 * 4) + 2 * 128 * 1024 * 2
     n32 = L.spa_attn_fwd_workspace_bytes(1, 1, 512, 64, 16, 64, spa.SPA_F32)
     assert n32 == 2 * 512 * 16 * 4
     assert L.spa_attn_fwd_workspace_bytes(1, 1, 512, 96, 16, 64, spa.SPA_BF16) == 0
