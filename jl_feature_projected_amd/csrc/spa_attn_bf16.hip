@@ -38,7 +38,6 @@
 // 11-bit significand keeps the score error small); V and the weights are bf16. The
 // normaliser is summed from the bf16-rounded weights, the same values the PV MFMA consumes.
 #include <type_traits>
-#include <utility>
 
 #include "spa_device.h"
 #include "spa_internal.h"
@@ -97,24 +96,6 @@ __device__ __forceinline__ int kswz(int row) {
     return (row & 1 ? b0 : 0) ^ (row & 2 ? b1 : 0) ^ (row & 4 ? b2 : 0) ^ (row & 8 ? b3 : 0);
 }
 __device__ __forceinline__ int vtswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-
-// Scheduling groups for the PV MFMAs of a pipelined step (see pipelined_step): PV MFMA i
-// preceded by one DS read while any remain, followed from WSTART on by its share of the 16
-// weight pairs (4 VALU instructions each).
-template <int NPV, int PF, int WSTART, int... I>
-__device__ __forceinline__ void sched_pv_groups(std::integer_sequence<int, I...>) {
-    constexpr int NW = NPV - WSTART;
-    auto one = [](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        if constexpr (i + PF < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if constexpr (i >= WSTART) {
-            constexpr int pairs = (i - WSTART + 1) * 16 / NW - (i - WSTART) * 16 / NW;
-            if constexpr (pairs > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4 * pairs, 0);
-        }
-    };
-    (one(std::integral_constant<int, I>{}), ...);
-}
 
 template <int MP, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
@@ -301,12 +282,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     };
     // One pipelined step: scores of the next tile (K tile Kn) and PV of this one (V^T tile
     // Vs, weights p), with the next tile's weights (out pn) computed while the PV MFMAs run.
-    // The schedule is fixed explicitly, since the LDS reads and the MFMA -> exp dependency
-    // each take about three MFMA issue slots to come back:
-    //   all K operands and the first PF V operands are read up front; the score MFMAs
-    //   follow; PV MFMA i is preceded by the read of V operand i + PF; the weights start
-    //   WSTART PV MFMAs after the score MFMAs (their inputs are ready by then) and are spread
-    //   over the remaining PV MFMAs.
+    // The schedule is fixed explicitly (scheduling fences between slots), since the LDS
+    // reads and the MFMA -> exp dependency each take about three MFMA issue slots to come
+    // back: all K operands and the first PF V operands are read up front; the score MFMAs
+    // follow; PV MFMA i is preceded by the read of V operand i + PF; the weights start
+    // WSTART PV MFMAs after the score MFMAs (their inputs are ready by then) and are spread
+    // evenly over the remaining PV MFMAs.
     auto pipelined_step = [&](const char* Kn, const char* Vs, const u32x4 (&p)[2][2],
                               u32x4 (&pn)[2][2]) {
         constexpr int NPV = 4 * DB;  // PV MFMAs per tile
@@ -347,10 +328,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                     pn[u >> 3][(u >> 2) & 1][u & 3] =
                         weight_pair(sn, u >> 3, (u >> 2) & 1, u & 3);
             }
+            // Slot fence: the compiler keeps this order (it would otherwise bunch the exps).
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // The same order as scheduling groups (DS read 0x100, MFMA 0x008, VALU 0x002); a
-        // weight pair is four VALU instructions (two exps, a pack, a dot).
-        sched_pv_groups<NPV, PF, WSTART>(std::make_integer_sequence<int, NPV>{});
     };
     auto init_state = [&](float mu0) {
 #pragma unroll
