@@ -136,15 +136,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     const int Np = vt_padded_keys(N);  // row length of V^T
     const bf16_t* Vh = Vt + (size_t)bh * DV * Np;
 
-    // This lane's query as the B operand of the score MFMA (zero past N).
-    f16x8 qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (myq < N) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)myq * MP + ks * 16 + half * 8);
-        qf[ks] = __builtin_bit_cast(f16x8, v);
-    }
-
     const int kend = CAUSAL ? min(N, q0 + kBR) : N;
     const int ntiles = (kend + kBC - 1) / kBC;
 
@@ -187,6 +178,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         for (int i = 0; i < VPW; ++i)
             copy16_to_lds(vr, lds_wave + buf * BUF + K_BYTES + 1024 * kWaves * i, voff[i]);
     };
+
+    // The first tiles' copies go out before anything else is loaded, so their latency
+    // overlaps that of the query and key-norm loads below (the fast path starts from tile 0
+    // in buffer 0 and, when pipelined, the keys of tile 1 in buffer 1).
+    // (At MP = DV = 128 the pipelined loop does not fit the register budget of two
+    // workgroups per CU; that shape runs every tile through tile_loop.)
+    constexpr bool PIPELINED = !(MP == 128 && DV == 128);
+    const int nfull = !PIPELINED ? 0 : CAUSAL ? min(ntiles, q0 / kBC) : N / kBC;
+    copy_k(0, 0);
+    copy_v(0, 0);
+    if (nfull > 0 && ntiles > 1) copy_k(kBC, 1);
+
+    // This lane's query as the B operand of the score MFMA (zero past N).
+    f16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (myq < N) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)myq * MP + ks * 16 + half * 8);
+        qf[ks] = __builtin_bit_cast(f16x8, v);
+    }
 
     // Per-lane LDS read offsets, fixed across tiles.
     // Score operand: key row kb*32 + col, global chunk 2*ks + half.
@@ -414,23 +425,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     // issued separately, each one step before the step that reads it:
     //   step t reads K[t+1] (buffer (t+1)&1) and V[t] (buffer t&1), and copies V[t+1] into
     //   buffer (t+1)&1 and K[t+2] into buffer t&1.
-    // Returns nfull with tile nfull's K and V in buffer nfull&1, as tile_loop expects.
-    // (At MP = DV = 128 the pipelined loop does not fit the register budget of two
-    // workgroups per CU; that shape runs every tile through tile_loop.)
-    constexpr bool PIPELINED = !(MP == 128 && DV == 128);
-    const int nfull = !PIPELINED ? 0 : CAUSAL ? min(ntiles, q0 / kBC) : N / kBC;
+    // Returns nfull with tile nfull's K and V in buffer nfull&1, as tile_loop expects. The
+    // copies of tile 0 (and of tile 1's keys) were issued at the top of the kernel.
     auto fast_phase = [&]() -> int {
-        copy_k(0, 0);
-        copy_v(0, 0);
-        if (!PIPELINED || nfull == 0) {
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            return 0;
-        }
-        if constexpr (!PIPELINED) return 0;
-        if (ntiles > 1) copy_k(kBC, 1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if (!PIPELINED || nfull == 0) return 0;
+        if constexpr (!PIPELINED) return 0;
         u32x4 pa[2][2], pb[2][2];
         {
             f32x16 s[2];
