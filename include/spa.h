@@ -108,9 +108,9 @@ size_t spa_attn_fwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
  *         workspace is NULL the library allocates and frees it stream-ordered
  *         (hipMallocAsync / hipFreeAsync) inside the call.
  *
- * The bf16 path runs three launches on `stream`: the projection of Q and K (bf16 MFMA, fp32
- * accumulation, projected values rounded once to fp16, queries pre-multiplied by
- * scale*log2(e); it also records the per-block key norm maxima), the transpose of V, and
+ * The bf16 path runs two launches on `stream`: operand preparation (the projection of Q and
+ * K on bf16 MFMA with fp32 accumulation, projected values rounded once to fp16, queries
+ * pre-multiplied by scale*log2(e), the per-block key norm maxima, and V transposed) and
  * the attention launch (fp16 MFMA for the scores and bf16 MFMA for weights x V, both with
  * fp32 accumulation; the softmax weights are rounded to bf16 before they meet V and the
  * normaliser sums those rounded weights). Each row's exponent offset is the Cauchy-Schwarz

@@ -162,7 +162,8 @@ spa_status_t spa_project(const void* X, const void* P, void* Xt, int B, int H, i
     hipError_t e;
     if (dtype == SPA_BF16)
         e = spa::launch_project_bf16(X, nullptr, P, Xt, nullptr, 1, B * H, H, N, d, m, m, m,
-                                     1.0f, 1.0f, /*out_f16=*/false, nullptr, s);
+                                     1.0f, 1.0f, /*out_f16=*/false, nullptr, nullptr, nullptr,
+                                     0, s);
     else
         e = spa::launch_project_f32(static_cast<const float*>(X), static_cast<const float*>(P),
                                     static_cast<float*>(Xt), B * H, H, N, d, m, 1.0f, s);
@@ -269,8 +270,7 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
             // bf16 operands (8 bits) do not, at the same MFMA rate.
             const float qscale = scale * 1.44269504088896340736f;
             e = spa::launch_project_bf16(Q, K, P, Qt, Kt, 2, B * H, H, N, d, m, mp, mp, qscale,
-                                         1.0f, /*out_f16=*/true, kmax, s);
-            if (e == hipSuccess) e = spa::launch_vt_bf16(V, Vt, B * H, N, dv, s);
+                                         1.0f, /*out_f16=*/true, kmax, V, Vt, dv, s);
             if (e == hipSuccess && ev[1]) e = hipEventRecord(ev[1], s);
             if (e == hipSuccess)
                 e = spa::launch_attn_bf16(Qt, Kt, Vt, kmax, O, lse, B * H, N, mp, dv,

@@ -14,28 +14,28 @@ inline int padded_m(int m) { return m <= 16 ? 16 : m <= 32 ? 32 : m <= 64 ? 64 :
 constexpr int kProjBlockTokens = 256;
 __host__ __device__ inline int proj_blocks(int N) { return (N + kProjBlockTokens - 1) / kProjBlockTokens; }
 
-// Projection of bf16 inputs on bf16 MFMA: Y_z[bh, n, c] = out_scale_z * sum_k X_z[bh, n, k]
-// P[h, k, c] for z < nz (nz = 1 or 2, e.g. queries and keys in one launch), accumulated in
-// fp32 and rounded once to fp16 (out_f16) or bf16. P is [H, d, m]; columns m <= c <
-// out_cols are written as zeros. Output rows are out_stride elements apart. If kmax is not
-// null, kmax[bh * proj_blocks(N) + b] receives the largest row norm (fp32, before rounding)
-// of Y1 over tokens b*256 .. b*256+255 of head bh.
-hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, void* Y0,
-                               void* Y1, int nz, int BH, int H, int N, int d, int m,
-                               int out_stride, int out_cols, float out_scale0,
-                               float out_scale1, bool out_f16, float* kmax,
-                               hipStream_t stream);
-
-// V^T for the attention launch: Vt[bh, c, k] (bf16, [BH, dv, vt_padded_keys(N)]) holds
+// V^T layout for the attention launch: Vt[bh, c, k] (bf16, [BH, dv, vt_padded_keys(N)]) holds
 // V[bh, k', c], keys permuted within each group of 16 (order 0-3, 8-11, 4-7, 12-15) and
 // zero past N.
 constexpr int kVtTileKeys = 64;
 __host__ __device__ inline int vt_padded_keys(int N) { return (N + kVtTileKeys - 1) / kVtTileKeys * kVtTileKeys; }
-hipError_t launch_vt_bf16(const void* V, void* Vt, int BH, int N, int dv, hipStream_t stream);
+
+// Operand preparation of bf16 inputs, one launch. Projection on bf16 MFMA:
+// Y_z[bh, n, c] = out_scale_z * sum_k X_z[bh, n, k] P[h, k, c] for z < nz (nz = 1 or 2,
+// e.g. queries and keys), accumulated in fp32 and rounded once to fp16 (out_f16) or bf16.
+// P is [H, d, m]; columns m <= c < out_cols are written as zeros. Output rows are out_stride
+// elements apart. If kmax is not null, kmax[bh * proj_blocks(N) + b] receives the largest
+// row norm (fp32, before rounding) of Y1 over tokens b*256 .. b*256+255 of head bh. If Vt is
+// not null, the same launch writes V^T of V ([BH, N, dv] bf16) in the layout above.
+hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, void* Y0,
+                               void* Y1, int nz, int BH, int H, int N, int d, int m,
+                               int out_stride, int out_cols, float out_scale0,
+                               float out_scale1, bool out_f16, float* kmax, const void* V,
+                               void* Vt, int dv, hipStream_t stream);
 
 // Attention over projected inputs. Qt and Kt are fp16 [BH, N, mp] with zero columns past m
 // (score MFMA in fp16); Qt is pre-scaled by scale*log2(e) so the scores come out in base-2
-// exponent units. Vt is V^T as written by launch_vt_bf16 (weights x V MFMA in bf16). O is
+// exponent units. Vt is V^T as written by launch_project_bf16 (weights x V MFMA in bf16). O is
 // [BH, N, dv] in fp32 (out_f32) or bf16; lse [BH, N] optional. kmax holds the per-block key
 // norm maxima written by the projection launch.
 hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* Vt, const float* kmax,
