@@ -158,6 +158,18 @@ def main() -> int:
     proj_ms, attn_ms, calls = spa.profile_end()
     ev_ms = ev0.elapsed_time(ev1)
 
+    # Distribution of single calls (after the timed region, not part of it): each call
+    # bracketed by its own events on the launch stream.
+    per_call = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        per_call.append(e0.elapsed_time(e1))
+    per_call.sort()
+
     work = accounting.work(w.B, w.H, w.N, w.d, w.m, w.dv, w.causal)
     ms_per_step = max(wall * 1e3, ev_ms) / args.steps
     value = work.total_flops / (ms_per_step * 1e-3) / 1e12
@@ -185,6 +197,10 @@ def main() -> int:
                    "flops_per_step": work.total_flops},
         "pct_of_bf16_peak": round(100.0 * value / accounting.PEAK_BF16_DENSE_TFLOPS, 2),
         "launch_ms": {"project": round(proj_ms / calls, 5), "attn": round(attn_avg_ms, 5)},
+        "call_ms": {"median": round(per_call[len(per_call) // 2], 5),
+                    "min": round(per_call[0], 5),
+                    "p90": round(per_call[int(0.9 * (len(per_call) - 1))], 5),
+                    "calls": len(per_call)},
         "roofline": {
             "kernel": "attn_bf16_kernel" if w.dtype == "bf16" else "attn_f32_kernel",
             "bound": "mfma",
