@@ -57,6 +57,10 @@ def configure(lib):
                                          i64, i64, i64, i64, i64, i64, ip, ip, i64, dp, dp,
                                          ctypes.c_int]
     lib.spa_oracle_attn_rows.restype = ctypes.c_int
+    lib.spa_oracle_attn_bwd.argtypes = [dp, dp, dp, dp, dp, ctypes.c_double, ctypes.c_int,
+                                        i64, i64, i64, i64, i64, i64, dp, dp, dp, dp,
+                                        ctypes.c_int]
+    lib.spa_oracle_attn_bwd.restype = ctypes.c_int
     for name in ("spa_oracle_scores", "spa_oracle_weights"):
         f = getattr(lib, name)
         f.argtypes = [dp, dp, dp, ctypes.c_double, ctypes.c_int, i64, i64, i64, i64, i64, dp,
@@ -119,6 +123,21 @@ def attn_fwd(Q, K, V, P, scale: float, causal: bool, with_lse: bool = False,
                                      _ptr(lse) if with_lse else None, nthreads)
     _check(rc, "attn_fwd")
     return (O, lse) if with_lse else O
+
+
+def attn_bwd(Q, K, V, P, dO, scale: float, causal: bool, nthreads: int = 0):
+    """Gradients of L = sum(dO * O) for the forward above: (dQ, dK, dV, dP), float64."""
+    Q, K, V, P, dO = _f64(Q), _f64(K), _f64(V), _f64(P), _f64(dO)
+    B, H, N, d, m, dv = _shape4(Q, K, V, P)
+    if dO.shape != V.shape:
+        raise ValueError("dO must have the shape of V (and of O)")
+    dQ, dK = np.empty((B, H, N, d)), np.empty((B, H, N, d))
+    dV, dP = np.empty((B, H, N, dv)), np.empty((H, d, m))
+    rc = _load().spa_oracle_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(P), _ptr(dO), float(scale),
+                                     int(bool(causal)), B, H, N, d, m, dv, _ptr(dQ), _ptr(dK),
+                                     _ptr(dV), _ptr(dP), nthreads)
+    _check(rc, "attn_bwd")
+    return dQ, dK, dV, dP
 
 
 def attn_rows(Q, K, V, P, scale: float, causal: bool, row_bh, row_i, with_lse: bool = False,

@@ -291,3 +291,126 @@ int spa_oracle_weights(const double* Q, const double* K, const double* P, double
     }
     return 0;
 }
+
+/*
+ * Backward of spa_oracle_attn_fwd for a loss L with dL/dO = dO: the chain rule of the
+ * definition above. The "Sparse Projection Attention" page, Sec. 3.2 and Algorithm 2, learns
+ * the projection by backpropagation and writes the query term of dL/dP; P multiplies the
+ * keys too, so the key term enters the same way. Per (b, h), with A the row softmax and
+ * O = A V as in the forward:
+ *
+ *   D_i    = sum_c dO_ic O_ic
+ *   dA_ij  = sum_c dO_ic V_jc
+ *   dS_ij  = A_ij (dA_ij - D_i)            (zero where the causal mask removes the key)
+ *   dV_j   = sum_i A_ij dO_i
+ *   dQt_i  = scale sum_j dS_ij Kt_j,       dKt_j = scale sum_i dS_ij Qt_i
+ *   dQ     = dQt P_h^T,  dK = dKt P_h^T,   dP_h = sum_b (Q^T dQt + K^T dKt)
+ *
+ * Rows are visited in ascending order within a head, heads in parallel; dP is summed over
+ * b in ascending order at the end. Arrays: dO, dV [B,H,N,dv]; dQ, dK [B,H,N,d]; dP [H,d,m].
+ */
+int spa_oracle_attn_bwd(const double* Q, const double* K, const double* V, const double* P,
+                        const double* dO, double scale, int causal, int64_t B, int64_t H,
+                        int64_t N, int64_t d, int64_t m, int64_t dv, double* dQ, double* dK,
+                        double* dV, double* dP, int nthreads) {
+    if (check_attn_args(Q, K, V, P, scale, causal, B, H, N, d, m, dv)) return -1;
+    if (!dO || !dQ || !dK || !dV || !dP) return -1;
+    const int nt = threads_to_use(nthreads);
+    const int64_t BH = B * H;
+    double* dPp = (double*)calloc((size_t)(BH * d * m), sizeof(double));
+    if (!dPp) return -2;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const int64_t h = bh % H;
+        const double* ph = P + h * d * m;
+        const double* Qh = Q + bh * N * d;
+        const double* Kh = K + bh * N * d;
+        const double* Vh = V + bh * N * dv;
+        const double* dOh = dO + bh * N * dv;
+        double* dVh = dV + bh * N * dv;
+        double* Qt = (double*)malloc(sizeof(double) * (size_t)(N * m));
+        double* Kt = (double*)malloc(sizeof(double) * (size_t)(N * m));
+        double* dQt = (double*)calloc((size_t)(N * m), sizeof(double));
+        double* dKt = (double*)calloc((size_t)(N * m), sizeof(double));
+        double* a = (double*)malloc(sizeof(double) * (size_t)N);
+        double* o = (double*)malloc(sizeof(double) * (size_t)dv);
+        if (!Qt || !Kt || !dQt || !dKt || !a || !o) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            for (int64_t n = 0; n < N; ++n) {
+                project_row(Qh + n * d, ph, d, m, Qt + n * m);
+                project_row(Kh + n * d, ph, d, m, Kt + n * m);
+            }
+            for (int64_t j = 0; j < N * dv; ++j) dVh[j] = 0.0;
+            for (int64_t i = 0; i < N; ++i) {
+                const int64_t nk = key_count(i, N, causal);
+                /* the forward's row: scores, two-pass softmax, output */
+                for (int64_t j = 0; j < nk; ++j) {
+                    double acc = 0.0;
+                    for (int64_t c = 0; c < m; ++c) acc += Qt[i * m + c] * Kt[j * m + c];
+                    a[j] = scale * acc;
+                }
+                double mx = -INFINITY;
+                for (int64_t j = 0; j < nk; ++j)
+                    if (a[j] > mx) mx = a[j];
+                double sum = 0.0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    a[j] = exp(a[j] - mx);
+                    sum += a[j];
+                }
+                for (int64_t j = 0; j < nk; ++j) a[j] /= sum;
+                for (int64_t c = 0; c < dv; ++c) o[c] = 0.0;
+                for (int64_t j = 0; j < nk; ++j)
+                    for (int64_t c = 0; c < dv; ++c) o[c] += a[j] * Vh[j * dv + c];
+                /* D_i */
+                double Di = 0.0;
+                for (int64_t c = 0; c < dv; ++c) Di += dOh[i * dv + c] * o[c];
+                /* per key: dA, dS, and the three accumulations */
+                for (int64_t j = 0; j < nk; ++j) {
+                    double dA = 0.0;
+                    for (int64_t c = 0; c < dv; ++c) dA += dOh[i * dv + c] * Vh[j * dv + c];
+                    const double dS = a[j] * (dA - Di);
+                    for (int64_t c = 0; c < dv; ++c) dVh[j * dv + c] += a[j] * dOh[i * dv + c];
+                    for (int64_t c = 0; c < m; ++c) {
+                        dQt[i * m + c] += scale * dS * Kt[j * m + c];
+                        dKt[j * m + c] += scale * dS * Qt[i * m + c];
+                    }
+                }
+            }
+            /* back through the projection */
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t k = 0; k < d; ++k) {
+                    double gq = 0.0, gk = 0.0;
+                    for (int64_t c = 0; c < m; ++c) {
+                        gq += dQt[n * m + c] * ph[k * m + c];
+                        gk += dKt[n * m + c] * ph[k * m + c];
+                    }
+                    dQ[(bh * N + n) * d + k] = gq;
+                    dK[(bh * N + n) * d + k] = gk;
+                }
+            double* dPb = dPp + bh * d * m;
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t k = 0; k < d; ++k)
+                    for (int64_t c = 0; c < m; ++c)
+                        dPb[k * m + c] += Qh[n * d + k] * dQt[n * m + c] + Kh[n * d + k] * dKt[n * m + c];
+        }
+        free(Qt);
+        free(Kt);
+        free(dQt);
+        free(dKt);
+        free(a);
+        free(o);
+    }
+    if (!failed) {
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t e = 0; e < d * m; ++e) {
+                double acc = 0.0;
+                for (int64_t b = 0; b < B; ++b) acc += dPp[(b * H + h) * d * m + e];
+                dP[h * d * m + e] = acc;
+            }
+    }
+    free(dPp);
+    return failed ? -2 : 0;
+}
