@@ -125,6 +125,47 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Workspace bytes spa_attn_bwd needs for these sizes (0 for arguments it would reject).
+ * Contents (each region 256-byte aligned): the projected queries (scaled by
+ * scale*log2(e)) and keys, fp16, row-major and transposed; dO transposed (bf16); the row
+ * terms D_i = <dO_i, O_i> (fp32); the gradients of the projected queries and keys (fp32);
+ * the projection gradient's per-256-row partial sums (fp32).
+ */
+size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
+                                    spa_dtype_t dtype);
+
+/*
+ * spa_attn_bwd -- gradients of a loss L through spa_attn_fwd, given dO = dL/dO: the chain
+ * rule of the forward's definition (SPA page Sec. 3.1.3 and Algorithm 1; Sec. 3.2 and
+ * Algorithm 2 learn the projection by backpropagation and write the query term of its
+ * gradient, the key term entering the same way). With A the forward's row softmax:
+ *
+ *   D_i = <dO_i, O_i>,  dS_ij = A_ij (<dO_i, V_j> - D_i)
+ *   dV_j = sum_i A_ij dO_i,  dQ = scale * (dS Kt) P^T,  dK = scale * (dS^T Qt) P^T
+ *   dP_h = sum over batches of Q^T (scale dS Kt) + K^T (scale dS^T Qt)
+ *
+ *   Q, K, V, P, scale, causal, B, H, N, d, m, dv, dtype: as passed to spa_attn_fwd.
+ *   O    [B,H,N,dv] the forward's output, bf16; dO [B,H,N,dv] bf16.
+ *   lse  [B,H,N] fp32, the forward's lse output (the weights are recomputed from it).
+ *   dQ, dK [B,H,N,d] and dV [B,H,N,dv] in g_dtype (SPA_BF16 or SPA_F32); dP [H,d,m] fp32.
+ *        No output may overlap an input, another output or the workspace.
+ *   workspace / workspace_bytes: as for spa_attn_fwd, sized by
+ *        spa_attn_bwd_workspace_bytes (NULL: allocated and freed stream-ordered).
+ *
+ * Supported: dtype SPA_BF16, d in {64, 128}, dv in {64, 128}, 1 <= m <= 64
+ * (SPA_ERR_UNSUPPORTED otherwise). The projected queries and keys are prepared exactly as
+ * in the forward (fp16), so the recomputed scores match the forward's bit for bit; the
+ * weights meet dO in bf16 and dS meets the projected operands in fp16, all on MFMA with fp32
+ * accumulation. Six launches on `stream`; results are deterministic (no atomics).
+ */
+spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const void* P,
+                          const void* O, const void* dO, const float* lse, float scale,
+                          int causal, int B, int H, int N, int d, int m, int dv,
+                          spa_dtype_t dtype, void* dQ, void* dK, void* dV, float* dP,
+                          spa_dtype_t g_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * Per-launch timing for benchmarks. spa_profile_begin(max_calls) starts recording HIP
  * events around the projection and attention launches of the next max_calls spa_attn_fwd
  * calls (1 <= max_calls <= 65536; fails with SPA_ERR_INVALID_ARGUMENT if a recording is

@@ -26,8 +26,8 @@ SPA_F32 = 0
 SPA_BF16 = 1
 
 EXPORTS = ("spa_version", "spa_status_string", "spa_last_error", "spa_project",
-           "spa_attn_fwd_workspace_bytes", "spa_attn_fwd", "spa_profile_begin",
-           "spa_profile_end")
+           "spa_attn_fwd_workspace_bytes", "spa_attn_fwd", "spa_attn_bwd_workspace_bytes",
+           "spa_attn_bwd", "spa_profile_begin", "spa_profile_end")
 
 
 class SpaError(RuntimeError):
@@ -65,6 +65,11 @@ def lib() -> ctypes.CDLL:
     L.spa_attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.spa_attn_fwd.restype = st
     L.spa_attn_fwd.argtypes = [vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, vp, i, vp, vp, z, vp]
+    L.spa_attn_bwd_workspace_bytes.restype = z
+    L.spa_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.spa_attn_bwd.restype = st
+    L.spa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, vp, vp,
+                               vp, vp, i, vp, z, vp]
     L.spa_profile_begin.restype = st
     L.spa_profile_begin.argtypes = [i]
     dp = ctypes.POINTER(ctypes.c_double)
@@ -172,6 +177,56 @@ def spa_attn_fwd(Q, K, V, P, scale: float | None = None, causal: bool = False,
                              lse.data_ptr() if lse is not None else None, ws_ptr, ws_bytes,
                              _stream_ptr(Q.device)))
     return (out, lse) if return_lse else out
+
+
+def spa_attn_bwd_workspace_bytes(B, H, N, d, m, dv, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().spa_attn_bwd_workspace_bytes(B, H, N, d, m, dv, code))
+
+
+def spa_attn_bwd(Q, K, V, P, O, dO, lse, scale: float | None = None, causal: bool = False,
+                 grad_dtype=None, workspace=None):
+    """Gradients (dQ, dK, dV, dP) of a loss through spa_attn_fwd, given dO = dL/dO.
+
+    Q, K, V, P as passed to spa_attn_fwd (bf16); O the forward's output (bf16) and lse its
+    log-sum-exp (fp32 [B,H,N], spa_attn_fwd(..., return_lse=True)); dO bf16 like O.
+    grad_dtype: torch.float32 or torch.bfloat16 for dQ, dK, dV (default float32); dP is
+    fp32 [H,d,m]. Runs on the current stream.
+    """
+    torch = _torch()
+    for name, x in (("Q", Q), ("K", K), ("V", V), ("P", P), ("O", O), ("dO", dO), ("lse", lse)):
+        _device_tensor(x, name)
+    if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3]:
+        raise ValueError("Q, K must be [B,H,N,d] and V [B,H,N,dv]")
+    B, H, N, d = Q.shape
+    dv = V.shape[3]
+    if P.dim() != 3 or P.shape[0] != H or P.shape[1] != d:
+        raise ValueError("P must be [H,d,m]")
+    m = P.shape[2]
+    if O.shape != V.shape or dO.shape != V.shape or lse.shape != (B, H, N):
+        raise ValueError("O and dO must be [B,H,N,dv] and lse [B,H,N]")
+    if lse.dtype != torch.float32:
+        raise ValueError("lse must be float32")
+    dt = Q.dtype
+    if any(x.dtype != dt for x in (K, V, P)):
+        raise ValueError("Q, K, V and P must share a dtype")
+    gdt = torch.float32 if grad_dtype is None else grad_dtype
+    dQ = torch.empty((B, H, N, d), dtype=gdt, device=Q.device)
+    dK = torch.empty((B, H, N, d), dtype=gdt, device=Q.device)
+    dV = torch.empty((B, H, N, dv), dtype=gdt, device=Q.device)
+    dP = torch.empty((H, d, m), dtype=torch.float32, device=Q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _device_tensor(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().spa_attn_bwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), P.data_ptr(),
+                             O.data_ptr(), dO.data_ptr(), lse.data_ptr(), float(scale),
+                             int(bool(causal)), B, H, N, d, m, dv, _dtype_code(dt),
+                             dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), dP.data_ptr(),
+                             _dtype_code(gdt), ws_ptr, ws_bytes, _stream_ptr(Q.device)))
+    return dQ, dK, dV, dP
 
 
 def profile_begin(max_calls: int) -> None:

@@ -76,6 +76,36 @@ WorkspaceLayout workspace_layout(int BH, int N, int m, int dv, spa_dtype_t dtype
     return w;
 }
 
+// Backward workspace (bf16 path), each region 256-byte aligned: projected queries (scaled)
+// and keys, fp16 [BH, N, mp] each; the same transposed, fp16 [BH, mp, Np] each; dO
+// transposed, bf16 [BH, dv, Np]; D, fp32 [BH, N]; the projected gradients, fp32 [BH, N, mp]
+// each; the projection gradient's partials, fp32 [BH, ceil(N / 256), d, m].
+struct BwdLayout {
+    size_t qs, kt, qst, ktt, dot, D, dqt, dkt, part, total;
+};
+BwdLayout bwd_layout(int BH, int N, int d, int m, int dv) {
+    const size_t mp = (size_t)spa::padded_m(m), np = (size_t)spa::vt_padded_keys(N);
+    const size_t rows = (size_t)BH * N;
+    BwdLayout w;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    w.qs = take(rows * mp * 2);
+    w.kt = take(rows * mp * 2);
+    w.qst = take((size_t)BH * mp * np * 2);
+    w.ktt = take((size_t)BH * mp * np * 2);
+    w.dot = take((size_t)BH * dv * np * 2);
+    w.D = take(rows * 4);
+    w.dqt = take(rows * mp * 4);
+    w.dkt = take(rows * mp * 4);
+    w.part = take((size_t)BH * ((N + 255) / 256) * d * m * 4);
+    w.total = o;
+    return w;
+}
+
 spa_status_t check_dims(const char* fn, int B, int H, int N, int d, int m, int dv) {
     if (B < 1 || H < 1 || N < 1 || d < 1 || m < 1 || dv < 1)
         return fail(SPA_ERR_INVALID_ARGUMENT,
@@ -293,6 +323,129 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
         }
     }
     if (e == hipSuccess && ev[2]) e = hipEventRecord(ev[2], s);
+    if (!workspace) {
+        hipError_t e2 = hipFreeAsync(ws, s);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return SPA_OK;
+}
+
+size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
+                                    spa_dtype_t dtype) {
+    if (B < 1 || H < 1 || N < 1 || N > kMaxN || (long long)B * H * N >= kMaxRows) return 0;
+    if (dtype != SPA_BF16 || (d != 64 && d != 128) || m < 1 || m > 64 || (dv != 64 && dv != 128))
+        return 0;
+    return bwd_layout(B * H, N, d, m, dv).total;
+}
+
+spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const void* P,
+                          const void* O, const void* dO, const float* lse, float scale,
+                          int causal, int B, int H, int N, int d, int m, int dv,
+                          spa_dtype_t dtype, void* dQ, void* dK, void* dV, float* dP,
+                          spa_dtype_t g_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    g_err[0] = '\0';
+    const char* fn = "spa_attn_bwd";
+    if (!Q || !K || !V || !P || !O || !dO || !lse || !dQ || !dK || !dV || !dP)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+    spa_status_t st = check_dims(fn, B, H, N, d, m, dv);
+    if (st != SPA_OK) return st;
+    if (causal != 0 && causal != 1)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1, got %d", fn, causal);
+    if (!std::isfinite(scale))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: scale must be finite", fn);
+    if (dtype != SPA_BF16 && dtype != SPA_F32)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
+    if (g_dtype != SPA_BF16 && g_dtype != SPA_F32)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: unknown g_dtype %d", fn, (int)g_dtype);
+    if (dtype != SPA_BF16)
+        return fail(SPA_ERR_UNSUPPORTED, "%s: only the bf16 path has a backward", fn);
+    if ((d != 64 && d != 128) || m > 64 || (dv != 64 && dv != 128))
+        return fail(SPA_ERR_UNSUPPORTED,
+                    "%s: backward needs d in {64,128}, m <= 64, dv in {64,128} (d=%d m=%d dv=%d)",
+                    fn, d, m, dv);
+    const void* al16[] = {Q, K, V, P, O, dO, dQ, dK, dV};
+    for (const void* p : al16)
+        if (!aligned(p, 16))
+            return fail(SPA_ERR_INVALID_ARGUMENT, "%s: tensor base not 16-byte aligned", fn);
+    if (!aligned(lse, 4) || !aligned(dP, 4))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: lse or dP not 4-byte aligned", fn);
+    if (workspace && !aligned(workspace, 16))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace not 16-byte aligned", fn);
+    const long long rows = (long long)B * H * N;
+    const BwdLayout wl = bwd_layout(B * H, N, d, m, dv);
+    if (workspace && workspace_bytes < wl.total)
+        return fail(SPA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn,
+                    workspace_bytes, wl.total);
+    const size_t ge = g_dtype == SPA_F32 ? 4 : 2;
+    const Range ins[8] = {range(Q, rows * d * 2),  range(K, rows * d * 2),
+                          range(V, rows * dv * 2), range(P, (size_t)H * d * m * 2),
+                          range(O, rows * dv * 2), range(dO, rows * dv * 2),
+                          range(lse, rows * 4),    range(workspace, workspace ? wl.total : 0)};
+    const Range outs[4] = {range(dQ, rows * d * ge), range(dK, rows * d * ge),
+                           range(dV, rows * dv * ge), range(dP, (size_t)H * d * m * 4)};
+    for (int i = 0; i < 4; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r))
+                return fail(SPA_ERR_INVALID_ARGUMENT, "%s: an output overlaps an input or the workspace", fn);
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], outs[j]))
+                return fail(SPA_ERR_INVALID_ARGUMENT, "%s: outputs overlap", fn);
+    }
+    if (workspace)
+        for (int i = 0; i < 7; ++i)
+            if (overlap(ins[7], ins[i]))
+                return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace overlaps an input", fn);
+
+    // ---- validated: HIP work starts here ------------------------------------------------
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    if (!ws) {
+        hipError_t e = hipMallocAsync(&ws, wl.total, s);
+        if (e != hipSuccess) return hip_fail("spa_attn_bwd: hipMallocAsync", e);
+    }
+    char* w = static_cast<char*>(ws);
+    const int mp = spa::padded_m(m);
+    const float qscale = scale * 1.44269504088896340736f;
+    hipError_t e = spa::launch_project_bf16(Q, K, P, w + wl.qs, w + wl.kt, 2, B * H, H, N, d, m,
+                                            mp, mp, qscale, 1.0f, /*out_f16=*/true, nullptr, dO,
+                                            w + wl.dot, dv, s, w + wl.qst, w + wl.ktt);
+    if (e == hipSuccess) {
+        spa::BwdArgs a;
+        a.Q = static_cast<const uint16_t*>(Q);
+        a.K = static_cast<const uint16_t*>(K);
+        a.P = static_cast<const uint16_t*>(P);
+        a.Qs = reinterpret_cast<const uint16_t*>(w + wl.qs);
+        a.Kt = reinterpret_cast<const uint16_t*>(w + wl.kt);
+        a.Qst = reinterpret_cast<const uint16_t*>(w + wl.qst);
+        a.Ktt = reinterpret_cast<const uint16_t*>(w + wl.ktt);
+        a.V = static_cast<const uint16_t*>(V);
+        a.O = static_cast<const uint16_t*>(O);
+        a.dO = static_cast<const uint16_t*>(dO);
+        a.dOt = reinterpret_cast<const uint16_t*>(w + wl.dot);
+        a.lse = lse;
+        a.D = reinterpret_cast<float*>(w + wl.D);
+        a.dQt = reinterpret_cast<float*>(w + wl.dqt);
+        a.dKt = reinterpret_cast<float*>(w + wl.dkt);
+        a.dPpart = reinterpret_cast<float*>(w + wl.part);
+        a.dP = dP;
+        a.dQ = dQ;
+        a.dK = dK;
+        a.dV = dV;
+        a.g_f32 = g_dtype == SPA_F32 ? 1 : 0;
+        a.BH = B * H;
+        a.H = H;
+        a.N = N;
+        a.Np = spa::vt_padded_keys(N);
+        a.d = d;
+        a.m = m;
+        a.mp = mp;
+        a.dv = dv;
+        a.causal = causal;
+        a.scale = scale;
+        e = spa::launch_attn_bwd_bf16(a, s);
+    }
     if (!workspace) {
         hipError_t e2 = hipFreeAsync(ws, s);
         if (e == hipSuccess) e = e2;

@@ -1,0 +1,598 @@
+// spa_bwd.hip -- backward of the projected attention for bf16 inputs on gfx950 MFMA.
+//
+// What it computes: the chain rule of the forward ("Sparse Projection Attention" page,
+// Sec. 3.1.3 and Algorithm 1; Sec. 3.2 and Algorithm 2 train the projection by
+// backpropagation, with the query term of the projection's gradient written out; the key
+// term enters the same way). With A the row softmax of the forward, O = A V, dO = dL/dO:
+//   D_i = <dO_i, O_i>,  dA_ij = <dO_i, V_j>,  dS_ij = A_ij (dA_ij - D_i)
+//   dV_j = sum_i A_ij dO_i,  dQt_i = scale sum_j dS_ij Kt_j,  dKt_j = scale sum_i dS_ij Qt_i
+//   dQ = dQt P^T,  dK = dKt P^T,  dP_h = sum over batches and rows of Q^T dQt + K^T dKt.
+// The weights A are recomputed from the forward's log-sum-exp: the projected queries and keys
+// are prepared exactly as in the forward (fp16, queries pre-scaled by scale*log2(e)), so the
+// recomputed base-2 scores are the forward's, bit for bit.
+//
+// Kernels (all on 32x32x16 MFMA; see the forward for the operand layouts):
+//   bwd_q_kernel   query-major: per 32-query wave, a loop over 32-key tiles computes
+//                  dQt^T = Kt^T . dS^T, after D_i from the wave's own dO and O rows.
+//   bwd_kv_kernel  key-major: per 32-key wave, a loop over 32-query tiles computes
+//                  dV^T = dO^T . A and dKt^T = Qt^T . dS. Needs D from bwd_q_kernel.
+//   proj_back_kernel   dQ = dQt P^T and dK = dKt P^T.
+//   dp_partial_kernel / dp_reduce_kernel   the projection gradient, per 256-row chunk and
+//                  then summed over chunks and batches in a fixed order (deterministic).
+// In the transposed (A-operand) tiles the rows are V^T-ordered: within every 16 tokens the
+// order 0-3, 8-11, 4-7, 12-15, which is the order in which a score accumulator lane holds
+// its 8 tokens of a 16-token k-step. So every MFMA operand is one 16-byte LDS read or a
+// register, as in the forward.
+#include "spa_device.h"
+#include "spa_internal.h"
+
+namespace spa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 32;  // keys (query-major kernel) or queries (key-major kernel) per step
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// fp32 score-layout values (slots 8*half + j of k-step tt) -> packed pairs
+template <bool F16>
+__device__ __forceinline__ u32x4 pack_kstep(const f32x16& x, int tt) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float lo = x[8 * tt + 2 * j], hi = x[8 * tt + 2 * j + 1];
+        w[j] = F16 ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+    }
+    return w;
+}
+
+// ---------------------------------------------------------------------------------------
+// Query-major kernel: dQt and D.
+// Inputs: Qs [BH,N,MP] fp16 (scaled), Kt [BH,N,MP] fp16, Ktt [BH,MP,Np] fp16 (transposed,
+// permuted), V [BH,N,DV] bf16, O, dO [BH,N,DV] bf16, lse [BH,N] (natural log).
+// Outputs: dQt [BH,N,MP] fp32 (scaled by `scale`), D [BH,N] fp32.
+template <int MP, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
+    const uint16_t* __restrict__ Qs, const uint16_t* __restrict__ Kt,
+    const uint16_t* __restrict__ Ktt, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+    const float* __restrict__ lse, float* __restrict__ dQt, float* __restrict__ Dout, int N,
+    int Np, int nqb, float scale) {
+    constexpr int KS = MP / 16;                // score k-steps
+    constexpr int MB = (MP + 31) / 32;         // 32-row blocks of dQt^T
+    constexpr int CS = DV / 16;                // dA k-steps
+    constexpr int K_B = kTile * MP * 2;        // Kt tile bytes
+    constexpr int KT_B = MB * 32 * kTile * 2;  // Kt^T tile bytes (rows past MP zero)
+    constexpr int V_B = kTile * DV * 2;        // V tile bytes
+    constexpr int BUF = K_B + KT_B + V_B;
+    constexpr int NCH = BUF / 16;              // 16-byte chunks per tile
+    constexpr int CPT = (NCH + kThreads - 1) / kThreads;
+    __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+
+    const int bh = blockIdx.x / nqb;
+    const int qb = blockIdx.x - bh * nqb;
+    const int q0 = qb * 128;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+    const int myq = q0 + wave * 32 + col;
+    const bool qvalid = myq < N;
+
+    const uint16_t* Qh = Qs + (size_t)bh * N * MP;
+    const uint16_t* Kh = Kt + (size_t)bh * N * MP;
+    const uint16_t* Kth = Ktt + (size_t)bh * MP * Np;
+    const uint16_t* Vh = V + (size_t)bh * N * DV;
+
+    // This lane's query (B operand of the scores) and dO row (B operand of dA).
+    f16x8 qf[KS];
+    bf16x8 dof[CS];
+    float dpart = 0.0f;  // this lane's half of <dO_q, O_q>
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (qvalid) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)myq * MP + ks * 16 + half * 8);
+        qf[ks] = __builtin_bit_cast(f16x8, v);
+    }
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+        u32x4 v = {0u, 0u, 0u, 0u}, o = {0u, 0u, 0u, 0u};
+        if (qvalid) {
+            const size_t off = ((size_t)bh * N + myq) * DV + cs * 16 + half * 8;
+            v = *reinterpret_cast<const u32x4*>(dO + off);
+            o = *reinterpret_cast<const u32x4*>(O + off);
+        }
+        dof[cs] = __builtin_bit_cast(bf16x8, v);
+        const bf16x8 ob = __builtin_bit_cast(bf16x8, o);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dpart += (float)dof[cs][i] * (float)ob[i];
+    }
+    const float Dq = halves_sum(dpart);
+    const float lse2 = qvalid ? lse[(size_t)bh * N + myq] * kLog2e : INFINITY;
+
+    const int kend = CAUSAL ? min(N, q0 + 128) : N;
+    const int ntiles = (kend + kTile - 1) / kTile;
+
+    // Tile staging: chunk c of the tile -> (region, row, 16-byte column).
+    u32x4 stage[CPT];
+    auto load_tile = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * kThreads;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (c < K_B / 16) {
+                const int r = c / (MP / 8), cc = c % (MP / 8);
+                if (k0 + r < N) v = *reinterpret_cast<const u32x4*>(Kh + (size_t)(k0 + r) * MP + cc * 8);
+            } else if (c < (K_B + KT_B) / 16) {
+                const int c2 = c - K_B / 16;
+                const int r = c2 / 4, cc = c2 % 4;  // feature row, 16-byte column of 32 keys
+                if (r < MP) v = *reinterpret_cast<const u32x4*>(Kth + (size_t)r * Np + k0 + cc * 8);
+            } else if (c < NCH) {
+                const int c2 = c - (K_B + KT_B) / 16;
+                const int r = c2 / (DV / 8), cc = c2 % (DV / 8);
+                if (k0 + r < N) v = *reinterpret_cast<const u32x4*>(Vh + (size_t)(k0 + r) * DV + cc * 8);
+            }
+            stage[i] = v;
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * kThreads;
+            if (c < NCH) *reinterpret_cast<u32x4*>(lds + buf * BUF + c * 16) = stage[i];
+        }
+    };
+
+    f32x16 acc[MB];
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[b] = f32x16_fill(0.0f);
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int t = 0; t < ntiles; ++t) {
+        const int k0 = t * kTile;
+        if (t + 1 < ntiles) load_tile(k0 + kTile);
+        const char* Ks = lds + (t & 1) * BUF;
+        const char* Kts = Ks + K_B;
+        const char* Vs = Kts + KT_B;
+        // causal: a wave whose queries all precede the tile has nothing to do in it
+        if (!CAUSAL || k0 <= q0 + wave * 32 + 31) {
+            // scores^T (32 keys x 32 queries), base-2 units
+            f32x16 s = f32x16_fill(0.0f);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const f16x8 a = __builtin_bit_cast(
+                    f16x8, *reinterpret_cast<const u32x4*>(Ks + col * MP * 2 + (ks * 16 + half * 8) * 2));
+                s = mfma32x32x16(a, qf[ks], s);
+            }
+            // dA^T (32 keys x 32 queries) = V . dO^T
+            f32x16 da = f32x16_fill(0.0f);
+#pragma unroll
+            for (int cs = 0; cs < CS; ++cs) {
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(Vs + col * DV * 2 + (cs * 16 + half * 8) * 2));
+                da = mfma32x32x16(a, dof[cs], da);
+            }
+            // dS = A (dA - D), masked entries zero
+            f32x16 ds;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
+                float w = __builtin_amdgcn_exp2f(s[i] - lse2);
+                if (CAUSAL && key > myq) w = 0.0f;
+                ds[i] = w * (da[i] - Dq);
+            }
+            // dQt^T (MP x 32 queries) += Kt^T . dS^T
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const f16x8 b = __builtin_bit_cast(f16x8, pack_kstep<true>(ds, tt));
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const f16x8 a = __builtin_bit_cast(
+                        f16x8, *reinterpret_cast<const u32x4*>(Kts + (mb * 32 + col) * kTile * 2 + (tt * 16 + half * 8) * 2));
+                    acc[mb] = mfma32x32x16(a, b, acc[mb]);
+                }
+            }
+        }
+        __syncthreads();  // everyone is done with the other buffer ...
+        if (t + 1 < ntiles) store_tile((t + 1) & 1);
+        __syncthreads();  // ... and the next tile is in it
+    }
+
+    if (qvalid) {
+        float* dst = dQt + ((size_t)bh * N + myq) * MP;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c0 = mb * 32 + 8 * g + 4 * half;
+                if (c0 < MP)
+                    *reinterpret_cast<float4*>(dst + c0) =
+                        make_float4(acc[mb][4 * g] * scale, acc[mb][4 * g + 1] * scale,
+                                    acc[mb][4 * g + 2] * scale, acc[mb][4 * g + 3] * scale);
+            }
+        if (half == 0) Dout[(size_t)bh * N + myq] = Dq;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Key-major kernel: dV and dKt.
+// Inputs: Qs [BH,N,MP] fp16 (scaled), Qst [BH,MP,Np] fp16 (transposed, permuted), Kt
+// [BH,N,MP] fp16, V [BH,N,DV] bf16, dO [BH,N,DV] bf16, dOt [BH,DV,Np] bf16 (transposed,
+// permuted), lse [BH,N], D [BH,N].
+// Outputs: dV [BH,N,DV] (fp32 or bf16), dKt [BH,N,MP] fp32 (scale applied).
+template <int MP, int DV, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd_kv_kernel(
+    const uint16_t* __restrict__ Qs, const uint16_t* __restrict__ Qst,
+    const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const uint16_t* __restrict__ dOt,
+    const float* __restrict__ lse, const float* __restrict__ Din, void* __restrict__ dV,
+    int dv_f32, float* __restrict__ dKt, int N, int Np, int nkb) {
+    constexpr int KS = MP / 16;
+    constexpr int MB = (MP + 31) / 32;
+    constexpr int CS = DV / 16;
+    constexpr int DB = DV / 32;
+    constexpr int Q_B = kTile * MP * 2;        // Qs tile
+    constexpr int QT_B = MB * 32 * kTile * 2;  // Qs^T tile (rows past MP zero)
+    constexpr int DO_B = kTile * DV * 2;       // dO tile
+    constexpr int DOT_B = DV * kTile * 2;      // dO^T tile
+    constexpr int L_B = kTile * 4;             // lse2 of the tile
+    constexpr int BUF = Q_B + QT_B + DO_B + DOT_B + 2 * L_B;
+    constexpr int NCH = (Q_B + QT_B + DO_B + DOT_B) / 16;
+    constexpr int CPT = (NCH + kThreads - 1) / kThreads;
+    __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+
+    const int bh = blockIdx.x / nkb;
+    const int kb = blockIdx.x - bh * nkb;
+    const int k0 = kb * 128;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+    const int k0w = k0 + wave * 32;
+    const int myk = k0w + col;
+    const bool kvalid = myk < N;
+
+    const uint16_t* Qh = Qs + (size_t)bh * N * MP;
+    const uint16_t* Qth = Qst + (size_t)bh * MP * Np;
+    const uint16_t* dOh = dO + (size_t)bh * N * DV;
+    const uint16_t* dOth = dOt + (size_t)bh * DV * Np;
+    const float* lseh = lse + (size_t)bh * N;
+    const float* Dh = Din + (size_t)bh * N;
+
+    // This lane's key (B operand of the scores) and value row (B operand of dA).
+    f16x8 kf[KS];
+    bf16x8 vf[CS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (kvalid) v = *reinterpret_cast<const u32x4*>(Kt + ((size_t)bh * N + myk) * MP + ks * 16 + half * 8);
+        kf[ks] = __builtin_bit_cast(f16x8, v);
+    }
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (kvalid) v = *reinterpret_cast<const u32x4*>(V + ((size_t)bh * N + myk) * DV + cs * 16 + half * 8);
+        vf[cs] = __builtin_bit_cast(bf16x8, v);
+    }
+
+    const int qstart = CAUSAL ? k0 : 0;
+    const int ntiles = (N - qstart + kTile - 1) / kTile;
+
+    u32x4 stage[CPT];
+    float lstage = 0.0f, dstage = 0.0f;
+    auto load_tile = [&](int q0) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * kThreads;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (c < Q_B / 16) {
+                const int r = c / (MP / 8), cc = c % (MP / 8);
+                if (q0 + r < N) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)(q0 + r) * MP + cc * 8);
+            } else if (c < (Q_B + QT_B) / 16) {
+                const int c2 = c - Q_B / 16;
+                const int r = c2 / 4, cc = c2 % 4;
+                if (r < MP) v = *reinterpret_cast<const u32x4*>(Qth + (size_t)r * Np + q0 + cc * 8);
+            } else if (c < (Q_B + QT_B + DO_B) / 16) {
+                const int c2 = c - (Q_B + QT_B) / 16;
+                const int r = c2 / (DV / 8), cc = c2 % (DV / 8);
+                if (q0 + r < N) v = *reinterpret_cast<const u32x4*>(dOh + (size_t)(q0 + r) * DV + cc * 8);
+            } else if (c < NCH) {
+                const int c2 = c - (Q_B + QT_B + DO_B) / 16;
+                const int r = c2 / 4, cc = c2 % 4;
+                v = *reinterpret_cast<const u32x4*>(dOth + (size_t)r * Np + q0 + cc * 8);
+            }
+            stage[i] = v;
+        }
+        if (tid < kTile) {
+            const int q = q0 + tid;
+            lstage = q < N ? lseh[q] * kLog2e : INFINITY;  // rows past N get zero weight
+            dstage = q < N ? Dh[q] : 0.0f;
+        }
+    };
+    auto store_tile = [&](int buf) {
+        char* base = lds + buf * BUF;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * kThreads;
+            if (c < NCH) *reinterpret_cast<u32x4*>(base + c * 16) = stage[i];
+        }
+        if (tid < kTile) {
+            reinterpret_cast<float*>(base + BUF - 2 * L_B)[tid] = lstage;
+            reinterpret_cast<float*>(base + BUF - L_B)[tid] = dstage;
+        }
+    };
+
+    f32x16 dva[DB], dka[MB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) dva[b] = f32x16_fill(0.0f);
+#pragma unroll
+    for (int b = 0; b < MB; ++b) dka[b] = f32x16_fill(0.0f);
+
+    load_tile(qstart);
+    store_tile(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int t = 0; t < ntiles; ++t) {
+        const int q0 = qstart + t * kTile;
+        if (t + 1 < ntiles) load_tile(q0 + kTile);
+        const char* Qts = lds + (t & 1) * BUF;  // Qs tile (rows = queries)
+        const char* QTs = Qts + Q_B;            // Qs^T tile (rows = features)
+        const char* dOs = QTs + QT_B;           // dO tile (rows = queries)
+        const char* dOTs = dOs + DO_B;          // dO^T tile (rows = V columns)
+        const float* L2s = reinterpret_cast<const float*>(Qts + BUF - 2 * L_B);
+        const float* Ds = reinterpret_cast<const float*>(Qts + BUF - L_B);
+        // causal: nothing to do if every query of the tile precedes every key of the wave
+        if (!CAUSAL || q0 + kTile - 1 >= k0w) {
+            // scores^T (32 queries x 32 keys)
+            f32x16 s = f32x16_fill(0.0f);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const f16x8 a = __builtin_bit_cast(
+                    f16x8, *reinterpret_cast<const u32x4*>(Qts + col * MP * 2 + (ks * 16 + half * 8) * 2));
+                s = mfma32x32x16(a, kf[ks], s);
+            }
+            // dA^T (32 queries x 32 keys) = dO . V^T
+            f32x16 da = f32x16_fill(0.0f);
+#pragma unroll
+            for (int cs = 0; cs < CS; ++cs) {
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(dOs + col * DV * 2 + (cs * 16 + half * 8) * 2));
+                da = mfma32x32x16(a, vf[cs], da);
+            }
+            // weights and dS; the row (query) of slot i is 8*(i/4) + 4*half + i%4
+            f32x16 w, ds;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 l4 = *reinterpret_cast<const float4*>(L2s + 8 * g + 4 * half);
+                const float4 d4 = *reinterpret_cast<const float4*>(Ds + 8 * g + 4 * half);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * g + r;
+                    const int q = q0 + 8 * g + 4 * half + r;
+                    float a = __builtin_amdgcn_exp2f(s[i] - lv[r]);
+                    if (CAUSAL && myk > q) a = 0.0f;
+                    w[i] = a;
+                    ds[i] = a * (da[i] - dv4[r]);
+                }
+            }
+            // dV^T (DV x 32 keys) += dO^T . A ; dKt^T (MP x 32 keys) += Qs^T . dS
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const bf16x8 bw = __builtin_bit_cast(bf16x8, pack_kstep<false>(w, tt));
+                const f16x8 bs = __builtin_bit_cast(f16x8, pack_kstep<true>(ds, tt));
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const bf16x8 a = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4*>(dOTs + (db * 32 + col) * kTile * 2 + (tt * 16 + half * 8) * 2));
+                    dva[db] = mfma32x32x16(a, bw, dva[db]);
+                }
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const f16x8 a = __builtin_bit_cast(
+                        f16x8, *reinterpret_cast<const u32x4*>(QTs + (mb * 32 + col) * kTile * 2 + (tt * 16 + half * 8) * 2));
+                    dka[mb] = mfma32x32x16(a, bs, dka[mb]);
+                }
+            }
+        }
+        __syncthreads();
+        if (t + 1 < ntiles) store_tile((t + 1) & 1);
+        __syncthreads();
+    }
+
+    if (kvalid) {
+        const size_t row = (size_t)bh * N + myk;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c0 = db * 32 + 8 * g + 4 * half;
+                const float x0 = dva[db][4 * g], x1 = dva[db][4 * g + 1];
+                const float x2 = dva[db][4 * g + 2], x3 = dva[db][4 * g + 3];
+                if (dv_f32) {
+                    *reinterpret_cast<float4*>(static_cast<float*>(dV) + row * DV + c0) = make_float4(x0, x1, x2, x3);
+                } else {
+                    u32x2 p;
+                    p.x = pack_bf16x2(x0, x1);
+                    p.y = pack_bf16x2(x2, x3);
+                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dV) + row * DV + c0) = p;
+                }
+            }
+        // dKt = scale * sum dS Qt = sum dS Qs / log2(e)
+        float* dst = dKt + row * MP;
+        constexpr float inv = 1.0f / kLog2e;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c0 = mb * 32 + 8 * g + 4 * half;
+                if (c0 < MP)
+                    *reinterpret_cast<float4*>(dst + c0) =
+                        make_float4(dka[mb][4 * g] * inv, dka[mb][4 * g + 1] * inv,
+                                    dka[mb][4 * g + 2] * inv, dka[mb][4 * g + 3] * inv);
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// dX[bh, n, k] = sum_{c < m} dXt[bh, n, c] P[h, k, c] for X in {Q, K} (z = blockIdx.y).
+// One workgroup per (head, 64 rows); P^T and the rows' dXt staged in LDS, fp32 FMAs.
+constexpr int kBackRows = 64;
+__global__ __launch_bounds__(kThreads) void proj_back_kernel(
+    const float* __restrict__ dQt, const float* __restrict__ dKt, const uint16_t* __restrict__ P,
+    void* __restrict__ dQ, void* __restrict__ dK, int out_f32, int N, int H, int d, int m,
+    int mp, int nrb) {
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    float* Ps = sm;                     // [m][d]: P^T of the head
+    float* Xs = sm + m * d;             // [kBackRows][m]
+    const int bh = blockIdx.x / nrb;
+    const int n0 = (blockIdx.x - bh * nrb) * kBackRows;
+    const int z = blockIdx.y;
+    const float* src = (z ? dKt : dQt) + (size_t)bh * N * mp;
+    const int h = bh % H;
+    for (int i = threadIdx.x; i < d * m; i += kThreads) {
+        const int k = i / m, c = i - k * m;
+        Ps[c * d + k] = __uint_as_float((uint32_t)P[(size_t)h * d * m + i] << 16);
+    }
+    for (int i = threadIdx.x; i < kBackRows * m; i += kThreads) {
+        const int r = i / m, c = i - r * m;
+        Xs[i] = n0 + r < N ? src[(size_t)(n0 + r) * mp + c] : 0.0f;
+    }
+    __syncthreads();
+    void* dst = z ? dK : dQ;
+    for (int i = threadIdx.x; i < kBackRows * d; i += kThreads) {
+        const int r = i / d, k = i - r * d;
+        if (n0 + r >= N) continue;
+        float acc = 0.0f;
+        for (int c = 0; c < m; ++c) acc += Xs[r * m + c] * Ps[c * d + k];
+        const size_t o = ((size_t)bh * N + n0 + r) * d + k;
+        if (out_f32) static_cast<float*>(dst)[o] = acc;
+        else static_cast<uint16_t*>(dst)[o] = (uint16_t)(pack_bf16x2(acc, 0.0f) & 0xffffu);
+    }
+}
+
+// partial[bh, chunk, k, c] = sum over the chunk's rows n of Q[n,k] dQt[n,c] + K[n,k] dKt[n,c].
+// Thread t owns feature k = t / TPK and columns c = t % TPK + TPK * i (TPK = 256 / d threads
+// per feature, at most 32 columns each for d >= 64, m <= 64).
+constexpr int kDpRows = 256;
+constexpr int kDpSub = 32;
+constexpr int kDpMaxC = 32;
+__global__ __launch_bounds__(kThreads) void dp_partial_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const float* __restrict__ dQt,
+    const float* __restrict__ dKt, float* __restrict__ part, int N, int d, int m, int mp,
+    int nch) {
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    float* Qs = sm;                      // [kDpSub][d]
+    float* Ks = Qs + kDpSub * d;         // [kDpSub][d]
+    float* dQs = Ks + kDpSub * d;        // [kDpSub][m]
+    float* dKs = dQs + kDpSub * m;       // [kDpSub][m]
+    const int bh = blockIdx.x / nch;
+    const int ch = blockIdx.x - bh * nch;
+    const int n0 = ch * kDpRows;
+    const int tpk = kThreads / d;
+    const int k = threadIdx.x / tpk, c0 = threadIdx.x % tpk;
+    const int nc = (m - c0 + tpk - 1) / tpk;  // columns of this thread
+    float acc[kDpMaxC];
+#pragma unroll
+    for (int i = 0; i < kDpMaxC; ++i) acc[i] = 0.0f;
+    for (int s0 = n0; s0 < n0 + kDpRows && s0 < N; s0 += kDpSub) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < kDpSub * d; i += kThreads) {
+            const int r = i / d, kk = i - r * d;
+            const bool ok = s0 + r < N;
+            const size_t o = ((size_t)bh * N + s0 + r) * d + kk;
+            Qs[i] = ok ? __uint_as_float((uint32_t)Q[o] << 16) : 0.0f;
+            Ks[i] = ok ? __uint_as_float((uint32_t)K[o] << 16) : 0.0f;
+        }
+        for (int i = threadIdx.x; i < kDpSub * m; i += kThreads) {
+            const int r = i / m, c = i - r * m;
+            const bool ok = s0 + r < N;
+            const size_t o = ((size_t)bh * N + s0 + r) * mp + c;
+            dQs[i] = ok ? dQt[o] : 0.0f;
+            dKs[i] = ok ? dKt[o] : 0.0f;
+        }
+        __syncthreads();
+        for (int r = 0; r < kDpSub; ++r) {
+            const float q = Qs[r * d + k], kv = Ks[r * d + k];
+#pragma unroll
+            for (int i = 0; i < kDpMaxC; ++i)
+                if (i < nc) {
+                    const int c = c0 + tpk * i;
+                    acc[i] += q * dQs[r * m + c] + kv * dKs[r * m + c];
+                }
+        }
+    }
+    float* dst = part + ((size_t)bh * nch + ch) * d * m + (size_t)k * m;
+#pragma unroll
+    for (int i = 0; i < kDpMaxC; ++i)
+        if (i < nc) dst[c0 + tpk * i] = acc[i];
+}
+
+// dP[h, k, c] = sum over b (ascending) and chunks (ascending) of the partials.
+__global__ __launch_bounds__(kThreads) void dp_reduce_kernel(const float* __restrict__ part,
+                                                             float* __restrict__ dP, int B,
+                                                             int H, int nout, int nch) {
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i >= H * nout) return;
+    const int h = i / nout, e = i - h * nout;
+    float acc = 0.0f;
+    for (int b = 0; b < B; ++b)
+        for (int ch = 0; ch < nch; ++ch) acc += part[(((size_t)(b * H + h)) * nch + ch) * nout + e];
+    dP[i] = acc;
+}
+
+template <int MP, int DV, bool CAUSAL>
+hipError_t launch_main(const BwdArgs& a, hipStream_t s) {
+    const int nqb = (a.N + 127) / 128;
+    bwd_q_kernel<MP, DV, CAUSAL><<<dim3(a.BH * nqb), kThreads, 0, s>>>(
+        a.Qs, a.Kt, a.Ktt, a.V, a.O, a.dO, a.lse, a.dQt, a.D, a.N, a.Np, nqb, a.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    bwd_kv_kernel<MP, DV, CAUSAL><<<dim3(a.BH * nqb), kThreads, 0, s>>>(
+        a.Qs, a.Qst, a.Kt, a.V, a.dO, a.dOt, a.lse, a.D, a.dV, a.g_f32, a.dKt, a.N, a.Np, nqb);
+    return hipGetLastError();
+}
+
+template <int MP, int DV>
+hipError_t launch_c(const BwdArgs& a, hipStream_t s) {
+    return a.causal ? launch_main<MP, DV, true>(a, s) : launch_main<MP, DV, false>(a, s);
+}
+
+template <int MP>
+hipError_t launch_dv(const BwdArgs& a, hipStream_t s) {
+    switch (a.dv) {
+        case 64: return launch_c<MP, 64>(a, s);
+        case 128: return launch_c<MP, 128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+    if ((long long)a.BH * ((a.N + 127) / 128) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipError_t e;
+    switch (a.mp) {
+        case 16: e = launch_dv<16>(a, stream); break;
+        case 32: e = launch_dv<32>(a, stream); break;
+        case 64: e = launch_dv<64>(a, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    // back through the projection
+    const int nrb = (a.N + kBackRows - 1) / kBackRows;
+    const size_t sm_back = sizeof(float) * ((size_t)a.m * a.d + (size_t)kBackRows * a.m);
+    proj_back_kernel<<<dim3(a.BH * nrb, 2), kThreads, sm_back, stream>>>(
+        a.dQt, a.dKt, a.P, a.dQ, a.dK, a.g_f32, a.N, a.H, a.d, a.m, a.mp, nrb);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nch = (a.N + kDpRows - 1) / kDpRows;
+    const size_t sm_dp = sizeof(float) * (2 * (size_t)kDpSub * a.d + 2 * (size_t)kDpSub * a.m);
+    dp_partial_kernel<<<dim3(a.BH * nch), kThreads, sm_dp, stream>>>(
+        a.Q, a.K, a.dQt, a.dKt, a.dPpart, a.N, a.d, a.m, a.mp, nch);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nout = a.d * a.m;
+    dp_reduce_kernel<<<dim3((a.H * nout + kThreads - 1) / kThreads), kThreads, 0, stream>>>(
+        a.dPpart, a.dP, a.BH / a.H, a.H, nout, nch);
+    return hipGetLastError();
+}
+
+}  // namespace spa

@@ -26,12 +26,15 @@ __host__ __device__ inline int vt_padded_keys(int N) { return (N + kVtTileKeys -
 // P is [H, d, m]; columns m <= c < out_cols are written as zeros. Output rows are out_stride
 // elements apart. If kmax is not null, kmax[bh * proj_blocks(N) + b] receives the largest
 // row norm (fp32, before rounding) of Y1 over tokens b*256 .. b*256+255 of head bh. If Vt is
-// not null, the same launch writes V^T of V ([BH, N, dv] bf16) in the layout above.
+// not null, the same launch writes V^T of V ([BH, N, dv] bf16) in the layout above. If Yt0
+// (Yt1) is not null, Y0 (Y1) is also written transposed, [BH, out_cols, vt_padded_keys(N)],
+// tokens in the same permuted order as V^T and zero past N.
 hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, void* Y0,
                                void* Y1, int nz, int BH, int H, int N, int d, int m,
                                int out_stride, int out_cols, float out_scale0,
                                float out_scale1, bool out_f16, float* kmax, const void* V,
-                               void* Vt, int dv, hipStream_t stream);
+                               void* Vt, int dv, hipStream_t stream, void* Yt0 = nullptr,
+                               void* Yt1 = nullptr);
 
 // Attention over projected inputs. Qt and Kt are fp16 [BH, N, mp] with zero columns past m
 // (score MFMA in fp16); Qt is pre-scaled by scale*log2(e) so the scores come out in base-2
@@ -41,6 +44,39 @@ hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, vo
 hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* Vt, const float* kmax,
                             void* O, float* lse, int BH, int N, int mp, int dv, bool causal,
                             bool out_f32, hipStream_t stream);
+
+// Backward of the bf16 path. The preparation launch (launch_project_bf16 with the queries
+// scaled by scale*log2(e), fp16 outputs, the transposed copies Qst and Ktt, and dO
+// transposed into dOt) runs first; this runs the rest: the query-major kernel (dQt and
+// D = rowsum(dO * O)), the key-major kernel (dV and dKt), dQ = dQt P^T and dK = dKt P^T, and
+// the projection gradient dP (fp32 partials per 256-row chunk in dPpart, then a fixed-order
+// sum). mp is 16, 32 or 64.
+struct BwdArgs {
+    const uint16_t* Q;    // bf16 [BH, N, d]
+    const uint16_t* K;    // bf16 [BH, N, d]
+    const uint16_t* P;    // bf16 [H, d, m]
+    const uint16_t* Qs;   // fp16 [BH, N, mp], queries projected and scaled by scale*log2(e)
+    const uint16_t* Kt;   // fp16 [BH, N, mp]
+    const uint16_t* Qst;  // fp16 [BH, mp, Np], Qs transposed, tokens permuted as in V^T
+    const uint16_t* Ktt;  // fp16 [BH, mp, Np]
+    const uint16_t* V;    // bf16 [BH, N, dv]
+    const uint16_t* O;    // bf16 [BH, N, dv] (the forward's output)
+    const uint16_t* dO;   // bf16 [BH, N, dv]
+    const uint16_t* dOt;  // bf16 [BH, dv, Np], dO transposed, tokens permuted
+    const float* lse;     // [BH, N], natural log (the forward's)
+    float* D;             // [BH, N]
+    float* dQt;           // [BH, N, mp]
+    float* dKt;           // [BH, N, mp]
+    float* dPpart;        // [BH, ceil(N / 256), d, m]
+    float* dP;            // [H, d, m]
+    void* dQ;             // [BH, N, d], fp32 (g_f32) or bf16
+    void* dK;
+    void* dV;             // [BH, N, dv]
+    int g_f32;
+    int BH, H, N, Np, d, m, mp, dv, causal;
+    float scale;
+};
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
 // fp32 projection: Y[bh, n, c] = out_scale * sum_k X[bh, n, k] P[h, k, c], fp32 FMAs.
 hipError_t launch_project_f32(const float* X, const float* P, float* Y, int BH, int H, int N,

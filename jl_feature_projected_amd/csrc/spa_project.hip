@@ -27,6 +27,9 @@
 //
 // Launch order: the roles of one (head, 256-token block) are adjacent, so the queries', keys'
 // and values' traffic of a block run side by side.
+//
+// For the backward pass the same launch can also write the projections transposed, with
+// the tokens of every 16-group in the V^T order (Yt0, Yt1), and transpose dO in place of V.
 #include "spa_device.h"
 #include "spa_internal.h"
 
@@ -47,6 +50,8 @@ struct PrepArgs {
     uint16_t* Y1;
     const uint16_t* V;  // V transpose role: input [BH, N, dv] ...
     uint16_t* Vt;       // ... and output [BH, dv, Np]; null: no such role
+    uint16_t* Yt0;      // optional transposed projections [BH, out_cols, Np], tokens
+    uint16_t* Yt1;      // permuted within 16-groups as in Vt
     float* kmax;
     int N, BH, H, m, out_stride, out_cols, nz, nroles, Np;
     float scale0, scale1;
@@ -139,6 +144,7 @@ __global__ __launch_bounds__(kProjThreads) void prep_bf16_kernel(PrepArgs a) {
     const int z = role;  // 0: X0 (queries), 1: X1 (keys)
     const bf16_t* X = z ? a.X1 : a.X0;
     uint16_t* Y = z ? a.Y1 : a.Y0;
+    uint16_t* Yt = z ? a.Yt1 : a.Yt0;
     const float out_scale = z ? a.scale1 : a.scale0;
     const int h = bh % a.H;
     const int m = a.m;
@@ -209,6 +215,17 @@ __global__ __launch_bounds__(kProjThreads) void prep_bf16_kernel(PrepArgs a) {
             if (want_norm) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) norm2 += acc[i] * acc[i];
+            }
+            if (Yt && tok < a.Np) {
+                // X~^T in the V^T token order: lane = token, rows = 16 of this block's columns.
+                const int pos = (tok & ~15) | vt_key(tok & 15);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int c = mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                    if (c < a.out_cols)
+                        Yt[((size_t)bh * a.out_cols + c) * a.Np + pos] =
+                            (uint16_t)(pack_out<F16>(acc[i] * out_scale, 0.0f) & 0xffffu);
+                }
             }
             if (!valid) continue;
 #pragma unroll
@@ -288,8 +305,10 @@ hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, vo
                                void* Y1, int nz, int BH, int H, int N, int d, int m,
                                int out_stride, int out_cols, float out_scale0,
                                float out_scale1, bool out_f16, float* kmax, const void* V,
-                               void* Vt, int dv, hipStream_t stream) {
+                               void* Vt, int dv, hipStream_t stream, void* Yt0, void* Yt1) {
     PrepArgs a;
+    a.Yt0 = static_cast<uint16_t*>(Yt0);
+    a.Yt1 = static_cast<uint16_t*>(Yt1);
     a.X0 = static_cast<const bf16_t*>(X0);
     a.X1 = static_cast<const bf16_t*>(X1);
     a.P = static_cast<const bf16_t*>(P);

@@ -193,3 +193,10 @@ def gaussian_projection(d: int, m: int, seed: int, heads: int = 1) -> np.ndarray
     """P[heads, d, m] with iid N(0, 1/m) entries from its own PCG64 stream (float64)."""
     rng = np.random.default_rng(seed)
     return rng.standard_normal((heads, d, m)) / math.sqrt(m)
+
+
+def draw_grad_output(w: Workload, seed: int) -> torch.Tensor:
+    """A seeded stand-in for dL/dO: iid N(0, 1) entries [B, H, N, dv] from its own PCG64
+    stream, stored like the other inputs (float64 -> float32 -> bf16 RNE)."""
+    rng = np.random.default_rng(seed)
+    return to_storage(rng.standard_normal((w.B, w.H, w.N, w.dv)), w.dtype)

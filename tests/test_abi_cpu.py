@@ -125,3 +125,48 @@ def test_binding_fails_loudly_without_device_tensors():
         spa.spa_attn_fwd(x, x, x, p, 0.125, True)
     with pytest.raises(ValueError):
         spa.spa_project(x, p)
+
+
+def _bwd(L, **kw):
+    a = dict(Q=A, K=A + 0x100000, V=A + 0x200000, P=A + 0x300000, O=A + 0x400000,
+             dO=A + 0x500000, lse=A + 0x600000, scale=0.125, causal=1, B=1, H=2, N=256,
+             d=128, m=32, dv=128, dtype=spa.SPA_BF16, dQ=E, dK=E + 0x100000, dV=E + 0x200000,
+             dP=E + 0x300000, g_dtype=spa.SPA_F32, ws=F, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.spa_attn_bwd(a["Q"], a["K"], a["V"], a["P"], a["O"], a["dO"], a["lse"], a["scale"],
+                          a["causal"], a["B"], a["H"], a["N"], a["d"], a["m"], a["dv"],
+                          a["dtype"], a["dQ"], a["dK"], a["dV"], a["dP"], a["g_dtype"], a["ws"],
+                          a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dO=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(lse=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(N=0), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(causal=3), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("nan")), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(g_dtype=4), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(dQ=E + 8), spa.SPA_ERR_INVALID_ARGUMENT),              # misaligned
+    (dict(dK=E + 0x10), spa.SPA_ERR_INVALID_ARGUMENT),           # overlaps dQ
+    (dict(dV=A + 0x40), spa.SPA_ERR_INVALID_ARGUMENT),           # overlaps Q
+    (dict(ws_bytes=100), spa.SPA_ERR_WORKSPACE),
+    (dict(dtype=spa.SPA_F32), spa.SPA_ERR_UNSUPPORTED),
+    (dict(m=65), spa.SPA_ERR_UNSUPPORTED),
+    (dict(d=96), spa.SPA_ERR_UNSUPPORTED),
+    (dict(dv=32), spa.SPA_ERR_UNSUPPORTED),
+])
+def test_attn_bwd_rejects_on_host(L, kw, code):
+    assert _bwd(L, **kw) == code
+    assert len(L.spa_last_error()) > 0
+
+
+def test_bwd_workspace_bytes(L):
+    a256 = lambda x: ((x + 255) // 256) * 256
+    BH, N, d, m, dv = 2, 100, 64, 8, 64
+    mp, np_ = 16, 128
+    rows = BH * N
+    sizes = [rows * mp * 2, rows * mp * 2, BH * mp * np_ * 2, BH * mp * np_ * 2, BH * dv * np_ * 2,
+             rows * 4, rows * mp * 4, rows * mp * 4, BH * 1 * d * m * 4]
+    assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, m, dv, spa.SPA_BF16) == sum(a256(s) for s in sizes)
+    assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, 65, dv, spa.SPA_BF16) == 0
+    assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, m, dv, spa.SPA_F32) == 0
