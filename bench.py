@@ -95,6 +95,38 @@ def cpu_baseline(w: inputs.Workload, x: inputs.Inputs, budget_s: float = 12.0) -
                       f"{t1:.2f} s, float64)"}
 
 
+def time_backward(w, x, Q, K, V, P, steps, warmup, dev) -> dict:
+    """spa_attn_bwd on the forward's own output and lse, dO a seeded N(0, 1) draw; steps
+    calls timed between events on the launch stream after warmup calls."""
+    O, lse = spa.spa_attn_fwd(Q, K, V, P, w.scale, w.causal, out_dtype=torch.bfloat16,
+                              return_lse=True)
+    dO = inputs.draw_grad_output(w, seed=w.seed + 1).to(dev)
+    ws = torch.empty(spa.spa_attn_bwd_workspace_bytes(w.B, w.H, w.N, w.d, w.m, w.dv,
+                                                      torch.bfloat16),
+                     dtype=torch.uint8, device=dev)
+
+    def bstep():
+        spa.spa_attn_bwd(Q, K, V, P, O, dO, lse, w.scale, w.causal, workspace=ws)
+
+    for _ in range(warmup):
+        bstep()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        bstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    bw = accounting.bwd_work(w.B, w.H, w.N, w.d, w.m, w.dv, w.causal)
+    tf = bw.total_flops / (ms * 1e-3) / 1e12
+    return {"ms_per_call": round(ms, 5), "value": round(tf, 3), "unit": "TFLOP/s",
+            "pct_of_bf16_peak": round(100.0 * tf / accounting.PEAK_BF16_DENSE_TFLOPS, 2),
+            "flops_per_call": bw.total_flops, "executed_n2_flops_per_call": bw.executed_n2_flops,
+            "grad_dtype": "f32"}
+
+
 def calibrate_copy(dev) -> None:
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -115,6 +147,9 @@ def main() -> int:
     ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time spa_attn_bwd (bf16 workloads) and report it in a "
+                         "'backward' object")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -212,6 +247,8 @@ def main() -> int:
             "algorithmic_bytes": bytes_["attn"],
         },
     }
+    if args.backward and w.dtype == "bf16":
+        res["backward"] = time_backward(w, x, Q, K, V, P, args.steps, args.warmup, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(res), flush=True)

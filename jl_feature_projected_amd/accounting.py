@@ -1,4 +1,5 @@
-"""Algorithmic work and traffic of the projected-attention forward (host-side arithmetic).
+"""Algorithmic work and traffic of the projected-attention forward and backward (host-side
+arithmetic).
 
 Work per head, following the cost model of the Sparse Projection Attention page (Sec. 4.1.1,
 dense projection, s = 1) and the time-complexity list of the Projection-Decomposition
@@ -44,6 +45,30 @@ def work(B: int, H: int, N: int, d: int, m: int, dv: int, causal: bool) -> Work:
                 score_flops=heads * c * 2.0 * N * N * m,
                 pv_flops=heads * c * 2.0 * N * N * dv,
                 exps=heads * c * float(N) * N)
+
+
+@dataclass(frozen=True)
+class BwdWork:
+    """Backward work: the five N^2 contractions of the chain rule (scores recomputed, dA,
+    dV, dQt, dKt) and the projection-side products (Qt, Kt recomputed, dQ, dK, dP)."""
+
+    n2_flops: float          # c N^2 (6m + 4dv) per head
+    projection_flops: float  # 12 N d m per head
+    executed_n2_flops: float  # what the kernels run: scores and dA are formed twice
+
+    @property
+    def total_flops(self) -> float:
+        return self.n2_flops + self.projection_flops
+
+
+def bwd_work(B: int, H: int, N: int, d: int, m: int, dv: int, causal: bool) -> BwdWork:
+    c = 0.5 if causal else 1.0
+    heads = B * H
+    return BwdWork(
+        n2_flops=heads * c * N * N * (6.0 * m + 4.0 * dv),
+        projection_flops=heads * 12.0 * N * d * m,
+        executed_n2_flops=heads * c * N * N * (8.0 * m + 6.0 * dv),
+    )
 
 
 def path_bytes(B: int, H: int, N: int, d: int, m: int, dv: int, elem: int = 2,

@@ -60,11 +60,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     constexpr int KS = MP / 16;                // score k-steps
     constexpr int MB = (MP + 31) / 32;         // 32-row blocks of dQt^T
     constexpr int CS = DV / 16;                // dA k-steps
-    constexpr int K_B = kTile * MP * 2;        // Kt tile bytes
-    constexpr int KT_B = MB * 32 * kTile * 2;  // Kt^T tile bytes (rows past MP zero)
-    constexpr int V_B = kTile * DV * 2;        // V tile bytes
+    // LDS tiles, rows padded by 16 bytes so that 16-byte reads of one chunk column across
+    // consecutive rows hit distinct banks (32 x 4-byte and 64 x 4-byte bank models alike).
+    constexpr int KP = MP * 2 + 16;            // Kt tile row pitch (bytes)
+    constexpr int TP = kTile * 2 + 16;         // transposed tile row pitch: 32 tokens
+    constexpr int VP = DV * 2 + 16;            // V tile row pitch
+    constexpr int K_B = kTile * KP;
+    constexpr int KT_B = MB * 32 * TP;         // rows past MP zero
+    constexpr int V_B = kTile * VP;
     constexpr int BUF = K_B + KT_B + V_B;
-    constexpr int NCH = BUF / 16;              // 16-byte chunks per tile
+    constexpr int NK = kTile * MP / 8, NKT = MB * 32 * 4, NV = kTile * DV / 8;  // 16-byte chunks
+    constexpr int NCH = NK + NKT + NV;
     constexpr int CPT = (NCH + kThreads - 1) / kThreads;
     __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
@@ -109,23 +115,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     const int kend = CAUSAL ? min(N, q0 + 128) : N;
     const int ntiles = (kend + kTile - 1) / kTile;
 
-    // Tile staging: chunk c of the tile -> (region, row, 16-byte column).
+    // Tile staging: chunk c of the tile -> (region, row, 16-byte column); a thread holds its
+    // chunks in registers between the global load and the LDS store.
     u32x4 stage[CPT];
+    auto chunk_dst = [&](int c) -> int {  // byte offset of chunk c inside a buffer
+        if (c < NK) return (c / (MP / 8)) * KP + (c % (MP / 8)) * 16;
+        if (c < NK + NKT) return K_B + ((c - NK) / 4) * TP + ((c - NK) % 4) * 16;
+        return K_B + KT_B + ((c - NK - NKT) / (DV / 8)) * VP + ((c - NK - NKT) % (DV / 8)) * 16;
+    };
     auto load_tile = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + i * kThreads;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (c < K_B / 16) {
+            if (c < NK) {
                 const int r = c / (MP / 8), cc = c % (MP / 8);
                 if (k0 + r < N) v = *reinterpret_cast<const u32x4*>(Kh + (size_t)(k0 + r) * MP + cc * 8);
-            } else if (c < (K_B + KT_B) / 16) {
-                const int c2 = c - K_B / 16;
-                const int r = c2 / 4, cc = c2 % 4;  // feature row, 16-byte column of 32 keys
+            } else if (c < NK + NKT) {
+                const int r = (c - NK) / 4, cc = (c - NK) % 4;  // feature row, 16-byte column
                 if (r < MP) v = *reinterpret_cast<const u32x4*>(Kth + (size_t)r * Np + k0 + cc * 8);
             } else if (c < NCH) {
-                const int c2 = c - (K_B + KT_B) / 16;
-                const int r = c2 / (DV / 8), cc = c2 % (DV / 8);
+                const int r = (c - NK - NKT) / (DV / 8), cc = (c - NK - NKT) % (DV / 8);
                 if (k0 + r < N) v = *reinterpret_cast<const u32x4*>(Vh + (size_t)(k0 + r) * DV + cc * 8);
             }
             stage[i] = v;
@@ -135,7 +145,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + i * kThreads;
-            if (c < NCH) *reinterpret_cast<u32x4*>(lds + buf * BUF + c * 16) = stage[i];
+            if (c < NCH) *reinterpret_cast<u32x4*>(lds + buf * BUF + chunk_dst(c)) = stage[i];
         }
     };
 
@@ -143,13 +153,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
 #pragma unroll
     for (int b = 0; b < MB; ++b) acc[b] = f32x16_fill(0.0f);
 
+    // One barrier per step: step t stores tile t+1 (loaded during step t-1) into the buffer
+    // step t-1 read, requests tile t+2, then computes tile t.
     load_tile(0);
     store_tile(0);
+    if (ntiles > 1) load_tile(kTile);
     __syncthreads();
 #pragma unroll 1
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * kTile;
-        if (t + 1 < ntiles) load_tile(k0 + kTile);
+        if (t + 1 < ntiles) store_tile((t + 1) & 1);
+        if (t + 2 < ntiles) load_tile(k0 + 2 * kTile);
         const char* Ks = lds + (t & 1) * BUF;
         const char* Kts = Ks + K_B;
         const char* Vs = Kts + KT_B;
@@ -160,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const f16x8 a = __builtin_bit_cast(
-                    f16x8, *reinterpret_cast<const u32x4*>(Ks + col * MP * 2 + (ks * 16 + half * 8) * 2));
+                    f16x8, *reinterpret_cast<const u32x4*>(Ks + col * KP + (ks * 16 + half * 8) * 2));
                 s = mfma32x32x16(a, qf[ks], s);
             }
             // dA^T (32 keys x 32 queries) = V . dO^T
@@ -168,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
 #pragma unroll
             for (int cs = 0; cs < CS; ++cs) {
                 const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(Vs + col * DV * 2 + (cs * 16 + half * 8) * 2));
+                    bf16x8, *reinterpret_cast<const u32x4*>(Vs + col * VP + (cs * 16 + half * 8) * 2));
                 da = mfma32x32x16(a, dof[cs], da);
             }
             // dS = A (dA - D), masked entries zero
@@ -187,14 +201,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     const f16x8 a = __builtin_bit_cast(
-                        f16x8, *reinterpret_cast<const u32x4*>(Kts + (mb * 32 + col) * kTile * 2 + (tt * 16 + half * 8) * 2));
+                        f16x8, *reinterpret_cast<const u32x4*>(Kts + (mb * 32 + col) * TP + (tt * 16 + half * 8) * 2));
                     acc[mb] = mfma32x32x16(a, b, acc[mb]);
                 }
             }
         }
-        __syncthreads();  // everyone is done with the other buffer ...
-        if (t + 1 < ntiles) store_tile((t + 1) & 1);
-        __syncthreads();  // ... and the next tile is in it
+        __syncthreads();
     }
 
     if (qvalid) {
@@ -230,13 +242,18 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
     constexpr int MB = (MP + 31) / 32;
     constexpr int CS = DV / 16;
     constexpr int DB = DV / 32;
-    constexpr int Q_B = kTile * MP * 2;        // Qs tile
-    constexpr int QT_B = MB * 32 * kTile * 2;  // Qs^T tile (rows past MP zero)
-    constexpr int DO_B = kTile * DV * 2;       // dO tile
-    constexpr int DOT_B = DV * kTile * 2;      // dO^T tile
-    constexpr int L_B = kTile * 4;             // lse2 of the tile
+    // LDS tiles, rows padded by 16 bytes (see the query-major kernel).
+    constexpr int QP = MP * 2 + 16;            // Qs tile row pitch
+    constexpr int TP = kTile * 2 + 16;         // transposed tiles' row pitch: 32 tokens
+    constexpr int OP = DV * 2 + 16;            // dO tile row pitch
+    constexpr int Q_B = kTile * QP;
+    constexpr int QT_B = MB * 32 * TP;         // rows past MP zero
+    constexpr int DO_B = kTile * OP;
+    constexpr int DOT_B = DV * TP;
+    constexpr int L_B = kTile * 4;             // lse2 (then D) of the tile
     constexpr int BUF = Q_B + QT_B + DO_B + DOT_B + 2 * L_B;
-    constexpr int NCH = (Q_B + QT_B + DO_B + DOT_B) / 16;
+    constexpr int NQ = kTile * MP / 8, NQT = MB * 32 * 4, NO = kTile * DV / 8, NOT = DV * 4;
+    constexpr int NCH = NQ + NQT + NO + NOT;
     constexpr int CPT = (NCH + kThreads - 1) / kThreads;
     __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
@@ -276,25 +293,29 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 
     u32x4 stage[CPT];
     float lstage = 0.0f, dstage = 0.0f;
+    auto chunk_dst = [&](int c) -> int {
+        if (c < NQ) return (c / (MP / 8)) * QP + (c % (MP / 8)) * 16;
+        if (c < NQ + NQT) return Q_B + ((c - NQ) / 4) * TP + ((c - NQ) % 4) * 16;
+        if (c < NQ + NQT + NO)
+            return Q_B + QT_B + ((c - NQ - NQT) / (DV / 8)) * OP + ((c - NQ - NQT) % (DV / 8)) * 16;
+        return Q_B + QT_B + DO_B + ((c - NQ - NQT - NO) / 4) * TP + ((c - NQ - NQT - NO) % 4) * 16;
+    };
     auto load_tile = [&](int q0) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + i * kThreads;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (c < Q_B / 16) {
+            if (c < NQ) {
                 const int r = c / (MP / 8), cc = c % (MP / 8);
                 if (q0 + r < N) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)(q0 + r) * MP + cc * 8);
-            } else if (c < (Q_B + QT_B) / 16) {
-                const int c2 = c - Q_B / 16;
-                const int r = c2 / 4, cc = c2 % 4;
+            } else if (c < NQ + NQT) {
+                const int r = (c - NQ) / 4, cc = (c - NQ) % 4;
                 if (r < MP) v = *reinterpret_cast<const u32x4*>(Qth + (size_t)r * Np + q0 + cc * 8);
-            } else if (c < (Q_B + QT_B + DO_B) / 16) {
-                const int c2 = c - (Q_B + QT_B) / 16;
-                const int r = c2 / (DV / 8), cc = c2 % (DV / 8);
+            } else if (c < NQ + NQT + NO) {
+                const int r = (c - NQ - NQT) / (DV / 8), cc = (c - NQ - NQT) % (DV / 8);
                 if (q0 + r < N) v = *reinterpret_cast<const u32x4*>(dOh + (size_t)(q0 + r) * DV + cc * 8);
             } else if (c < NCH) {
-                const int c2 = c - (Q_B + QT_B + DO_B) / 16;
-                const int r = c2 / 4, cc = c2 % 4;
+                const int r = (c - NQ - NQT - NO) / 4, cc = (c - NQ - NQT - NO) % 4;
                 v = *reinterpret_cast<const u32x4*>(dOth + (size_t)r * Np + q0 + cc * 8);
             }
             stage[i] = v;
@@ -310,7 +331,7 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + i * kThreads;
-            if (c < NCH) *reinterpret_cast<u32x4*>(base + c * 16) = stage[i];
+            if (c < NCH) *reinterpret_cast<u32x4*>(base + chunk_dst(c)) = stage[i];
         }
         if (tid < kTile) {
             reinterpret_cast<float*>(base + BUF - 2 * L_B)[tid] = lstage;
@@ -324,13 +345,16 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 #pragma unroll
     for (int b = 0; b < MB; ++b) dka[b] = f32x16_fill(0.0f);
 
+    // One barrier per step, as in the query-major kernel.
     load_tile(qstart);
     store_tile(0);
+    if (ntiles > 1) load_tile(qstart + kTile);
     __syncthreads();
 #pragma unroll 1
     for (int t = 0; t < ntiles; ++t) {
         const int q0 = qstart + t * kTile;
-        if (t + 1 < ntiles) load_tile(q0 + kTile);
+        if (t + 1 < ntiles) store_tile((t + 1) & 1);
+        if (t + 2 < ntiles) load_tile(q0 + 2 * kTile);
         const char* Qts = lds + (t & 1) * BUF;  // Qs tile (rows = queries)
         const char* QTs = Qts + Q_B;            // Qs^T tile (rows = features)
         const char* dOs = QTs + QT_B;           // dO tile (rows = queries)
@@ -344,7 +368,7 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const f16x8 a = __builtin_bit_cast(
-                    f16x8, *reinterpret_cast<const u32x4*>(Qts + col * MP * 2 + (ks * 16 + half * 8) * 2));
+                    f16x8, *reinterpret_cast<const u32x4*>(Qts + col * QP + (ks * 16 + half * 8) * 2));
                 s = mfma32x32x16(a, kf[ks], s);
             }
             // dA^T (32 queries x 32 keys) = dO . V^T
@@ -352,7 +376,7 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 #pragma unroll
             for (int cs = 0; cs < CS; ++cs) {
                 const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(dOs + col * DV * 2 + (cs * 16 + half * 8) * 2));
+                    bf16x8, *reinterpret_cast<const u32x4*>(dOs + col * OP + (cs * 16 + half * 8) * 2));
                 da = mfma32x32x16(a, vf[cs], da);
             }
             // weights and dS; the row (query) of slot i is 8*(i/4) + 4*half + i%4
@@ -381,19 +405,17 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const bf16x8 a = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const u32x4*>(dOTs + (db * 32 + col) * kTile * 2 + (tt * 16 + half * 8) * 2));
+                        bf16x8, *reinterpret_cast<const u32x4*>(dOTs + (db * 32 + col) * TP + (tt * 16 + half * 8) * 2));
                     dva[db] = mfma32x32x16(a, bw, dva[db]);
                 }
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     const f16x8 a = __builtin_bit_cast(
-                        f16x8, *reinterpret_cast<const u32x4*>(QTs + (mb * 32 + col) * kTile * 2 + (tt * 16 + half * 8) * 2));
+                        f16x8, *reinterpret_cast<const u32x4*>(QTs + (mb * 32 + col) * TP + (tt * 16 + half * 8) * 2));
                     dka[mb] = mfma32x32x16(a, bs, dka[mb]);
                 }
             }
         }
-        __syncthreads();
-        if (t + 1 < ntiles) store_tile((t + 1) & 1);
         __syncthreads();
     }
 
@@ -433,71 +455,100 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 
 // ---------------------------------------------------------------------------------------
 // dX[bh, n, k] = sum_{c < m} dXt[bh, n, c] P[h, k, c] for X in {Q, K} (z = blockIdx.y).
-// One workgroup per (head, 64 rows); P^T and the rows' dXt staged in LDS, fp32 FMAs.
+// One workgroup per (head, 64 rows); P^T and the rows' dXt staged in LDS; each thread
+// computes a block of RT rows x 4 features with fp32 FMAs (RT = D / 16).
 constexpr int kBackRows = 64;
+template <int D>
 __global__ __launch_bounds__(kThreads) void proj_back_kernel(
     const float* __restrict__ dQt, const float* __restrict__ dKt, const uint16_t* __restrict__ P,
-    void* __restrict__ dQ, void* __restrict__ dK, int out_f32, int N, int H, int d, int m,
-    int mp, int nrb) {
+    void* __restrict__ dQ, void* __restrict__ dK, int out_f32, int N, int H, int m, int mp,
+    int nrb) {
+    constexpr int KG = D / 4;                 // feature groups of 4
+    constexpr int RT = kBackRows * KG / kThreads;  // rows per thread
     extern __shared__ __attribute__((aligned(16))) float sm[];
-    float* Ps = sm;                     // [m][d]: P^T of the head
-    float* Xs = sm + m * d;             // [kBackRows][m]
+    float* Ps = sm;                           // [m][D]: P^T of the head
+    float* Xs = sm + m * D;                   // [kBackRows][m]
     const int bh = blockIdx.x / nrb;
     const int n0 = (blockIdx.x - bh * nrb) * kBackRows;
     const int z = blockIdx.y;
     const float* src = (z ? dKt : dQt) + (size_t)bh * N * mp;
     const int h = bh % H;
-    for (int i = threadIdx.x; i < d * m; i += kThreads) {
+    for (int i = threadIdx.x; i < D * m; i += kThreads) {
         const int k = i / m, c = i - k * m;
-        Ps[c * d + k] = __uint_as_float((uint32_t)P[(size_t)h * d * m + i] << 16);
+        Ps[c * D + k] = __uint_as_float((uint32_t)P[(size_t)h * D * m + i] << 16);
     }
     for (int i = threadIdx.x; i < kBackRows * m; i += kThreads) {
         const int r = i / m, c = i - r * m;
         Xs[i] = n0 + r < N ? src[(size_t)(n0 + r) * mp + c] : 0.0f;
     }
     __syncthreads();
+    const int kg = threadIdx.x % KG, rg = threadIdx.x / KG;
+    float acc[RT][4];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[r][j] = 0.0f;
+    for (int c = 0; c < m; ++c) {
+        const float4 p4 = *reinterpret_cast<const float4*>(Ps + c * D + 4 * kg);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const float x = Xs[(rg * RT + r) * m + c];
+            acc[r][0] += x * p4.x;
+            acc[r][1] += x * p4.y;
+            acc[r][2] += x * p4.z;
+            acc[r][3] += x * p4.w;
+        }
+    }
     void* dst = z ? dK : dQ;
-    for (int i = threadIdx.x; i < kBackRows * d; i += kThreads) {
-        const int r = i / d, k = i - r * d;
-        if (n0 + r >= N) continue;
-        float acc = 0.0f;
-        for (int c = 0; c < m; ++c) acc += Xs[r * m + c] * Ps[c * d + k];
-        const size_t o = ((size_t)bh * N + n0 + r) * d + k;
-        if (out_f32) static_cast<float*>(dst)[o] = acc;
-        else static_cast<uint16_t*>(dst)[o] = (uint16_t)(pack_bf16x2(acc, 0.0f) & 0xffffu);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int n = n0 + rg * RT + r;
+        if (n >= N) continue;
+        const size_t o = ((size_t)bh * N + n) * D + 4 * kg;
+        if (out_f32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(dst) + o) =
+                make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+        } else {
+            u32x2 w;
+            w.x = pack_bf16x2(acc[r][0], acc[r][1]);
+            w.y = pack_bf16x2(acc[r][2], acc[r][3]);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dst) + o) = w;
+        }
     }
 }
 
 // partial[bh, chunk, k, c] = sum over the chunk's rows n of Q[n,k] dQt[n,c] + K[n,k] dKt[n,c].
-// Thread t owns feature k = t / TPK and columns c = t % TPK + TPK * i (TPK = 256 / d threads
-// per feature, at most 32 columns each for d >= 64, m <= 64).
+// Thread t owns features 4*(t % (D/4)) .. +3 and columns c = t / (D/4) + CG * i (CG = 1024 /
+// D column groups, TC = D / 16 columns each, m <= 64), accumulated over rows in fp32.
 constexpr int kDpRows = 256;
 constexpr int kDpSub = 32;
-constexpr int kDpMaxC = 32;
+template <int D>
 __global__ __launch_bounds__(kThreads) void dp_partial_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const float* __restrict__ dQt,
-    const float* __restrict__ dKt, float* __restrict__ part, int N, int d, int m, int mp,
-    int nch) {
+    const float* __restrict__ dKt, float* __restrict__ part, int N, int m, int mp, int nch) {
+    constexpr int KG = D / 4;
+    constexpr int CG = kThreads / KG;
+    constexpr int TC = 64 / CG;
     extern __shared__ __attribute__((aligned(16))) float sm[];
-    float* Qs = sm;                      // [kDpSub][d]
-    float* Ks = Qs + kDpSub * d;         // [kDpSub][d]
-    float* dQs = Ks + kDpSub * d;        // [kDpSub][m]
+    float* Qs = sm;                      // [kDpSub][D]
+    float* Ks = Qs + kDpSub * D;         // [kDpSub][D]
+    float* dQs = Ks + kDpSub * D;        // [kDpSub][m]
     float* dKs = dQs + kDpSub * m;       // [kDpSub][m]
     const int bh = blockIdx.x / nch;
     const int ch = blockIdx.x - bh * nch;
     const int n0 = ch * kDpRows;
-    const int tpk = kThreads / d;
-    const int k = threadIdx.x / tpk, c0 = threadIdx.x % tpk;
-    const int nc = (m - c0 + tpk - 1) / tpk;  // columns of this thread
-    float acc[kDpMaxC];
+    const int kg = threadIdx.x % KG, cg = threadIdx.x / KG;
+    float acc[4][TC];
 #pragma unroll
-    for (int i = 0; i < kDpMaxC; ++i) acc[i] = 0.0f;
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < TC; ++i) acc[j][i] = 0.0f;
     for (int s0 = n0; s0 < n0 + kDpRows && s0 < N; s0 += kDpSub) {
         __syncthreads();
-        for (int i = threadIdx.x; i < kDpSub * d; i += kThreads) {
-            const int r = i / d, kk = i - r * d;
+        for (int i = threadIdx.x; i < kDpSub * D; i += kThreads) {
+            const int r = i / D, kk = i - r * D;
             const bool ok = s0 + r < N;
-            const size_t o = ((size_t)bh * N + s0 + r) * d + kk;
+            const size_t o = ((size_t)bh * N + s0 + r) * D + kk;
             Qs[i] = ok ? __uint_as_float((uint32_t)Q[o] << 16) : 0.0f;
             Ks[i] = ok ? __uint_as_float((uint32_t)K[o] << 16) : 0.0f;
         }
@@ -510,19 +561,29 @@ __global__ __launch_bounds__(kThreads) void dp_partial_kernel(
         }
         __syncthreads();
         for (int r = 0; r < kDpSub; ++r) {
-            const float q = Qs[r * d + k], kv = Ks[r * d + k];
+            const float4 q = *reinterpret_cast<const float4*>(Qs + r * D + 4 * kg);
+            const float4 kv = *reinterpret_cast<const float4*>(Ks + r * D + 4 * kg);
 #pragma unroll
-            for (int i = 0; i < kDpMaxC; ++i)
-                if (i < nc) {
-                    const int c = c0 + tpk * i;
-                    acc[i] += q * dQs[r * m + c] + kv * dKs[r * m + c];
+            for (int i = 0; i < TC; ++i) {
+                const int c = cg + CG * i;
+                if (c < m) {
+                    const float a = dQs[r * m + c], b = dKs[r * m + c];
+                    acc[0][i] += q.x * a + kv.x * b;
+                    acc[1][i] += q.y * a + kv.y * b;
+                    acc[2][i] += q.z * a + kv.z * b;
+                    acc[3][i] += q.w * a + kv.w * b;
                 }
+            }
         }
     }
-    float* dst = part + ((size_t)bh * nch + ch) * d * m + (size_t)k * m;
+    float* dst = part + ((size_t)bh * nch + ch) * D * m;
 #pragma unroll
-    for (int i = 0; i < kDpMaxC; ++i)
-        if (i < nc) dst[c0 + tpk * i] = acc[i];
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < TC; ++i) {
+            const int c = cg + CG * i;
+            if (c < m) dst[(size_t)(4 * kg + j) * m + c] = acc[j][i];
+        }
 }
 
 // dP[h, k, c] = sum over b (ascending) and chunks (ascending) of the partials.
@@ -579,14 +640,22 @@ hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
     // back through the projection
     const int nrb = (a.N + kBackRows - 1) / kBackRows;
     const size_t sm_back = sizeof(float) * ((size_t)a.m * a.d + (size_t)kBackRows * a.m);
-    proj_back_kernel<<<dim3(a.BH * nrb, 2), kThreads, sm_back, stream>>>(
-        a.dQt, a.dKt, a.P, a.dQ, a.dK, a.g_f32, a.N, a.H, a.d, a.m, a.mp, nrb);
+    if (a.d == 128)
+        proj_back_kernel<128><<<dim3(a.BH * nrb, 2), kThreads, sm_back, stream>>>(
+            a.dQt, a.dKt, a.P, a.dQ, a.dK, a.g_f32, a.N, a.H, a.m, a.mp, nrb);
+    else
+        proj_back_kernel<64><<<dim3(a.BH * nrb, 2), kThreads, sm_back, stream>>>(
+            a.dQt, a.dKt, a.P, a.dQ, a.dK, a.g_f32, a.N, a.H, a.m, a.mp, nrb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nch = (a.N + kDpRows - 1) / kDpRows;
     const size_t sm_dp = sizeof(float) * (2 * (size_t)kDpSub * a.d + 2 * (size_t)kDpSub * a.m);
-    dp_partial_kernel<<<dim3(a.BH * nch), kThreads, sm_dp, stream>>>(
-        a.Q, a.K, a.dQt, a.dKt, a.dPpart, a.N, a.d, a.m, a.mp, nch);
+    if (a.d == 128)
+        dp_partial_kernel<128><<<dim3(a.BH * nch), kThreads, sm_dp, stream>>>(
+            a.Q, a.K, a.dQt, a.dKt, a.dPpart, a.N, a.m, a.mp, nch);
+    else
+        dp_partial_kernel<64><<<dim3(a.BH * nch), kThreads, sm_dp, stream>>>(
+            a.Q, a.K, a.dQt, a.dKt, a.dPpart, a.N, a.m, a.mp, nch);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nout = a.d * a.m;
