@@ -33,6 +33,13 @@ constexpr int kThreads = 256;
 constexpr int kTile = 32;  // keys (query-major kernel) or queries (key-major kernel) per step
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// Linear workgroup index with the grid split into 8 contiguous ranges, range x on XCD x
+// (the dispatcher hands workgroups to the XCDs round-robin); identity unless 8 divides it.
+__device__ __forceinline__ int xcd_local_index() {
+    const int total = gridDim.x;
+    return (total & 7) == 0 ? (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+}
+
 // fp32 score-layout values (slots 8*half + j of k-step tt) -> packed pairs
 template <bool F16>
 __device__ __forceinline__ u32x4 pack_kstep(const f32x16& x, int tt) {
@@ -74,8 +81,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     constexpr int CPT = (NCH + kThreads - 1) / kThreads;
     __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
-    const int bh = blockIdx.x / nqb;
-    const int qb = blockIdx.x - bh * nqb;
+    // Workgroup -> (head, query block) as in the forward: XCD x (workgroups are handed to
+    // the 8 XCDs round-robin) gets a contiguous range of pairs, so a head's key tiles stay
+    // in one XCD's L2; causal blocks run heaviest (last) first.
+    const int li = xcd_local_index();
+    const int bh = li / nqb;
+    const int qbi = li - bh * nqb;
+    const int qb = CAUSAL ? nqb - 1 - qbi : qbi;
     const int q0 = qb * 128;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
     const int myq = q0 + wave * 32 + col;
@@ -257,8 +269,11 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
     constexpr int CPT = (NCH + kThreads - 1) / kThreads;
     __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
-    const int bh = blockIdx.x / nkb;
-    const int kb = blockIdx.x - bh * nkb;
+    // Workgroup -> (head, key block), XCD-contiguous as in the query-major kernel; causal
+    // key blocks are heaviest first already (block 0 meets every query).
+    const int li = xcd_local_index();
+    const int bh = li / nkb;
+    const int kb = li - bh * nkb;
     const int k0 = kb * 128;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
     const int k0w = k0 + wave * 32;
