@@ -40,6 +40,22 @@ __device__ __forceinline__ int xcd_local_index() {
     return (total & 7) == 0 ? (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3) : blockIdx.x;
 }
 
+// Tag for compile-time variants of a loop step.
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
+
+// Byte offset that is out of range for every tile resource below (loads read zero).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Raw buffer resource over max(bytes, 0) bytes from `base`: loads at offsets past the end
+// return zero instead of touching memory. base and bytes must be wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, max(bytes, 0),
+                                             0x00020000);
+}
+
 // fp32 score-layout values (slots 8*half + j of k-step tt) -> packed pairs
 template <bool F16>
 __device__ __forceinline__ u32x4 pack_kstep(const f32x16& x, int tt) {
@@ -68,7 +84,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     constexpr int MB = (MP + 31) / 32;         // 32-row blocks of dQt^T
     constexpr int CS = DV / 16;                // dA k-steps
     // LDS tiles, rows padded by 16 bytes so that 16-byte reads of one chunk column across
-    // consecutive rows hit distinct banks (32 x 4-byte and 64 x 4-byte bank models alike).
+    // consecutive rows hit distinct banks.
     constexpr int KP = MP * 2 + 16;            // Kt tile row pitch (bytes)
     constexpr int TP = kTile * 2 + 16;         // transposed tile row pitch: 32 tokens
     constexpr int VP = DV * 2 + 16;            // V tile row pitch
@@ -76,9 +92,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     constexpr int KT_B = MB * 32 * TP;         // rows past MP zero
     constexpr int V_B = kTile * VP;
     constexpr int BUF = K_B + KT_B + V_B;
-    constexpr int NK = kTile * MP / 8, NKT = MB * 32 * 4, NV = kTile * DV / 8;  // 16-byte chunks
+    // 16-byte chunks per region (each a multiple of 64, so one wave's slot is in one region)
+    constexpr int NK = kTile * MP / 8, NKT = MB * 32 * 4, NV = kTile * DV / 8;
     constexpr int NCH = NK + NKT + NV;
     constexpr int CPT = (NCH + kThreads - 1) / kThreads;
+    static_assert(NK % 64 == 0 && NKT % 64 == 0 && NV % 64 == 0, "region sizes");
     __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
     // Workgroup -> (head, query block) as in the forward: XCD x (workgroups are handed to
@@ -94,9 +112,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     const bool qvalid = myq < N;
 
     const uint16_t* Qh = Qs + (size_t)bh * N * MP;
-    const uint16_t* Kh = Kt + (size_t)bh * N * MP;
-    const uint16_t* Kth = Ktt + (size_t)bh * MP * Np;
-    const uint16_t* Vh = V + (size_t)bh * N * DV;
+    const char* Kh = reinterpret_cast<const char*>(Kt + (size_t)bh * N * MP);
+    const char* Kth = reinterpret_cast<const char*>(Ktt + (size_t)bh * MP * Np);
+    const char* Vh = reinterpret_cast<const char*>(V + (size_t)bh * N * DV);
 
     // This lane's query (B operand of the scores) and dO row (B operand of dA).
     f16x8 qf[KS];
@@ -126,39 +144,53 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
 
     const int kend = CAUSAL ? min(N, q0 + 128) : N;
     const int ntiles = (kend + kTile - 1) / kTile;
+    // Tiles before `nfree` need no mask: causal, all their keys precede the block's first
+    // query; otherwise every tile but a ragged last one.
+    const int nfree = CAUSAL ? min(ntiles, q0 / kTile) : N / kTile;
 
-    // Tile staging: chunk c of the tile -> (region, row, 16-byte column); a thread holds its
-    // chunks in registers between the global load and the LDS store.
+    // Staging slots: chunk i * kThreads + tid -> region (wave-uniform), byte offset from the
+    // tile's first token, LDS byte offset. Per region, the head's array, its bytes per token
+    // step and its size in bytes. Region 0: Kt rows; 1: Kt^T feature rows (rows past MP read
+    // zero); 2: V rows; none (slots past the tile).
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const char* sbase[CPT];
+    int sstep[CPT], stot[CPT];
+    bool slive[CPT];
+    uint32_t voff[CPT], loff[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int cw = i * kThreads + wu * 64;
+        const int c = cw + lane;
+        slive[i] = cw < NCH;
+        if (cw < NK) {
+            const int row = c / (MP / 8), cc = c % (MP / 8);
+            sbase[i] = Kh, sstep[i] = MP * 2, stot[i] = N * MP * 2;
+            voff[i] = row * MP * 2 + cc * 16, loff[i] = row * KP + cc * 16;
+        } else if (cw < NK + NKT) {
+            const int row = (c - NK) / 4, cc = (c - NK) % 4;
+            sbase[i] = Kth, sstep[i] = 2, stot[i] = MP * Np * 2;
+            voff[i] = row < MP ? row * Np * 2 + cc * 16 : kOutOfRange;
+            loff[i] = K_B + row * TP + cc * 16;
+        } else {
+            const int row = (c - NK - NKT) / (DV / 8), cc = (c - NK - NKT) % (DV / 8);
+            sbase[i] = Vh, sstep[i] = DV * 2, stot[i] = slive[i] ? N * DV * 2 : 0;
+            voff[i] = row * DV * 2 + cc * 16, loff[i] = K_B + KT_B + row * VP + cc * 16;
+        }
+    }
     u32x4 stage[CPT];
-    auto chunk_dst = [&](int c) -> int {  // byte offset of chunk c inside a buffer
-        if (c < NK) return (c / (MP / 8)) * KP + (c % (MP / 8)) * 16;
-        if (c < NK + NKT) return K_B + ((c - NK) / 4) * TP + ((c - NK) % 4) * 16;
-        return K_B + KT_B + ((c - NK - NKT) / (DV / 8)) * VP + ((c - NK - NKT) % (DV / 8)) * 16;
-    };
     auto load_tile = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * kThreads;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (c < NK) {
-                const int r = c / (MP / 8), cc = c % (MP / 8);
-                if (k0 + r < N) v = *reinterpret_cast<const u32x4*>(Kh + (size_t)(k0 + r) * MP + cc * 8);
-            } else if (c < NK + NKT) {
-                const int r = (c - NK) / 4, cc = (c - NK) % 4;  // feature row, 16-byte column
-                if (r < MP) v = *reinterpret_cast<const u32x4*>(Kth + (size_t)r * Np + k0 + cc * 8);
-            } else if (c < NCH) {
-                const int r = (c - NK - NKT) / (DV / 8), cc = (c - NK - NKT) % (DV / 8);
-                if (k0 + r < N) v = *reinterpret_cast<const u32x4*>(Vh + (size_t)(k0 + r) * DV + cc * 8);
-            }
-            stage[i] = v;
+            const int skip = k0 * sstep[i];
+            stage[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                tile_rsrc(sbase[i] + skip, stot[i] - skip), voff[i], 0, 0);
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * kThreads;
-            if (c < NCH) *reinterpret_cast<u32x4*>(lds + buf * BUF + chunk_dst(c)) = stage[i];
-        }
+        for (int i = 0; i < CPT; ++i)
+            if ((i + 1) * kThreads <= NCH || slive[i])
+                *reinterpret_cast<u32x4*>(lds + buf * BUF + loff[i]) = stage[i];
     };
 
     f32x16 acc[MB];
@@ -166,21 +198,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     for (int b = 0; b < MB; ++b) acc[b] = f32x16_fill(0.0f);
 
     // One barrier per step: step t stores tile t+1 (loaded during step t-1) into the buffer
-    // step t-1 read, requests tile t+2, then computes tile t.
-    load_tile(0);
-    store_tile(0);
-    if (ntiles > 1) load_tile(kTile);
-    __syncthreads();
-#pragma unroll 1
-    for (int t = 0; t < ntiles; ++t) {
+    // step t-1 read, requests tile t+2 (past the end: all reads out of range, zero), then
+    // computes tile t.
+    auto step = [&](int t, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int k0 = t * kTile;
-        if (t + 1 < ntiles) store_tile((t + 1) & 1);
-        if (t + 2 < ntiles) load_tile(k0 + 2 * kTile);
+        store_tile((t + 1) & 1);
+        load_tile(k0 + 2 * kTile);
         const char* Ks = lds + (t & 1) * BUF;
         const char* Kts = Ks + K_B;
         const char* Vs = Kts + KT_B;
         // causal: a wave whose queries all precede the tile has nothing to do in it
-        if (!CAUSAL || k0 <= q0 + wave * 32 + 31) {
+        if (!(MASK && CAUSAL) || k0 <= q0 + wave * 32 + 31) {
             // scores^T (32 keys x 32 queries), base-2 units
             f32x16 s = f32x16_fill(0.0f);
 #pragma unroll
@@ -197,13 +226,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
                     bf16x8, *reinterpret_cast<const u32x4*>(Vs + col * VP + (cs * 16 + half * 8) * 2));
                 da = mfma32x32x16(a, dof[cs], da);
             }
-            // dS = A (dA - D), masked entries zero
+            // dS = A (dA - D), masked entries (later keys, keys past N) zero
             f32x16 ds;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
                 float w = __builtin_amdgcn_exp2f(s[i] - lse2);
-                if (CAUSAL && key > myq) w = 0.0f;
+                if (MASK) {
+                    const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
+                    if ((CAUSAL && key > myq) || key >= N) w = 0.0f;
+                }
                 ds[i] = w * (da[i] - Dq);
             }
             // dQt^T (MP x 32 queries) += Kt^T . dS^T
@@ -219,7 +250,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
             }
         }
         __syncthreads();
-    }
+    };
+
+    load_tile(0);
+    store_tile(0);
+    load_tile(kTile);
+    __syncthreads();
+    int t = 0;
+#pragma unroll 1
+    for (; t < nfree; ++t) step(t, Flag<false>{});
+#pragma unroll 1
+    for (; t < ntiles; ++t) step(t, Flag<true>{});
 
     if (qvalid) {
         float* dst = dQt + ((size_t)bh * N + myq) * MP;
@@ -267,6 +308,7 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
     constexpr int NQ = kTile * MP / 8, NQT = MB * 32 * 4, NO = kTile * DV / 8, NOT = DV * 4;
     constexpr int NCH = NQ + NQT + NO + NOT;
     constexpr int CPT = (NCH + kThreads - 1) / kThreads;
+    static_assert(NQ % 64 == 0 && NQT % 64 == 0 && NO % 64 == 0 && NOT % 64 == 0, "region sizes");
     __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
 
     // Workgroup -> (head, key block), XCD-contiguous as in the query-major kernel; causal
@@ -280,10 +322,10 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
     const int myk = k0w + col;
     const bool kvalid = myk < N;
 
-    const uint16_t* Qh = Qs + (size_t)bh * N * MP;
-    const uint16_t* Qth = Qst + (size_t)bh * MP * Np;
-    const uint16_t* dOh = dO + (size_t)bh * N * DV;
-    const uint16_t* dOth = dOt + (size_t)bh * DV * Np;
+    const char* Qh = reinterpret_cast<const char*>(Qs + (size_t)bh * N * MP);
+    const char* Qth = reinterpret_cast<const char*>(Qst + (size_t)bh * MP * Np);
+    const char* dOh = reinterpret_cast<const char*>(dO + (size_t)bh * N * DV);
+    const char* dOth = reinterpret_cast<const char*>(dOt + (size_t)bh * DV * Np);
     const float* lseh = lse + (size_t)bh * N;
     const float* Dh = Din + (size_t)bh * N;
 
@@ -305,53 +347,67 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 
     const int qstart = CAUSAL ? k0 : 0;
     const int ntiles = (N - qstart + kTile - 1) / kTile;
+    // causal: the first four tiles meet the block's keys and need the mask
+    const int nmask = CAUSAL ? min(ntiles, 128 / kTile) : 0;
 
+    // Staging slots as in the query-major kernel. Region 0: Qs rows; 1: Qs^T feature rows
+    // (rows past MP read zero); 2: dO rows; 3: dO^T rows; none (slots past the tile).
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const char* sbase[CPT];
+    int sstep[CPT], stot[CPT];
+    bool slive[CPT];
+    uint32_t voff[CPT], loff[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int cw = i * kThreads + wu * 64;
+        const int c = cw + lane;
+        slive[i] = cw < NCH;
+        if (cw < NQ) {
+            const int row = c / (MP / 8), cc = c % (MP / 8);
+            sbase[i] = Qh, sstep[i] = MP * 2, stot[i] = N * MP * 2;
+            voff[i] = row * MP * 2 + cc * 16, loff[i] = row * QP + cc * 16;
+        } else if (cw < NQ + NQT) {
+            const int row = (c - NQ) / 4, cc = (c - NQ) % 4;
+            sbase[i] = Qth, sstep[i] = 2, stot[i] = MP * Np * 2;
+            voff[i] = row < MP ? row * Np * 2 + cc * 16 : kOutOfRange;
+            loff[i] = Q_B + row * TP + cc * 16;
+        } else if (cw < NQ + NQT + NO) {
+            const int row = (c - NQ - NQT) / (DV / 8), cc = (c - NQ - NQT) % (DV / 8);
+            sbase[i] = dOh, sstep[i] = DV * 2, stot[i] = N * DV * 2;
+            voff[i] = row * DV * 2 + cc * 16, loff[i] = Q_B + QT_B + row * OP + cc * 16;
+        } else {
+            const int row = (c - NQ - NQT - NO) / 4, cc = (c - NQ - NQT - NO) % 4;
+            sbase[i] = dOth, sstep[i] = 2, stot[i] = slive[i] ? DV * Np * 2 : 0;
+            voff[i] = row * Np * 2 + cc * 16;
+            loff[i] = Q_B + QT_B + DO_B + row * TP + cc * 16;
+        }
+    }
     u32x4 stage[CPT];
-    float lstage = 0.0f, dstage = 0.0f;
-    auto chunk_dst = [&](int c) -> int {
-        if (c < NQ) return (c / (MP / 8)) * QP + (c % (MP / 8)) * 16;
-        if (c < NQ + NQT) return Q_B + ((c - NQ) / 4) * TP + ((c - NQ) % 4) * 16;
-        if (c < NQ + NQT + NO)
-            return Q_B + QT_B + ((c - NQ - NQT) / (DV / 8)) * OP + ((c - NQ - NQT) % (DV / 8)) * 16;
-        return Q_B + QT_B + DO_B + ((c - NQ - NQT - NO) / 4) * TP + ((c - NQ - NQT - NO) % 4) * 16;
-    };
+    float lstage, dstage;
+    const int ql = tid & (kTile - 1);  // every thread stages the lse and D of query ql
     auto load_tile = [&](int q0) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * kThreads;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (c < NQ) {
-                const int r = c / (MP / 8), cc = c % (MP / 8);
-                if (q0 + r < N) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)(q0 + r) * MP + cc * 8);
-            } else if (c < NQ + NQT) {
-                const int r = (c - NQ) / 4, cc = (c - NQ) % 4;
-                if (r < MP) v = *reinterpret_cast<const u32x4*>(Qth + (size_t)r * Np + q0 + cc * 8);
-            } else if (c < NQ + NQT + NO) {
-                const int r = (c - NQ - NQT) / (DV / 8), cc = (c - NQ - NQT) % (DV / 8);
-                if (q0 + r < N) v = *reinterpret_cast<const u32x4*>(dOh + (size_t)(q0 + r) * DV + cc * 8);
-            } else if (c < NCH) {
-                const int r = (c - NQ - NQT - NO) / 4, cc = (c - NQ - NQT - NO) % 4;
-                v = *reinterpret_cast<const u32x4*>(dOth + (size_t)r * Np + q0 + cc * 8);
-            }
-            stage[i] = v;
+            const int skip = q0 * sstep[i];
+            stage[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                tile_rsrc(sbase[i] + skip, stot[i] - skip), voff[i], 0, 0);
         }
-        if (tid < kTile) {
-            const int q = q0 + tid;
-            lstage = q < N ? lseh[q] * kLog2e : INFINITY;  // rows past N get zero weight
-            dstage = q < N ? Dh[q] : 0.0f;
-        }
+        const int nl = (N - q0) * 4;
+        const float l = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(lseh + q0, nl), ql * 4, 0, 0));
+        dstage = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(Dh + q0, nl), ql * 4, 0, 0));
+        lstage = q0 + ql < N ? l * kLog2e : INFINITY;  // rows past N get zero weight
     };
     auto store_tile = [&](int buf) {
         char* base = lds + buf * BUF;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * kThreads;
-            if (c < NCH) *reinterpret_cast<u32x4*>(base + chunk_dst(c)) = stage[i];
-        }
-        if (tid < kTile) {
-            reinterpret_cast<float*>(base + BUF - 2 * L_B)[tid] = lstage;
-            reinterpret_cast<float*>(base + BUF - L_B)[tid] = dstage;
-        }
+        for (int i = 0; i < CPT; ++i)
+            if ((i + 1) * kThreads <= NCH || slive[i])
+                *reinterpret_cast<u32x4*>(base + loff[i]) = stage[i];
+        // identical values from the threads that share ql
+        reinterpret_cast<float*>(base + BUF - 2 * L_B)[ql] = lstage;
+        reinterpret_cast<float*>(base + BUF - L_B)[ql] = dstage;
     };
 
     f32x16 dva[DB], dka[MB];
@@ -361,15 +417,11 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
     for (int b = 0; b < MB; ++b) dka[b] = f32x16_fill(0.0f);
 
     // One barrier per step, as in the query-major kernel.
-    load_tile(qstart);
-    store_tile(0);
-    if (ntiles > 1) load_tile(qstart + kTile);
-    __syncthreads();
-#pragma unroll 1
-    for (int t = 0; t < ntiles; ++t) {
+    auto step = [&](int t, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int q0 = qstart + t * kTile;
-        if (t + 1 < ntiles) store_tile((t + 1) & 1);
-        if (t + 2 < ntiles) load_tile(q0 + 2 * kTile);
+        store_tile((t + 1) & 1);
+        load_tile(q0 + 2 * kTile);
         const char* Qts = lds + (t & 1) * BUF;  // Qs tile (rows = queries)
         const char* QTs = Qts + Q_B;            // Qs^T tile (rows = features)
         const char* dOs = QTs + QT_B;           // dO tile (rows = queries)
@@ -377,7 +429,7 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
         const float* L2s = reinterpret_cast<const float*>(Qts + BUF - 2 * L_B);
         const float* Ds = reinterpret_cast<const float*>(Qts + BUF - L_B);
         // causal: nothing to do if every query of the tile precedes every key of the wave
-        if (!CAUSAL || q0 + kTile - 1 >= k0w) {
+        if (!MASK || q0 + kTile - 1 >= k0w) {
             // scores^T (32 queries x 32 keys)
             f32x16 s = f32x16_fill(0.0f);
 #pragma unroll
@@ -405,9 +457,8 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 4 * g + r;
-                    const int q = q0 + 8 * g + 4 * half + r;
                     float a = __builtin_amdgcn_exp2f(s[i] - lv[r]);
-                    if (CAUSAL && myk > q) a = 0.0f;
+                    if (MASK && myk > q0 + 8 * g + 4 * half + r) a = 0.0f;
                     w[i] = a;
                     ds[i] = a * (da[i] - dv4[r]);
                 }
@@ -432,7 +483,17 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
             }
         }
         __syncthreads();
-    }
+    };
+
+    load_tile(qstart);
+    store_tile(0);
+    load_tile(qstart + kTile);
+    __syncthreads();
+    int t = 0;
+#pragma unroll 1
+    for (; t < nmask; ++t) step(t, Flag<true>{});
+#pragma unroll 1
+    for (; t < ntiles; ++t) step(t, Flag<false>{});
 
     if (kvalid) {
         const size_t row = (size_t)bh * N + myk;
