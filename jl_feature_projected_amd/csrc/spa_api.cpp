@@ -78,10 +78,11 @@ WorkspaceLayout workspace_layout(int BH, int N, int m, int dv, spa_dtype_t dtype
 
 // Backward workspace (bf16 path), each region 256-byte aligned: projected queries (scaled)
 // and keys, fp16 [BH, N, mp] each; the same transposed, fp16 [BH, mp, Np] each; dO
-// transposed, bf16 [BH, dv, Np]; D, fp32 [BH, N]; the projected gradients, fp32 [BH, N, mp]
+// transposed, bf16 [BH, dv, Np]; per query -lse*log2(e) and -D (D = <dO, O>), fp32
+// [BH, Np/32, 2, 32]; the projected gradients, fp32 [BH, N, mp]
 // each; the projection gradient's partials, fp32 [BH, ceil(N / 256), d, m].
 struct BwdLayout {
-    size_t qs, kt, qst, ktt, dot, D, dqt, dkt, part, total;
+    size_t qs, kt, qst, ktt, dot, ld, dqt, dkt, part, total;
 };
 BwdLayout bwd_layout(int BH, int N, int d, int m, int dv) {
     const size_t mp = (size_t)spa::padded_m(m), np = (size_t)spa::vt_padded_keys(N);
@@ -98,7 +99,7 @@ BwdLayout bwd_layout(int BH, int N, int d, int m, int dv) {
     w.qst = take((size_t)BH * mp * np * 2);
     w.ktt = take((size_t)BH * mp * np * 2);
     w.dot = take((size_t)BH * dv * np * 2);
-    w.D = take(rows * 4);
+    w.ld = take((size_t)BH * np * 2 * 4);
     w.dqt = take(rows * mp * 4);
     w.dkt = take(rows * mp * 4);
     w.part = take((size_t)BH * ((N + 255) / 256) * d * m * 4);
@@ -425,7 +426,7 @@ spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const voi
         a.dO = static_cast<const uint16_t*>(dO);
         a.dOt = reinterpret_cast<const uint16_t*>(w + wl.dot);
         a.lse = lse;
-        a.D = reinterpret_cast<float*>(w + wl.D);
+        a.LD = reinterpret_cast<float*>(w + wl.ld);
         a.dQt = reinterpret_cast<float*>(w + wl.dqt);
         a.dKt = reinterpret_cast<float*>(w + wl.dkt);
         a.dPpart = reinterpret_cast<float*>(w + wl.part);

@@ -30,6 +30,8 @@ namespace spa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kBufs = 3;   // tile buffers of the MFMA kernels' loops
 constexpr int kTile = 32;  // keys (query-major kernel) or queries (key-major kernel) per step
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -69,35 +71,33 @@ __device__ __forceinline__ u32x4 pack_kstep(const f32x16& x, int tt) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Query-major kernel: dQt and D.
+// Query-major kernel: dQt, and per query -lse2 and -D for the key-major kernel.
 // Inputs: Qs [BH,N,MP] fp16 (scaled), Kt [BH,N,MP] fp16, Ktt [BH,MP,Np] fp16 (transposed,
 // permuted), V [BH,N,DV] bf16, O, dO [BH,N,DV] bf16, lse [BH,N] (natural log).
-// Outputs: dQt [BH,N,MP] fp32 (scaled by `scale`), D [BH,N] fp32.
+// Outputs: dQt [BH,N,MP] fp32 (scaled by `scale`); LD [BH, Np/32, 2, 32] fp32: per 32
+// queries, -lse*log2(e) then -D (-inf and 0 for queries past N).
 template <int MP, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     const uint16_t* __restrict__ Qs, const uint16_t* __restrict__ Kt,
     const uint16_t* __restrict__ Ktt, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-    const float* __restrict__ lse, float* __restrict__ dQt, float* __restrict__ Dout, int N,
+    const float* __restrict__ lse, float* __restrict__ dQt, float* __restrict__ LD, int N,
     int Np, int nqb, float scale) {
     constexpr int KS = MP / 16;                // score k-steps
     constexpr int MB = (MP + 31) / 32;         // 32-row blocks of dQt^T
     constexpr int CS = DV / 16;                // dA k-steps
-    // LDS tiles, rows padded by 16 bytes so that 16-byte reads of one chunk column across
-    // consecutive rows hit distinct banks.
-    constexpr int KP = MP * 2 + 16;            // Kt tile row pitch (bytes)
-    constexpr int TP = kTile * 2 + 16;         // transposed tile row pitch: 32 tokens
-    constexpr int VP = DV * 2 + 16;            // V tile row pitch
-    constexpr int K_B = kTile * KP;
-    constexpr int KT_B = MB * 32 * TP;         // rows past MP zero
-    constexpr int V_B = kTile * VP;
+    // Tile buffer: Kt rows (32 keys x MP fp16), Kt^T rows (MB*32 feature rows x 32 keys,
+    // rows past MP zero), V rows (32 keys x DV bf16). Rows unpadded, 16-byte chunks
+    // swizzled (kswz of the row's element count); every region a whole number of 1 KiB
+    // wave copies.
+    constexpr int K_B = kTile * MP * 2;
+    constexpr int KT_B = MB * 32 * kTile * 2;
+    constexpr int V_B = kTile * DV * 2;
     constexpr int BUF = K_B + KT_B + V_B;
-    // 16-byte chunks per region (each a multiple of 64, so one wave's slot is in one region)
-    constexpr int NK = kTile * MP / 8, NKT = MB * 32 * 4, NV = kTile * DV / 8;
-    constexpr int NCH = NK + NKT + NV;
-    constexpr int CPT = (NCH + kThreads - 1) / kThreads;
-    static_assert(NK % 64 == 0 && NKT % 64 == 0 && NV % 64 == 0, "region sizes");
-    __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+    constexpr int NCP = BUF / 1024;                    // wave copies per tile
+    constexpr int CPW = (NCP + kWaves - 1) / kWaves;   // ... per wave
+    static_assert(K_B % 1024 == 0 && KT_B % 1024 == 0 && V_B % 1024 == 0, "copy regions");
+    __shared__ __attribute__((aligned(16))) char lds[kBufs * BUF];
 
     // Workgroup -> (head, query block) as in the forward: XCD x (workgroups are handed to
     // the 8 XCDs round-robin) gets a contiguous range of pairs, so a head's key tiles stay
@@ -115,6 +115,55 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     const char* Kh = reinterpret_cast<const char*>(Kt + (size_t)bh * N * MP);
     const char* Kth = reinterpret_cast<const char*>(Ktt + (size_t)bh * MP * Np);
     const char* Vh = reinterpret_cast<const char*>(V + (size_t)bh * N * DV);
+
+    const int kend = CAUSAL ? min(N, q0 + 128) : N;
+    const int ntiles = (kend + kTile - 1) / kTile;
+    // Tiles before `nfree` need no mask: causal, all their keys precede the block's first
+    // query; otherwise every tile but a ragged last one.
+    const int nfree = CAUSAL ? min(ntiles, q0 / kTile) : N / kTile;
+
+    // ---- HBM -> LDS tile copies ------------------------------------------------------
+    // Wave copy j (j = wave, wave + 4, ...) fills buffer chunks 64j .. 64j+63; lane l writes
+    // chunk c = 64j + l, which holds global chunk (slot ^ swizzle(row)) of its region's row.
+    // Per copy: the head's array, its bytes per token of tile advance and its size (loads
+    // past it read zero), the lane's byte offset from the tile's first token. A wave past
+    // the last copy repeats it (same bytes to the same place).
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const char* cbase[CPW];
+    int cstep[CPW], ctot[CPW];
+    uint32_t coff[CPW], cdst[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int j = min(wu + kWaves * i, NCP - 1);
+        const int c = 64 * j + lane;
+        cdst[i] = 1024 * j;
+        if (64 * j < K_B / 16) {
+            const int row = c / (MP / 8), slot = c % (MP / 8);
+            cbase[i] = Kh, cstep[i] = MP * 2, ctot[i] = N * MP * 2;
+            coff[i] = row * MP * 2 + 16 * (slot ^ kswz<MP>(row));
+        } else if (64 * j < (K_B + KT_B) / 16) {
+            const int cc = c - K_B / 16, row = cc >> 2, slot = cc & 3;
+            cbase[i] = Kth, cstep[i] = 2, ctot[i] = MP * Np * 2;
+            coff[i] = row < MP ? row * Np * 2 + 16 * (slot ^ kswz<kTile>(row)) : kOutOfRange;
+        } else {
+            const int cc = c - (K_B + KT_B) / 16, row = cc / (DV / 8), slot = cc % (DV / 8);
+            cbase[i] = Vh, cstep[i] = DV * 2, ctot[i] = N * DV * 2;
+            coff[i] = row * DV * 2 + 16 * (slot ^ kswz<DV>(row));
+        }
+    }
+    const uint32_t lds0 = lds_address(lds);
+    auto copy_tile = [&](int k0, int buf) {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int skip = k0 * cstep[i];
+            copy16_to_lds(make_rsrc(cbase[i] + skip, (uint32_t)max(ctot[i] - skip, 0)),
+                          lds0 + buf * BUF + cdst[i], coff[i]);
+        }
+    };
+    // Tile 0's copies go out before the lane's own rows are loaded; the wait for both
+    // comes before tile 1's copies (a wait left to the compiler would land inside the tile
+    // loop, where it would also wait for the copies in flight).
+    copy_tile(0, 0);
 
     // This lane's query (B operand of the scores) and dO row (B operand of dA).
     f16x8 qf[KS];
@@ -141,101 +190,63 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
     }
     const float Dq = halves_sum(dpart);
     const float lse2 = qvalid ? lse[(size_t)bh * N + myq] * kLog2e : INFINITY;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    copy_tile(kTile, 1);
+    // The score accumulator starts at -lse2 and the dA accumulator at -D, so the MFMAs
+    // leave s - lse2 and dA - D.
+    const f32x16 sinit = f32x16_fill(-lse2);
+    const f32x16 dinit = f32x16_fill(-Dq);
 
-    const int kend = CAUSAL ? min(N, q0 + 128) : N;
-    const int ntiles = (kend + kTile - 1) / kTile;
-    // Tiles before `nfree` need no mask: causal, all their keys precede the block's first
-    // query; otherwise every tile but a ragged last one.
-    const int nfree = CAUSAL ? min(ntiles, q0 / kTile) : N / kTile;
-
-    // Staging slots: chunk i * kThreads + tid -> region (wave-uniform), byte offset from the
-    // tile's first token, LDS byte offset. Per region, the head's array, its bytes per token
-    // step and its size in bytes. Region 0: Kt rows; 1: Kt^T feature rows (rows past MP read
-    // zero); 2: V rows; none (slots past the tile).
-    const int wu = __builtin_amdgcn_readfirstlane(wave);
-    const char* sbase[CPT];
-    int sstep[CPT], stot[CPT];
-    bool slive[CPT];
-    uint32_t voff[CPT], loff[CPT];
+    // Per-lane LDS read offsets (fixed across tiles). Kt tile: row col, chunk 2ks + half;
+    // V tile: row col, chunk 2cs + half; Kt^T tile: row mb*32 + col (same swizzle for
+    // every mb), chunk 2tt + half.
+    uint32_t kread[KS], vread[CS], tread[2];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const int cw = i * kThreads + wu * 64;
-        const int c = cw + lane;
-        slive[i] = cw < NCH;
-        if (cw < NK) {
-            const int row = c / (MP / 8), cc = c % (MP / 8);
-            sbase[i] = Kh, sstep[i] = MP * 2, stot[i] = N * MP * 2;
-            voff[i] = row * MP * 2 + cc * 16, loff[i] = row * KP + cc * 16;
-        } else if (cw < NK + NKT) {
-            const int row = (c - NK) / 4, cc = (c - NK) % 4;
-            sbase[i] = Kth, sstep[i] = 2, stot[i] = MP * Np * 2;
-            voff[i] = row < MP ? row * Np * 2 + cc * 16 : kOutOfRange;
-            loff[i] = K_B + row * TP + cc * 16;
-        } else {
-            const int row = (c - NK - NKT) / (DV / 8), cc = (c - NK - NKT) % (DV / 8);
-            sbase[i] = Vh, sstep[i] = DV * 2, stot[i] = slive[i] ? N * DV * 2 : 0;
-            voff[i] = row * DV * 2 + cc * 16, loff[i] = K_B + KT_B + row * VP + cc * 16;
-        }
-    }
-    u32x4 stage[CPT];
-    auto load_tile = [&](int k0) {
+    for (int ks = 0; ks < KS; ++ks) kread[ks] = col * MP * 2 + 16 * ((2 * ks + half) ^ kswz<MP>(col));
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int skip = k0 * sstep[i];
-            stage[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                tile_rsrc(sbase[i] + skip, stot[i] - skip), voff[i], 0, 0);
-        }
-    };
-    auto store_tile = [&](int buf) {
+    for (int cs = 0; cs < CS; ++cs) vread[cs] = col * DV * 2 + 16 * ((2 * cs + half) ^ kswz<DV>(col));
 #pragma unroll
-        for (int i = 0; i < CPT; ++i)
-            if ((i + 1) * kThreads <= NCH || slive[i])
-                *reinterpret_cast<u32x4*>(lds + buf * BUF + loff[i]) = stage[i];
-    };
+    for (int tt = 0; tt < 2; ++tt) tread[tt] = col * kTile * 2 + 16 * ((2 * tt + half) ^ kswz<kTile>(col));
 
     f32x16 acc[MB];
 #pragma unroll
     for (int b = 0; b < MB; ++b) acc[b] = f32x16_fill(0.0f);
 
-    // One barrier per step: step t stores tile t+1 (loaded during step t-1) into the buffer
-    // step t-1 read, requests tile t+2 (past the end: all reads out of range, zero), then
-    // computes tile t.
-    auto step = [&](int t, auto mask_tag) {
+    // Three buffers, one barrier per step: step t requests tile t+2 into the buffer step t-1
+    // read, computes tile t, then waits for its own copies of tile t+1 before the barrier
+    // that hands tile t+1 to every wave. Copies past the last tile read real or zero bytes
+    // into a buffer no step reads.
+    auto step = [&](int t, int cur, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int k0 = t * kTile;
-        store_tile((t + 1) & 1);
-        load_tile(k0 + 2 * kTile);
-        const char* Ks = lds + (t & 1) * BUF;
+        copy_tile(k0 + 2 * kTile, cur == 0 ? kBufs - 1 : cur - 1);
+        const char* Ks = lds + cur * BUF;
         const char* Kts = Ks + K_B;
         const char* Vs = Kts + KT_B;
         // causal: a wave whose queries all precede the tile has nothing to do in it
         if (!(MASK && CAUSAL) || k0 <= q0 + wave * 32 + 31) {
-            // scores^T (32 keys x 32 queries), base-2 units
-            f32x16 s = f32x16_fill(0.0f);
+            // scores^T (32 keys x 32 queries), base-2 units, minus lse2
+            f32x16 s = sinit;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const f16x8 a = __builtin_bit_cast(
-                    f16x8, *reinterpret_cast<const u32x4*>(Ks + col * KP + (ks * 16 + half * 8) * 2));
-                s = mfma32x32x16(a, qf[ks], s);
-            }
-            // dA^T (32 keys x 32 queries) = V . dO^T
-            f32x16 da = f32x16_fill(0.0f);
+            for (int ks = 0; ks < KS; ++ks)
+                s = mfma32x32x16(__builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(Ks + kread[ks])),
+                                 qf[ks], s);
+            // dA^T (32 keys x 32 queries) = V . dO^T, minus D
+            f32x16 da = dinit;
 #pragma unroll
-            for (int cs = 0; cs < CS; ++cs) {
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(Vs + col * VP + (cs * 16 + half * 8) * 2));
-                da = mfma32x32x16(a, dof[cs], da);
-            }
+            for (int cs = 0; cs < CS; ++cs)
+                da = mfma32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Vs + vread[cs])),
+                                  dof[cs], da);
             // dS = A (dA - D), masked entries (later keys, keys past N) zero
             f32x16 ds;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float w = __builtin_amdgcn_exp2f(s[i] - lse2);
+                float w = __builtin_amdgcn_exp2f(s[i]);
                 if (MASK) {
                     const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
                     if ((CAUSAL && key > myq) || key >= N) w = 0.0f;
                 }
-                ds[i] = w * (da[i] - Dq);
+                ds[i] = w * da[i];
             }
             // dQt^T (MP x 32 queries) += Kt^T . dS^T
 #pragma unroll
@@ -244,23 +255,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     const f16x8 a = __builtin_bit_cast(
-                        f16x8, *reinterpret_cast<const u32x4*>(Kts + (mb * 32 + col) * TP + (tt * 16 + half * 8) * 2));
+                        f16x8, *reinterpret_cast<const u32x4*>(Kts + mb * 32 * kTile * 2 + tread[tt]));
                     acc[mb] = mfma32x32x16(a, b, acc[mb]);
                 }
             }
         }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW));
         __syncthreads();
     };
 
-    load_tile(0);
-    store_tile(0);
-    load_tile(kTile);
-    __syncthreads();
-    int t = 0;
+    __syncthreads();  // tile 0 from every wave
+    int t = 0, cur = 0;
 #pragma unroll 1
-    for (; t < nfree; ++t) step(t, Flag<false>{});
+    for (; t < nfree; ++t, cur = cur == kBufs - 1 ? 0 : cur + 1) step(t, cur, Flag<false>{});
 #pragma unroll 1
-    for (; t < ntiles; ++t) step(t, Flag<true>{});
+    for (; t < ntiles; ++t, cur = cur == kBufs - 1 ? 0 : cur + 1) step(t, cur, Flag<true>{});
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy may land after the workgroup ends
 
     if (qvalid) {
         float* dst = dQt + ((size_t)bh * N + myq) * MP;
@@ -274,7 +284,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
                         make_float4(acc[mb][4 * g] * scale, acc[mb][4 * g + 1] * scale,
                                     acc[mb][4 * g + 2] * scale, acc[mb][4 * g + 3] * scale);
             }
-        if (half == 0) Dout[(size_t)bh * N + myq] = Dq;
+    }
+    if (half == 0 && myq < Np) {
+        float* dst = LD + ((size_t)bh * Np + (myq & ~(kTile - 1))) * 2 + (myq & (kTile - 1));
+        dst[0] = -lse2;
+        dst[kTile] = -Dq;
     }
 }
 
@@ -282,34 +296,33 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
 // Key-major kernel: dV and dKt.
 // Inputs: Qs [BH,N,MP] fp16 (scaled), Qst [BH,MP,Np] fp16 (transposed, permuted), Kt
 // [BH,N,MP] fp16, V [BH,N,DV] bf16, dO [BH,N,DV] bf16, dOt [BH,DV,Np] bf16 (transposed,
-// permuted), lse [BH,N], D [BH,N].
+// permuted), LD (from the query-major kernel).
 // Outputs: dV [BH,N,DV] (fp32 or bf16), dKt [BH,N,MP] fp32 (scale applied).
 template <int MP, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd_kv_kernel(
     const uint16_t* __restrict__ Qs, const uint16_t* __restrict__ Qst,
     const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const uint16_t* __restrict__ dOt,
-    const float* __restrict__ lse, const float* __restrict__ Din, void* __restrict__ dV,
-    int dv_f32, float* __restrict__ dKt, int N, int Np, int nkb) {
+    const float* __restrict__ LD, void* __restrict__ dV, int dv_f32, float* __restrict__ dKt,
+    int N, int Np, int nkb) {
     constexpr int KS = MP / 16;
     constexpr int MB = (MP + 31) / 32;
     constexpr int CS = DV / 16;
     constexpr int DB = DV / 32;
-    // LDS tiles, rows padded by 16 bytes (see the query-major kernel).
-    constexpr int QP = MP * 2 + 16;            // Qs tile row pitch
-    constexpr int TP = kTile * 2 + 16;         // transposed tiles' row pitch: 32 tokens
-    constexpr int OP = DV * 2 + 16;            // dO tile row pitch
-    constexpr int Q_B = kTile * QP;
-    constexpr int QT_B = MB * 32 * TP;         // rows past MP zero
-    constexpr int DO_B = kTile * OP;
-    constexpr int DOT_B = DV * TP;
-    constexpr int L_B = kTile * 4;             // lse2 (then D) of the tile
-    constexpr int BUF = Q_B + QT_B + DO_B + DOT_B + 2 * L_B;
-    constexpr int NQ = kTile * MP / 8, NQT = MB * 32 * 4, NO = kTile * DV / 8, NOT = DV * 4;
-    constexpr int NCH = NQ + NQT + NO + NOT;
-    constexpr int CPT = (NCH + kThreads - 1) / kThreads;
-    static_assert(NQ % 64 == 0 && NQT % 64 == 0 && NO % 64 == 0 && NOT % 64 == 0, "region sizes");
-    __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+    // Tile buffer: Qs rows (32 queries x MP fp16), Qs^T rows (MB*32 feature rows x 32
+    // queries, rows past MP zero), dO rows (32 x DV bf16), dO^T rows (DV x 32 queries), all
+    // as in the query-major kernel; then -lse2 and -D of the 32 queries.
+    constexpr int Q_B = kTile * MP * 2;
+    constexpr int QT_B = MB * 32 * kTile * 2;
+    constexpr int DO_B = kTile * DV * 2;
+    constexpr int DOT_B = DV * kTile * 2;
+    constexpr int B16 = Q_B + QT_B + DO_B + DOT_B;     // bytes copied 16 per lane
+    constexpr int BUF = B16 + 2 * kTile * 4;
+    constexpr int NCP = B16 / 1024;
+    constexpr int CPW = (NCP + kWaves - 1) / kWaves;
+    static_assert(Q_B % 1024 == 0 && QT_B % 1024 == 0 && DO_B % 1024 == 0 && DOT_B % 1024 == 0,
+                  "copy regions");
+    __shared__ __attribute__((aligned(16))) char lds[kBufs * BUF];
 
     // Workgroup -> (head, key block), XCD-contiguous as in the query-major kernel; causal
     // key blocks are heaviest first already (block 0 meets every query).
@@ -326,8 +339,55 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
     const char* Qth = reinterpret_cast<const char*>(Qst + (size_t)bh * MP * Np);
     const char* dOh = reinterpret_cast<const char*>(dO + (size_t)bh * N * DV);
     const char* dOth = reinterpret_cast<const char*>(dOt + (size_t)bh * DV * Np);
-    const float* lseh = lse + (size_t)bh * N;
-    const float* Dh = Din + (size_t)bh * N;
+    const float* LDh = LD + (size_t)bh * Np * 2;
+
+    const int qstart = CAUSAL ? k0 : 0;
+    const int ntiles = (N - qstart + kTile - 1) / kTile;
+    // causal: the first four tiles meet the block's keys and need the mask
+    const int nmask = CAUSAL ? min(ntiles, 128 / kTile) : 0;
+
+    // ---- HBM -> LDS tile copies, as in the query-major kernel ---------------------------
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const char* cbase[CPW];
+    int cstep[CPW], ctot[CPW];
+    uint32_t coff[CPW], cdst[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int j = min(wu + kWaves * i, NCP - 1);
+        const int c = 64 * j + lane;
+        cdst[i] = 1024 * j;
+        if (64 * j < Q_B / 16) {
+            const int row = c / (MP / 8), slot = c % (MP / 8);
+            cbase[i] = Qh, cstep[i] = MP * 2, ctot[i] = N * MP * 2;
+            coff[i] = row * MP * 2 + 16 * (slot ^ kswz<MP>(row));
+        } else if (64 * j < (Q_B + QT_B) / 16) {
+            const int cc = c - Q_B / 16, row = cc >> 2, slot = cc & 3;
+            cbase[i] = Qth, cstep[i] = 2, ctot[i] = MP * Np * 2;
+            coff[i] = row < MP ? row * Np * 2 + 16 * (slot ^ kswz<kTile>(row)) : kOutOfRange;
+        } else if (64 * j < (Q_B + QT_B + DO_B) / 16) {
+            const int cc = c - (Q_B + QT_B) / 16, row = cc / (DV / 8), slot = cc % (DV / 8);
+            cbase[i] = dOh, cstep[i] = DV * 2, ctot[i] = N * DV * 2;
+            coff[i] = row * DV * 2 + 16 * (slot ^ kswz<DV>(row));
+        } else {
+            const int cc = c - (Q_B + QT_B + DO_B) / 16, row = cc >> 2, slot = cc & 3;
+            cbase[i] = dOth, cstep[i] = 2, ctot[i] = DV * Np * 2;
+            coff[i] = row * Np * 2 + 16 * (slot ^ kswz<kTile>(row));
+        }
+    }
+    const uint32_t lds0 = lds_address(lds);
+    // CPW 16-byte copies, then the tile's -lse2 and -D (one 4-byte copy, the same in every
+    // wave).
+    auto copy_tile = [&](int q0, int buf) {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int skip = q0 * cstep[i];
+            copy16_to_lds(make_rsrc(cbase[i] + skip, (uint32_t)max(ctot[i] - skip, 0)),
+                          lds0 + buf * BUF + cdst[i], coff[i]);
+        }
+        copy4_to_lds(make_rsrc(LDh + 2 * q0, (uint32_t)max(Np - q0, 0) * 8), lds0 + buf * BUF + B16,
+                     4 * lane);
+    };
+    copy_tile(qstart, 0);  // then the lane's rows, then one wait, as in the query-major kernel
 
     // This lane's key (B operand of the scores) and value row (B operand of dA).
     f16x8 kf[KS];
@@ -344,71 +404,18 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
         if (kvalid) v = *reinterpret_cast<const u32x4*>(V + ((size_t)bh * N + myk) * DV + cs * 16 + half * 8);
         vf[cs] = __builtin_bit_cast(bf16x8, v);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    copy_tile(qstart + kTile, 1);
 
-    const int qstart = CAUSAL ? k0 : 0;
-    const int ntiles = (N - qstart + kTile - 1) / kTile;
-    // causal: the first four tiles meet the block's keys and need the mask
-    const int nmask = CAUSAL ? min(ntiles, 128 / kTile) : 0;
-
-    // Staging slots as in the query-major kernel. Region 0: Qs rows; 1: Qs^T feature rows
-    // (rows past MP read zero); 2: dO rows; 3: dO^T rows; none (slots past the tile).
-    const int wu = __builtin_amdgcn_readfirstlane(wave);
-    const char* sbase[CPT];
-    int sstep[CPT], stot[CPT];
-    bool slive[CPT];
-    uint32_t voff[CPT], loff[CPT];
+    // Per-lane LDS read offsets: Qs tile row col, chunk 2ks + half; dO tile row col, chunk
+    // 2cs + half; transposed tiles (Qs^T, dO^T) row blk*32 + col, chunk 2tt + half.
+    uint32_t kread[KS], oread[CS], tread[2];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const int cw = i * kThreads + wu * 64;
-        const int c = cw + lane;
-        slive[i] = cw < NCH;
-        if (cw < NQ) {
-            const int row = c / (MP / 8), cc = c % (MP / 8);
-            sbase[i] = Qh, sstep[i] = MP * 2, stot[i] = N * MP * 2;
-            voff[i] = row * MP * 2 + cc * 16, loff[i] = row * QP + cc * 16;
-        } else if (cw < NQ + NQT) {
-            const int row = (c - NQ) / 4, cc = (c - NQ) % 4;
-            sbase[i] = Qth, sstep[i] = 2, stot[i] = MP * Np * 2;
-            voff[i] = row < MP ? row * Np * 2 + cc * 16 : kOutOfRange;
-            loff[i] = Q_B + row * TP + cc * 16;
-        } else if (cw < NQ + NQT + NO) {
-            const int row = (c - NQ - NQT) / (DV / 8), cc = (c - NQ - NQT) % (DV / 8);
-            sbase[i] = dOh, sstep[i] = DV * 2, stot[i] = N * DV * 2;
-            voff[i] = row * DV * 2 + cc * 16, loff[i] = Q_B + QT_B + row * OP + cc * 16;
-        } else {
-            const int row = (c - NQ - NQT - NO) / 4, cc = (c - NQ - NQT - NO) % 4;
-            sbase[i] = dOth, sstep[i] = 2, stot[i] = slive[i] ? DV * Np * 2 : 0;
-            voff[i] = row * Np * 2 + cc * 16;
-            loff[i] = Q_B + QT_B + DO_B + row * TP + cc * 16;
-        }
-    }
-    u32x4 stage[CPT];
-    float lstage, dstage;
-    const int ql = tid & (kTile - 1);  // every thread stages the lse and D of query ql
-    auto load_tile = [&](int q0) {
+    for (int ks = 0; ks < KS; ++ks) kread[ks] = col * MP * 2 + 16 * ((2 * ks + half) ^ kswz<MP>(col));
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int skip = q0 * sstep[i];
-            stage[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                tile_rsrc(sbase[i] + skip, stot[i] - skip), voff[i], 0, 0);
-        }
-        const int nl = (N - q0) * 4;
-        const float l = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(lseh + q0, nl), ql * 4, 0, 0));
-        dstage = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(tile_rsrc(Dh + q0, nl), ql * 4, 0, 0));
-        lstage = q0 + ql < N ? l * kLog2e : INFINITY;  // rows past N get zero weight
-    };
-    auto store_tile = [&](int buf) {
-        char* base = lds + buf * BUF;
+    for (int cs = 0; cs < CS; ++cs) oread[cs] = col * DV * 2 + 16 * ((2 * cs + half) ^ kswz<DV>(col));
 #pragma unroll
-        for (int i = 0; i < CPT; ++i)
-            if ((i + 1) * kThreads <= NCH || slive[i])
-                *reinterpret_cast<u32x4*>(base + loff[i]) = stage[i];
-        // identical values from the threads that share ql
-        reinterpret_cast<float*>(base + BUF - 2 * L_B)[ql] = lstage;
-        reinterpret_cast<float*>(base + BUF - L_B)[ql] = dstage;
-    };
+    for (int tt = 0; tt < 2; ++tt) tread[tt] = col * kTile * 2 + 16 * ((2 * tt + half) ^ kswz<kTile>(col));
 
     f32x16 dva[DB], dka[MB];
 #pragma unroll
@@ -416,52 +423,45 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 #pragma unroll
     for (int b = 0; b < MB; ++b) dka[b] = f32x16_fill(0.0f);
 
-    // One barrier per step, as in the query-major kernel.
-    auto step = [&](int t, auto mask_tag) {
+    // Three buffers, one barrier per step, as in the query-major kernel.
+    auto step = [&](int t, int cur, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int q0 = qstart + t * kTile;
-        store_tile((t + 1) & 1);
-        load_tile(q0 + 2 * kTile);
-        const char* Qts = lds + (t & 1) * BUF;  // Qs tile (rows = queries)
+        copy_tile(q0 + 2 * kTile, cur == 0 ? kBufs - 1 : cur - 1);
+        const char* Qts = lds + cur * BUF;      // Qs tile (rows = queries)
         const char* QTs = Qts + Q_B;            // Qs^T tile (rows = features)
         const char* dOs = QTs + QT_B;           // dO tile (rows = queries)
         const char* dOTs = dOs + DO_B;          // dO^T tile (rows = V columns)
-        const float* L2s = reinterpret_cast<const float*>(Qts + BUF - 2 * L_B);
-        const float* Ds = reinterpret_cast<const float*>(Qts + BUF - L_B);
+        const float* Ls = reinterpret_cast<const float*>(Qts + B16);  // -lse2 [32], -D [32]
         // causal: nothing to do if every query of the tile precedes every key of the wave
         if (!MASK || q0 + kTile - 1 >= k0w) {
-            // scores^T (32 queries x 32 keys)
-            f32x16 s = f32x16_fill(0.0f);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const f16x8 a = __builtin_bit_cast(
-                    f16x8, *reinterpret_cast<const u32x4*>(Qts + col * QP + (ks * 16 + half * 8) * 2));
-                s = mfma32x32x16(a, kf[ks], s);
-            }
-            // dA^T (32 queries x 32 keys) = dO . V^T
-            f32x16 da = f32x16_fill(0.0f);
-#pragma unroll
-            for (int cs = 0; cs < CS; ++cs) {
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4*>(dOs + col * OP + (cs * 16 + half * 8) * 2));
-                da = mfma32x32x16(a, vf[cs], da);
-            }
-            // weights and dS; the row (query) of slot i is 8*(i/4) + 4*half + i%4
-            f32x16 w, ds;
+            // accumulators start at -lse2 and -D of the slot's query (8*(i/4) + 4*half + i%4)
+            f32x16 s, da;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float4 l4 = *reinterpret_cast<const float4*>(L2s + 8 * g + 4 * half);
-                const float4 d4 = *reinterpret_cast<const float4*>(Ds + 8 * g + 4 * half);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+                const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * g + 4 * half);
+                const float4 d4 = *reinterpret_cast<const float4*>(Ls + kTile + 8 * g + 4 * half);
+                s[4 * g] = l4.x, s[4 * g + 1] = l4.y, s[4 * g + 2] = l4.z, s[4 * g + 3] = l4.w;
+                da[4 * g] = d4.x, da[4 * g + 1] = d4.y, da[4 * g + 2] = d4.z, da[4 * g + 3] = d4.w;
+            }
+            // scores^T (32 queries x 32 keys) - lse2
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 4 * g + r;
-                    float a = __builtin_amdgcn_exp2f(s[i] - lv[r]);
-                    if (MASK && myk > q0 + 8 * g + 4 * half + r) a = 0.0f;
-                    w[i] = a;
-                    ds[i] = a * (da[i] - dv4[r]);
-                }
+            for (int ks = 0; ks < KS; ++ks)
+                s = mfma32x32x16(__builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(Qts + kread[ks])),
+                                 kf[ks], s);
+            // dA^T (32 queries x 32 keys) = dO . V^T, minus D
+#pragma unroll
+            for (int cs = 0; cs < CS; ++cs)
+                da = mfma32x32x16(__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dOs + oread[cs])),
+                                  vf[cs], da);
+            // weights and dS
+            f32x16 w, ds;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float a = __builtin_amdgcn_exp2f(s[i]);
+                if (MASK && myk > q0 + 8 * (i >> 2) + 4 * half + (i & 3)) a = 0.0f;
+                w[i] = a;
+                ds[i] = a * da[i];
             }
             // dV^T (DV x 32 keys) += dO^T . A ; dKt^T (MP x 32 keys) += Qs^T . dS
 #pragma unroll
@@ -471,29 +471,28 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const bf16x8 a = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const u32x4*>(dOTs + (db * 32 + col) * TP + (tt * 16 + half * 8) * 2));
+                        bf16x8, *reinterpret_cast<const u32x4*>(dOTs + db * 32 * kTile * 2 + tread[tt]));
                     dva[db] = mfma32x32x16(a, bw, dva[db]);
                 }
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
                     const f16x8 a = __builtin_bit_cast(
-                        f16x8, *reinterpret_cast<const u32x4*>(QTs + (mb * 32 + col) * TP + (tt * 16 + half * 8) * 2));
+                        f16x8, *reinterpret_cast<const u32x4*>(QTs + mb * 32 * kTile * 2 + tread[tt]));
                     dka[mb] = mfma32x32x16(a, bs, dka[mb]);
                 }
             }
         }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(CPW + 1));
         __syncthreads();
     };
 
-    load_tile(qstart);
-    store_tile(0);
-    load_tile(qstart + kTile);
-    __syncthreads();
-    int t = 0;
+    __syncthreads();  // tile 0 from every wave
+    int t = 0, cur = 0;
 #pragma unroll 1
-    for (; t < nmask; ++t) step(t, Flag<true>{});
+    for (; t < nmask; ++t, cur = cur == kBufs - 1 ? 0 : cur + 1) step(t, cur, Flag<true>{});
 #pragma unroll 1
-    for (; t < ntiles; ++t) step(t, Flag<false>{});
+    for (; t < ntiles; ++t, cur = cur == kBufs - 1 ? 0 : cur + 1) step(t, cur, Flag<false>{});
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy may land after the workgroup ends
 
     if (kvalid) {
         const size_t row = (size_t)bh * N + myk;
@@ -679,11 +678,11 @@ template <int MP, int DV, bool CAUSAL>
 hipError_t launch_main(const BwdArgs& a, hipStream_t s) {
     const int nqb = (a.N + 127) / 128;
     bwd_q_kernel<MP, DV, CAUSAL><<<dim3(a.BH * nqb), kThreads, 0, s>>>(
-        a.Qs, a.Kt, a.Ktt, a.V, a.O, a.dO, a.lse, a.dQt, a.D, a.N, a.Np, nqb, a.scale);
+        a.Qs, a.Kt, a.Ktt, a.V, a.O, a.dO, a.lse, a.dQt, a.LD, a.N, a.Np, nqb, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     bwd_kv_kernel<MP, DV, CAUSAL><<<dim3(a.BH * nqb), kThreads, 0, s>>>(
-        a.Qs, a.Qst, a.Kt, a.V, a.dO, a.dOt, a.lse, a.D, a.dV, a.g_f32, a.dKt, a.N, a.Np, nqb);
+        a.Qs, a.Qst, a.Kt, a.V, a.dO, a.dOt, a.LD, a.dV, a.g_f32, a.dKt, a.N, a.Np, nqb);
     return hipGetLastError();
 }
 

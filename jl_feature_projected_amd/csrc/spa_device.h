@@ -77,4 +77,73 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Buffer descriptor over [base, base + bytes): loads past the end return zero. Raw buffer
+// (stride 0), 32-bit data format. The fields go through readfirstlane so they are SGPRs
+// (the asm operand needs them there) even where the compiler cannot prove them uniform.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+    r.z = __builtin_amdgcn_readfirstlane(bytes);
+    r.w = 0x00020000u;
+    return r;
+}
+
+// 16 bytes per lane from buffer offset voff straight into LDS at byte address m0 + 16 * lane
+// (m0 wave-uniform; readfirstlane keeps it in an SGPR where the compiler cannot prove that).
+// Issued as inline assembly so the compiler does not track it: it cannot tell that the LDS
+// it writes (another buffer) is disjoint from the LDS the tile loop reads, and would
+// otherwise wait for the copy before the first read. The copy's completion is awaited
+// explicitly (vmcnt) before the barrier that hands the buffer over. Device pass only: the
+// host pass does not parse AMDGPU assembly constraints.
+__device__ __forceinline__ void copy16_to_lds(u32x4 rsrc, uint32_t m0, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(rsrc)
+                 : "m0");
+#endif
+}
+
+// 16-byte chunk swizzles: LDS slot = global chunk ^ swizzle(row), a GF(2)-linear function of
+// the row's low bits, chosen so that every operand read touches each LDS bank once per
+// service cycle, whether the LDS serves 128 bytes per cycle over 32 banks or 256 bytes over
+// 64 (the K-tile tables were found by exhaustive search over such functions):
+//   K tile (rows of MP*2 bytes), score operand: 8 or 16 consecutive rows, one chunk each
+//   (the backward's tiles of rows of R*2 bytes, R in {16, 32, 64, 128}, are read the same
+//   way and use kswz<R>);
+//   V^T tile (rows of 128 bytes = 64 keys), PV operand: 8 or 16 consecutive rows, one chunk
+//   each. Rows r and r+8 share their position in a 256-byte bank row pair only if they differ
+//   in bit 0 after the swizzle, hence the extra bit-3 term.
+template <int MP>
+__device__ __forceinline__ int kswz(int row) {
+    constexpr int b0 = MP == 16 ? 0 : MP == 32 ? 0 : 1;
+    constexpr int b1 = MP == 16 ? 0 : MP == 32 ? 1 : 2;
+    constexpr int b2 = MP == 16 ? 1 : MP == 32 ? 2 : 4;
+    constexpr int b3 = MP == 16 ? 1 : MP == 32 ? 1 : MP == 64 ? 1 : 8;
+    return (row & 1 ? b0 : 0) ^ (row & 2 ? b1 : 0) ^ (row & 4 ? b2 : 0) ^ (row & 8 ? b3 : 0);
+}
+__device__ __forceinline__ int vtswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// As copy16_to_lds, 4 bytes per lane, to m0 + 4 * lane.
+__device__ __forceinline__ void copy4_to_lds(u32x4 rsrc, uint32_t m0, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(rsrc)
+                 : "m0");
+#endif
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
+// (expcnt and lgkmcnt left at their maxima, i.e. not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// LDS byte address of a __shared__ array's first byte (wave-uniform).
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
+}
+
 }  // namespace spa

@@ -64,7 +64,7 @@ struct BwdArgs {
     const uint16_t* dO;   // bf16 [BH, N, dv]
     const uint16_t* dOt;  // bf16 [BH, dv, Np], dO transposed, tokens permuted
     const float* lse;     // [BH, N], natural log (the forward's)
-    float* D;             // [BH, N]
+    float* LD;            // [BH, Np/32, 2, 32]: per 32 queries, -lse*log2(e) then -D
     float* dQt;           // [BH, N, mp]
     float* dKt;           // [BH, N, mp]
     float* dPpart;        // [BH, ceil(N / 256), d, m]

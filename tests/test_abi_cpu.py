@@ -166,7 +166,7 @@ def test_bwd_workspace_bytes(L):
     mp, np_ = 16, 128
     rows = BH * N
     sizes = [rows * mp * 2, rows * mp * 2, BH * mp * np_ * 2, BH * mp * np_ * 2, BH * dv * np_ * 2,
-             rows * 4, rows * mp * 4, rows * mp * 4, BH * 1 * d * m * 4]
+             BH * np_ * 2 * 4, rows * mp * 4, rows * mp * 4, BH * 1 * d * m * 4]
     assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, m, dv, spa.SPA_BF16) == sum(a256(s) for s in sizes)
     assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, 65, dv, spa.SPA_BF16) == 0
     assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, m, dv, spa.SPA_F32) == 0
