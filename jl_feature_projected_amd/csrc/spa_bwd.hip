@@ -16,9 +16,10 @@
 //                  dQt^T = Kt^T . dS^T, after D_i from the wave's own dO and O rows.
 //   bwd_kv_kernel  key-major: per 32-key wave, a loop over 32-query tiles computes
 //                  dV^T = dO^T . A and dKt^T = Qt^T . dS. Needs D from bwd_q_kernel.
-//   proj_back_kernel   dQ = dQt P^T and dK = dKt P^T.
-//   dp_partial_kernel / dp_reduce_kernel   the projection gradient, per 256-row chunk and
-//                  then summed over chunks and batches in a fixed order (deterministic).
+//   proj_grad_kernel   dQ = dQt P^T, dK = dKt P^T and the projection gradient's partial
+//                  per 256-row chunk (bf16 MFMAs, fp32 factors split hi + lo).
+//   dp_reduce_kernel   the partials summed over chunks and batches in a fixed order
+//                  (deterministic).
 // In the transposed (A-operand) tiles the rows are V^T-ordered: within every 16 tokens the
 // order 0-3, 8-11, 4-7, 12-15, which is the order in which a score accumulator lane holds
 // its 8 tokens of a 16-token k-step. So every MFMA operand is one 16-byte LDS read or a
@@ -529,136 +530,216 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 }
 
 // ---------------------------------------------------------------------------------------
-// dX[bh, n, k] = sum_{c < m} dXt[bh, n, c] P[h, k, c] for X in {Q, K} (z = blockIdx.y).
-// One workgroup per (head, 64 rows); P^T and the rows' dXt staged in LDS; each thread
-// computes a block of RT rows x 4 features with fp32 FMAs (RT = D / 16).
-constexpr int kBackRows = 64;
-template <int D>
-__global__ __launch_bounds__(kThreads) void proj_back_kernel(
-    const float* __restrict__ dQt, const float* __restrict__ dKt, const uint16_t* __restrict__ P,
-    void* __restrict__ dQ, void* __restrict__ dK, int out_f32, int N, int H, int m, int mp,
-    int nrb) {
-    constexpr int KG = D / 4;                 // feature groups of 4
-    constexpr int RT = kBackRows * KG / kThreads;  // rows per thread
-    extern __shared__ __attribute__((aligned(16))) float sm[];
-    float* Ps = sm;                           // [m][D]: P^T of the head
-    float* Xs = sm + m * D;                   // [kBackRows][m]
-    const int bh = blockIdx.x / nrb;
-    const int n0 = (blockIdx.x - bh * nrb) * kBackRows;
-    const int z = blockIdx.y;
-    const float* src = (z ? dKt : dQt) + (size_t)bh * N * mp;
-    const int h = bh % H;
-    for (int i = threadIdx.x; i < D * m; i += kThreads) {
-        const int k = i / m, c = i - k * m;
-        Ps[c * D + k] = __uint_as_float((uint32_t)P[(size_t)h * D * m + i] << 16);
-    }
-    for (int i = threadIdx.x; i < kBackRows * m; i += kThreads) {
-        const int r = i / m, c = i - r * m;
-        Xs[i] = n0 + r < N ? src[(size_t)(n0 + r) * mp + c] : 0.0f;
-    }
-    __syncthreads();
-    const int kg = threadIdx.x % KG, rg = threadIdx.x / KG;
-    float acc[RT][4];
-#pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[r][j] = 0.0f;
-    for (int c = 0; c < m; ++c) {
-        const float4 p4 = *reinterpret_cast<const float4*>(Ps + c * D + 4 * kg);
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            const float x = Xs[(rg * RT + r) * m + c];
-            acc[r][0] += x * p4.x;
-            acc[r][1] += x * p4.y;
-            acc[r][2] += x * p4.z;
-            acc[r][3] += x * p4.w;
-        }
-    }
-    void* dst = z ? dK : dQ;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-        const int n = n0 + rg * RT + r;
-        if (n >= N) continue;
-        const size_t o = ((size_t)bh * N + n) * D + 4 * kg;
-        if (out_f32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(dst) + o) =
-                make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
-        } else {
-            u32x2 w;
-            w.x = pack_bf16x2(acc[r][0], acc[r][1]);
-            w.y = pack_bf16x2(acc[r][2], acc[r][3]);
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dst) + o) = w;
-        }
-    }
+// Back through the projection, one pass over the rows of a head:
+//   dQ = dQt P^T, dK = dKt P^T                (rows of the workgroup's chunk)
+//   partial[bh, chunk] = Q^T dQt + K^T dKt    (the chunk's share of the projection gradient)
+// on bf16 MFMAs with each fp32 factor of dQt and dKt split as hi + lo (both bf16, hi the
+// rounded value, lo the rounded remainder): the products keep about 16 significant bits of
+// the fp32 factor, the accumulation is fp32. Q, K and P are bf16 already.
+// Workgroup: kPgRows rows of one head, in passes of kPgSub rows staged in LDS transposed
+// (feature-major) for the products that contract over rows.
+constexpr int kPgRows = 256;
+constexpr int kPgSub = 64;
+
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+    const uint32_t h = pack_bf16x2(x, 0.0f) & 0xffffu;
+    hi = (uint16_t)h;
+    lo = (uint16_t)(pack_bf16x2(x - __uint_as_float(h << 16), 0.0f) & 0xffffu);
 }
 
-// partial[bh, chunk, k, c] = sum over the chunk's rows n of Q[n,k] dQt[n,c] + K[n,k] dKt[n,c].
-// Thread t owns features 4*(t % (D/4)) .. +3 and columns c = t / (D/4) + CG * i (CG = 1024 /
-// D column groups, TC = D / 16 columns each, m <= 64), accumulated over rows in fp32.
-constexpr int kDpRows = 256;
-constexpr int kDpSub = 32;
-template <int D>
-__global__ __launch_bounds__(kThreads) void dp_partial_kernel(
+template <int D, int MP>
+__global__ __launch_bounds__(kThreads, 2) void proj_grad_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const float* __restrict__ dQt,
-    const float* __restrict__ dKt, float* __restrict__ part, int N, int m, int mp, int nch) {
-    constexpr int KG = D / 4;
-    constexpr int CG = kThreads / KG;
-    constexpr int TC = 64 / CG;
-    extern __shared__ __attribute__((aligned(16))) float sm[];
-    float* Qs = sm;                      // [kDpSub][D]
-    float* Ks = Qs + kDpSub * D;         // [kDpSub][D]
-    float* dQs = Ks + kDpSub * D;        // [kDpSub][m]
-    float* dKs = dQs + kDpSub * m;       // [kDpSub][m]
+    const float* __restrict__ dKt, const uint16_t* __restrict__ P, void* __restrict__ dQ,
+    void* __restrict__ dK, int out_f32, float* __restrict__ part, int N, int H, int m, int nch) {
+    constexpr int KB = D / 32;                 // 32-feature blocks
+    constexpr int KS = MP / 16;                // k-steps over the projected columns
+    constexpr int MB = (MP + 31) / 32;         // 32-column blocks of the partial
+    constexpr int TP = kPgSub * 2 + 16;        // transposed tile row pitch (bytes), padded
+    constexpr int QT_B = D * TP;               // Q^T or K^T: D feature rows x kPgSub rows
+    constexpr int XT_B = MB * 32 * TP;         // one bf16 plane of dQt^T or dKt^T
+    constexpr int ZW = KB == 4 ? 1 : 2;        // waves per feature block (D = 64: one per term)
+    static_assert(KB * ZW == kWaves, "one feature block (and term) per wave");
+    __shared__ __attribute__((aligned(16))) char lds[2 * QT_B + 4 * XT_B];
+    // Q^T (z = 0) and K^T (z = 1); then the hi (p = 0) and lo planes of dQt^T and dKt^T
+    auto QTs = [&](int z) { return lds + z * QT_B; };
+    auto XTs = [&](int z, int p) { return lds + 2 * QT_B + (2 * z + p) * XT_B; };
+
     const int bh = blockIdx.x / nch;
     const int ch = blockIdx.x - bh * nch;
-    const int n0 = ch * kDpRows;
-    const int kg = threadIdx.x % KG, cg = threadIdx.x / KG;
-    float acc[4][TC];
+    const int h = bh % H;
+    const int r0 = ch * kPgRows;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+    const int kb = wave % KB;                  // this wave's feature block
+
+    // Feature rows past MP of the dQt^T planes stay zero.
+    if (MB * 32 > MP) {
+        for (int i = tid; i < (MB * 32 - MP) * TP / 4; i += kThreads)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+            for (int z = 0; z < 2; ++z)
 #pragma unroll
-        for (int i = 0; i < TC; ++i) acc[j][i] = 0.0f;
-    for (int s0 = n0; s0 < n0 + kDpRows && s0 < N; s0 += kDpSub) {
-        __syncthreads();
-        for (int i = threadIdx.x; i < kDpSub * D; i += kThreads) {
-            const int r = i / D, kk = i - r * D;
-            const bool ok = s0 + r < N;
-            const size_t o = ((size_t)bh * N + s0 + r) * D + kk;
-            Qs[i] = ok ? __uint_as_float((uint32_t)Q[o] << 16) : 0.0f;
-            Ks[i] = ok ? __uint_as_float((uint32_t)K[o] << 16) : 0.0f;
+                for (int p = 0; p < 2; ++p) reinterpret_cast<uint32_t*>(XTs(z, p) + MP * TP)[i] = 0u;
+    }
+
+    // A operands of dX = dXt P^T: P[k][c] for k = kb*32 + col, c = 16ks + 8half .. +7 (zero
+    // past m).
+    bf16x8 pa[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const uint16_t* prow = P + ((size_t)h * D + kb * 32 + col) * m;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = ks * 16 + half * 8 + e;
+            pa[ks][e] = __builtin_bit_cast(bf16_t, c < m ? prow[c] : (uint16_t)0);
         }
-        for (int i = threadIdx.x; i < kDpSub * m; i += kThreads) {
-            const int r = i / m, c = i - r * m;
-            const bool ok = s0 + r < N;
-            const size_t o = ((size_t)bh * N + s0 + r) * mp + c;
-            dQs[i] = ok ? dQt[o] : 0.0f;
-            dKs[i] = ok ? dKt[o] : 0.0f;
+    }
+
+    f32x16 accp[MB];  // this wave's share of the partial: features kb*32.., columns mb*32..
+#pragma unroll
+    for (int b = 0; b < MB; ++b) accp[b] = f32x16_fill(0.0f);
+
+#pragma unroll 1
+    for (int rs = r0; rs < r0 + kPgRows && rs < N; rs += kPgSub) {
+        __syncthreads();  // the previous pass's tiles are read
+        // Q^T and K^T: thread = (row, 16-byte chunk column), 8 two-byte transposed writes.
+        const int row = tid % kPgSub;
+        const bool rok = rs + row < N;
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+            const uint16_t* X = (z ? K : Q) + ((size_t)bh * N + rs + row) * D;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) {
+                const int cc = tid / kPgSub + kWaves * i;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (rok) v = *reinterpret_cast<const u32x4*>(X + cc * 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    *reinterpret_cast<uint16_t*>(QTs(z) + (cc * 8 + e) * TP + row * 2) =
+                        (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+        // dQt^T and dKt^T, hi and lo planes: thread = (row, 4-column chunk).
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+            const float* X = (z ? dKt : dQt) + ((size_t)bh * N + rs + row) * MP;
+#pragma unroll
+            for (int i = 0; i < (MP / 4 + kWaves - 1) / kWaves; ++i) {
+                const int cc = tid / kPgSub + kWaves * i;
+                if (cc < MP / 4) {
+                    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    if (rok) v = *reinterpret_cast<const float4*>(X + cc * 4);
+                    const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint16_t hi, lo;
+                        split_bf16(f[e], hi, lo);
+                        *reinterpret_cast<uint16_t*>(XTs(z, 0) + (cc * 4 + e) * TP + row * 2) = hi;
+                        *reinterpret_cast<uint16_t*>(XTs(z, 1) + (cc * 4 + e) * TP + row * 2) = lo;
+                    }
+                }
+            }
         }
         __syncthreads();
-        for (int r = 0; r < kDpSub; ++r) {
-            const float4 q = *reinterpret_cast<const float4*>(Qs + r * D + 4 * kg);
-            const float4 kv = *reinterpret_cast<const float4*>(Ks + r * D + 4 * kg);
+
+        // dQ, dK: output block (term z, 32-row block rb, feature block kb):
+        // D[k][row] = sum_c P[k][c] Xt[row][c], B operand = lane row's 8 columns, hi and lo.
 #pragma unroll
-            for (int i = 0; i < TC; ++i) {
-                const int c = cg + CG * i;
-                if (c < m) {
-                    const float a = dQs[r * m + c], b = dKs[r * m + c];
-                    acc[0][i] += q.x * a + kv.x * b;
-                    acc[1][i] += q.y * a + kv.y * b;
-                    acc[2][i] += q.z * a + kv.z * b;
-                    acc[3][i] += q.w * a + kv.w * b;
+        for (int i = 0; i < 4 / ZW; ++i) {
+            const int bz = (wave / KB) + ZW * i;   // 0..3 over (z, rb)
+            const int z = bz >> 1, rb = bz & 1;
+            const int orow = rs + rb * 32 + col;
+            const bool ook = orow < N;
+            const float* X = (z ? dKt : dQt) + ((size_t)bh * N + orow) * MP;
+            f32x16 o = f32x16_fill(0.0f);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f), b = a;
+                if (ook) {
+                    a = *reinterpret_cast<const float4*>(X + ks * 16 + half * 8);
+                    b = *reinterpret_cast<const float4*>(X + ks * 16 + half * 8 + 4);
+                }
+                const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                bf16x8 bh8, bl8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uint16_t hi, lo;
+                    split_bf16(f[e], hi, lo);
+                    bh8[e] = __builtin_bit_cast(bf16_t, hi);
+                    bl8[e] = __builtin_bit_cast(bf16_t, lo);
+                }
+                o = mfma32x32x16(pa[ks], bh8, o);
+                o = mfma32x32x16(pa[ks], bl8, o);
+            }
+            if (ook) {
+                void* dst = z ? dK : dQ;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const size_t at = ((size_t)bh * N + orow) * D + kb * 32 + 8 * g + 4 * half;
+                    if (out_f32) {
+                        *reinterpret_cast<float4*>(static_cast<float*>(dst) + at) =
+                            make_float4(o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]);
+                    } else {
+                        u32x2 w;
+                        w.x = pack_bf16x2(o[4 * g], o[4 * g + 1]);
+                        w.y = pack_bf16x2(o[4 * g + 2], o[4 * g + 3]);
+                        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dst) + at) = w;
+                    }
+                }
+            }
+        }
+
+        // Partial: D[k][c] += sum_rows X^T[k][row] Xt[row][c] over this wave's term(s).
+#pragma unroll
+        for (int zi = 0; zi < 2 / ZW; ++zi) {
+            const int z = ZW == 1 ? zi : wave / KB;
+#pragma unroll
+            for (int s4 = 0; s4 < kPgSub / 16; ++s4) {
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(QTs(z) + (kb * 32 + col) * TP + (16 * s4 + 8 * half) * 2));
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        const bf16x8 b = __builtin_bit_cast(
+                            bf16x8, *reinterpret_cast<const u32x4*>(XTs(z, p) + (mb * 32 + col) * TP + (16 * s4 + 8 * half) * 2));
+                        accp[mb] = mfma32x32x16(a, b, accp[mb]);
+                    }
+            }
+        }
+    }
+
+    // D = 64: the K-term waves hand their partial to the Q-term waves of the same block.
+    if (ZW == 2) {
+        __syncthreads();
+        float* red = reinterpret_cast<float*>(lds);
+        if (wave >= KB) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) red[((kb * MB + mb) * 16 + i) * 64 + lane] = accp[mb][i];
+        }
+        __syncthreads();
+        if (wave < KB) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) accp[mb][i] += red[((kb * MB + mb) * 16 + i) * 64 + lane];
+        }
+    }
+    if (wave < KB) {
+        float* dst = part + ((size_t)bh * nch + ch) * D * m;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int c = mb * 32 + col;
+            if (c < m) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int k = kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                    dst[(size_t)k * m + c] = accp[mb][i];
                 }
             }
         }
     }
-    float* dst = part + ((size_t)bh * nch + ch) * D * m;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < TC; ++i) {
-            const int c = cg + CG * i;
-            if (c < m) dst[(size_t)(4 * kg + j) * m + c] = acc[j][i];
-        }
 }
 
 // dP[h, k, c] = sum over b (ascending) and chunks (ascending) of the partials.
@@ -713,24 +794,22 @@ hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
     }
     if (e != hipSuccess) return e;
     // back through the projection
-    const int nrb = (a.N + kBackRows - 1) / kBackRows;
-    const size_t sm_back = sizeof(float) * ((size_t)a.m * a.d + (size_t)kBackRows * a.m);
-    if (a.d == 128)
-        proj_back_kernel<128><<<dim3(a.BH * nrb, 2), kThreads, sm_back, stream>>>(
-            a.dQt, a.dKt, a.P, a.dQ, a.dK, a.g_f32, a.N, a.H, a.m, a.mp, nrb);
-    else
-        proj_back_kernel<64><<<dim3(a.BH * nrb, 2), kThreads, sm_back, stream>>>(
-            a.dQt, a.dKt, a.P, a.dQ, a.dK, a.g_f32, a.N, a.H, a.m, a.mp, nrb);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int nch = (a.N + kDpRows - 1) / kDpRows;
-    const size_t sm_dp = sizeof(float) * (2 * (size_t)kDpSub * a.d + 2 * (size_t)kDpSub * a.m);
-    if (a.d == 128)
-        dp_partial_kernel<128><<<dim3(a.BH * nch), kThreads, sm_dp, stream>>>(
-            a.Q, a.K, a.dQt, a.dKt, a.dPpart, a.N, a.m, a.mp, nch);
-    else
-        dp_partial_kernel<64><<<dim3(a.BH * nch), kThreads, sm_dp, stream>>>(
-            a.Q, a.K, a.dQt, a.dKt, a.dPpart, a.N, a.m, a.mp, nch);
+    const int nch = (a.N + kPgRows - 1) / kPgRows;
+    const dim3 grid(a.BH * nch);
+#define SPA_PG(D_, MP_)                                                                  \
+    proj_grad_kernel<D_, MP_><<<grid, kThreads, 0, stream>>>(a.Q, a.K, a.dQt, a.dKt, a.P, \
+                                                            a.dQ, a.dK, a.g_f32, a.dPpart, \
+                                                            a.N, a.H, a.m, nch)
+    if (a.d == 128) {
+        if (a.mp == 16) SPA_PG(128, 16);
+        else if (a.mp == 32) SPA_PG(128, 32);
+        else SPA_PG(128, 64);
+    } else {
+        if (a.mp == 16) SPA_PG(64, 16);
+        else if (a.mp == 32) SPA_PG(64, 32);
+        else SPA_PG(64, 64);
+    }
+#undef SPA_PG
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nout = a.d * a.m;
