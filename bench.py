@@ -32,13 +32,18 @@ import jl_feature_projected_amd as spa  # noqa: E402
 from jl_feature_projected_amd import accounting, inputs  # noqa: E402
 
 METRIC = "projected-attention fwd TFLOP/s and % bf16 MFMA peak at N=8192,d=128,m=32"
-ATTN_SRC = os.path.join(ROOT, "jl_feature_projected_amd", "csrc", "spa_attn_bf16.hip")
+# The attention kernel's source: the kernel file and the device helpers it includes.
+ATTN_SRCS = [os.path.join(ROOT, "jl_feature_projected_amd", "csrc", f)
+             for f in ("spa_attn_bf16.hip", "spa_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_c3_hbm_traffic.md")
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload_name: str):
@@ -52,7 +57,7 @@ def measured_traffic(workload_name: str):
     m_b = re.search(r"hbm bytes per launch:\s*`?([0-9.eE+]+)", text)
     if not (m_hash and m_wl and m_b):
         return None
-    if m_hash.group(1) != source_hash(ATTN_SRC) or m_wl.group(1) != workload_name:
+    if m_hash.group(1) != source_hash(ATTN_SRCS) or m_wl.group(1) != workload_name:
         return None
     return float(m_b.group(1))
 
