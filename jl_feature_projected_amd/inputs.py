@@ -48,7 +48,10 @@ class Workload:
     qk: str = "iid"  # "iid" or "lowrank"
     qk_norm: bool = True  # rescale Q and K rows to norm sqrt(d)
     v_norm: bool = True  # rescale V rows to norm sqrt(dv)
-    proj: str = "gauss"  # "gauss" (N(0, 1/m)) or "identity" (m == d)
+    proj: str = "gauss"  # "gauss" (N(0, 1/m)), "identity" (m == d), "sparse", "block", "banded"
+    proj_s: float = 0.0  # "sparse": the sparsity level s (0: sqrt(d))
+    proj_block: tuple = (16, 4)  # "block": a input features x b outputs per block
+    proj_band: int = 16  # "banded": nonzeros per input feature
     seed: int = 0
 
     @property
@@ -111,16 +114,59 @@ def _qk_block(rng: np.random.Generator, w: Workload) -> np.ndarray:
     return x
 
 
+def sparse_projection(rng: np.random.Generator, d: int, m: int, s: float) -> np.ndarray:
+    """[d, m]: the sparse random matrix of the Sparse Projection Attention page, Sec. 2.2
+    Definition 1 -- each entry independently sqrt(s/m) times +1 or -1 with probability
+    1/(2s) each, else 0 (s >= 1)."""
+    if s < 1.0:
+        raise ValueError("the sparsity level s must be >= 1")
+    u = rng.random((d, m))
+    sign = np.where(u < 0.5 / s, 1.0, np.where(u < 1.0 / s, -1.0, 0.0))
+    return sign * math.sqrt(s / m)
+
+
+def block_projection(rng: np.random.Generator, d: int, m: int, a: int, b: int) -> np.ndarray:
+    """[d, m]: block pattern a x b -- input features [a r, a r + a) feed outputs
+    [b c, b c + b) with c = r mod (m / b), entries N(0, 1/b) inside the blocks, zero
+    elsewhere (every input feature has b nonzeros, so E[P P^T] = I)."""
+    if d % a or m % b:
+        raise ValueError("the block shape must divide d x m")
+    p = np.zeros((d, m))
+    for r in range(d // a):
+        c = r % (m // b)
+        p[a * r:a * r + a, b * c:b * c + b] = rng.standard_normal((a, b)) / math.sqrt(b)
+    return p
+
+
+def banded_projection(rng: np.random.Generator, d: int, m: int, w: int) -> np.ndarray:
+    """[d, m]: banded pattern of width w -- input feature i feeds the w outputs
+    (floor(i m / d) - w // 2 + t) mod m, t < w, with N(0, 1/w) entries (E[P P^T] = I)."""
+    if not 1 <= w <= m:
+        raise ValueError("the band width must be in [1, m]")
+    p = np.zeros((d, m))
+    for i in range(d):
+        cols = (i * m // d - w // 2 + np.arange(w)) % m
+        p[i, cols] = rng.standard_normal(w) / math.sqrt(w)
+    return p
+
+
 def _projection(rng: np.random.Generator, w: Workload) -> np.ndarray:
     if w.proj == "identity":
         if w.m != w.d:
             raise ValueError("identity projection needs m == d")
         return np.broadcast_to(np.eye(w.d), (w.H, w.d, w.d)).copy()
-    if w.proj != "gauss":
-        raise ValueError(f"unknown projection {w.proj!r}")
     p = np.empty((w.H, w.d, w.m))
     for h in range(w.H):
-        p[h] = rng.standard_normal((w.d, w.m)) / math.sqrt(w.m)
+        if w.proj == "gauss":
+            p[h] = rng.standard_normal((w.d, w.m)) / math.sqrt(w.m)
+        elif w.proj == "sparse":
+            p[h] = sparse_projection(rng, w.d, w.m, w.proj_s or math.sqrt(w.d))
+        elif w.proj == "block":
+            p[h] = block_projection(rng, w.d, w.m, *w.proj_block)
+        elif w.proj == "banded":
+            p[h] = banded_projection(rng, w.d, w.m, w.proj_band)
+        else:
+            raise ValueError(f"unknown projection {w.proj!r}")
     return p
 
 

@@ -130,6 +130,31 @@ def test_small_shapes_full(dev, oracle_mod, N, d, m, dv, causal):
     assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
 
 
+# Fixed sparse and structured projections (Sparse Projection Attention page, Sec. 2.2
+# Definition 1; the block and banded patterns of Sec. 3.2 / Table 6 as the input generators
+# read them): the kernel takes any dense P, zeros included.
+PROJECTIONS = [
+    dict(proj="sparse"),                    # s = sqrt(d)
+    dict(proj="sparse", proj_s=20.0),       # 95 % zeros
+    dict(proj="block", proj_block=(16, 4)),
+    dict(proj="block", proj_block=(8, 8)),
+    dict(proj="banded", proj_band=16),
+]
+
+
+@pytest.mark.parametrize("kw", PROJECTIONS, ids=lambda kw: "-".join(str(v) for v in kw.values()))
+@pytest.mark.parametrize("causal", [True, False])
+def test_structured_projections_full(dev, oracle_mod, kw, causal):
+    w = inputs.Workload(f"proj-{'-'.join(str(v) for v in kw.values())}-c{int(causal)}", 2, 2,
+                        700, 128, 32, 128, causal, seed=2000 + int(causal), **kw)
+    x = inputs.draw(w)
+    note(w.name)
+    O, lse = run(x, dev, return_lse=True)
+    Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, causal, with_lse=True)
+    assert_bf16_close(np64(O), Or, what=w.name)
+    assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
+
+
 @pytest.mark.parametrize("N,m,dv,causal", [(200, 16, 64, True), (333, 40, 128, False)])
 def test_fp32_path_other_shapes(dev, oracle_mod, N, m, dv, causal):
     w = inputs.Workload(f"f32-n{N}-m{m}", 1, 2, N, 96, m, dv, causal, dtype="f32", seed=7)
