@@ -132,6 +132,38 @@ def time_backward(w, x, Q, K, V, P, steps, warmup, dev) -> dict:
             "grad_dtype": "f32"}
 
 
+def time_decode(w, x, P, steps, warmup, dev) -> dict:
+    """One decode step per call: the last query of every head against the whole cache of
+    projected keys (fp16) and values, spa_attn_decode timed between events on the launch
+    stream. HBM-bound: the reported rate is the cache bytes read per second."""
+    K, V = x.K.to(dev), x.V.to(dev)
+    cache = torch.empty((w.B, w.H, w.N, w.m), dtype=torch.float16, device=dev)
+    spa.spa_kcache_append(K, P, cache, 0)
+    Q = x.Q[:, :, -1:].contiguous().to(dev)
+    ws = torch.empty(spa.spa_attn_decode_workspace_bytes(w.B, w.H, 1, w.N, w.dv),
+                     dtype=torch.uint8, device=dev)
+
+    def dstep():
+        spa.spa_attn_decode(Q, cache, V, P, w.N, w.scale, w.causal, workspace=ws)
+
+    for _ in range(warmup):
+        dstep()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        dstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    cache_bytes = w.B * w.H * w.N * (2 * w.m + 2 * w.dv)
+    gbs = cache_bytes / (ms * 1e-3) / 1e9
+    return {"ms_per_step": round(ms, 5), "cache_bytes": cache_bytes,
+            "value": round(gbs, 1), "unit": "GB/s", "frac_of_hbm_peak": round(gbs / 8000.0, 4),
+            "k_cache_vs_k_bytes": round(w.m / w.d, 4), "queries_per_head": 1}
+
+
 def calibrate_copy(dev) -> None:
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -152,6 +184,9 @@ def main() -> int:
     ap.add_argument("--workload", default=inputs.HEADLINE, choices=sorted(inputs.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="also time one decode step (spa_attn_decode, one query per head "
+                         "against the whole cache) and report it in a 'decode' object")
     ap.add_argument("--backward", action="store_true",
                     help="also time spa_attn_bwd (bf16 workloads) and report it in a "
                          "'backward' object")
@@ -254,6 +289,8 @@ def main() -> int:
     }
     if args.backward and w.dtype == "bf16":
         res["backward"] = time_backward(w, x, Q, K, V, P, args.steps, args.warmup, dev)
+    if args.decode and w.dtype == "bf16":
+        res["decode"] = time_decode(w, x, P, args.steps, args.warmup, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(res), flush=True)

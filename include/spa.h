@@ -156,7 +156,7 @@ size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
  * (SPA_ERR_UNSUPPORTED otherwise). The projected queries and keys are prepared exactly as
  * in the forward (fp16), so the recomputed scores match the forward's bit for bit; the
  * weights meet dO in bf16 and dS meets the projected operands in fp16, all on MFMA with fp32
- * accumulation. Six launches on `stream`; results are deterministic (no atomics).
+ * accumulation. Five launches on `stream`; results are deterministic (no atomics).
  */
 spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const void* P,
                           const void* O, const void* dO, const float* lse, float scale,
@@ -164,6 +164,61 @@ spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const voi
                           spa_dtype_t dtype, void* dQ, void* dK, void* dV, float* dP,
                           spa_dtype_t g_dtype, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * spa_kcache_append -- write projected keys into a key cache (SPA page Sec. 3.1.2: keys
+ * enter the scores only through Kt = K P, so a cache of Kt serves every later query):
+ *
+ *   cache[b, h, row0 + n, :] = fp16(K[b, h, n, :] . P[h])   for 0 <= n < N
+ *
+ *   K      [B,H,N,d] bf16 (dtype SPA_BF16; d in {64, 128}), the new keys.
+ *   P      [H,d,m] bf16, 1 <= m <= 128.
+ *   cache  [B,H,rows,m] fp16 (device, caller-owned), rows per head >= row0 + N; rows outside
+ *          [row0, row0 + N) are not touched. fp32 accumulation, one RNE rounding to fp16.
+ *
+ * 16-byte aligned bases; the cache may not overlap K or P. One launch on `stream`.
+ */
+spa_status_t spa_kcache_append(const void* K, const void* P, void* cache, int B, int H, int N,
+                               int d, int m, int rows, int row0, spa_dtype_t dtype,
+                               void* stream);
+
+/*
+ * spa_attn_decode_workspace_bytes -- bytes of scratch spa_attn_decode needs (per query and
+ * key split dv + 2 floats, per query 128 floats for its projection), 0 if the shape is
+ * invalid or unsupported.
+ */
+size_t spa_attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int dv);
+
+/*
+ * spa_attn_decode -- Nq queries against the first Nk rows of a projected-key cache and a
+ * value cache: the forward of spa_attn_fwd (SPA page Sec. 3.1.3, Algorithm 1; PDA page
+ * Algorithm 2.1 steps 1-3 and 5) with the keys given as Kt = K P:
+ *
+ *   O[b,h,i,:] = sum_j softmax_j(scale * (Q[b,h,i,:] P[h]) . cache[b,h,j,:]) Vc[b,h,j,:]
+ *
+ * over keys j < Nk; with causal = 1 the mask is aligned to the end of the cache: query i
+ * sits at position Nk - Nq + i and sees keys j <= Nk - Nq + i (so Nq = Nk reproduces the
+ * square causal forward, and Nq = 1 is one decode step).
+ *
+ *   Q      [B,H,Nq,d] bf16 (dtype SPA_BF16), d in {64, 128}; P [H,d,m] bf16, 1 <= m <= 128.
+ *   cache  [B,H,rows,m] fp16, written by spa_kcache_append; Vc [B,H,rows,dv] bf16,
+ *          dv in {64, 128}; 1 <= Nq <= Nk <= rows.
+ *   O      [B,H,Nq,dv] in o_dtype (SPA_F32 or SPA_BF16); lse [B,H,Nq] fp32 (natural log of
+ *          the softmax normaliser of the scaled scores) or NULL.
+ *   workspace / workspace_bytes: spa_attn_decode_workspace_bytes(B, H, Nq, Nk, dv) bytes,
+ *          or NULL (allocated and freed stream-ordered).
+ *
+ * Queries are projected in fp32; scores, an exact online softmax and the weights x V are
+ * fp32 (HBM-bound: each cache byte is read once per head and group of up to 16 queries).
+ * Keys are split across workgroups and the splits merged in a fixed order: deterministic.
+ * Errors: SPA_ERR_INVALID_ARGUMENT (nulls, dimensions, alignment, overlaps, Nq > Nk > rows),
+ * SPA_ERR_UNSUPPORTED (dtype, d, m, dv), SPA_ERR_WORKSPACE, SPA_ERR_HIP. Three launches.
+ */
+spa_status_t spa_attn_decode(const void* Q, const void* cache, const void* Vc, const void* P,
+                             float scale, int causal, int B, int H, int Nq, int Nk, int rows,
+                             int d, int m, int dv, spa_dtype_t dtype, void* O,
+                             spa_dtype_t o_dtype, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * Per-launch timing for benchmarks. spa_profile_begin(max_calls) starts recording HIP

@@ -27,7 +27,8 @@ SPA_BF16 = 1
 
 EXPORTS = ("spa_version", "spa_status_string", "spa_last_error", "spa_project",
            "spa_attn_fwd_workspace_bytes", "spa_attn_fwd", "spa_attn_bwd_workspace_bytes",
-           "spa_attn_bwd", "spa_profile_begin", "spa_profile_end")
+           "spa_attn_bwd", "spa_kcache_append", "spa_attn_decode_workspace_bytes",
+           "spa_attn_decode", "spa_profile_begin", "spa_profile_end")
 
 
 class SpaError(RuntimeError):
@@ -70,6 +71,13 @@ def lib() -> ctypes.CDLL:
     L.spa_attn_bwd.restype = st
     L.spa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, vp, vp,
                                vp, vp, i, vp, z, vp]
+    L.spa_kcache_append.restype = st
+    L.spa_kcache_append.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, vp]
+    L.spa_attn_decode_workspace_bytes.restype = z
+    L.spa_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.spa_attn_decode.restype = st
+    L.spa_attn_decode.argtypes = [vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, i, i, vp, i, vp,
+                                  vp, z, vp]
     L.spa_profile_begin.restype = st
     L.spa_profile_begin.argtypes = [i]
     dp = ctypes.POINTER(ctypes.c_double)
@@ -227,6 +235,74 @@ def spa_attn_bwd(Q, K, V, P, O, dO, lse, scale: float | None = None, causal: boo
                              dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), dP.data_ptr(),
                              _dtype_code(gdt), ws_ptr, ws_bytes, _stream_ptr(Q.device)))
     return dQ, dK, dV, dP
+
+
+def spa_kcache_append(K, P, cache, row0: int) -> None:
+    """cache[b,h,row0:row0+N,:] = fp16(K[b,h] @ P[h]) on the current stream.
+
+    K [B,H,N,d] bf16 (the new keys), P [H,d,m] bf16, cache [B,H,rows,m] float16 (device,
+    caller-owned, modified in place).
+    """
+    torch = _torch()
+    for name, x in (("K", K), ("P", P), ("cache", cache)):
+        _device_tensor(x, name)
+    if K.dim() != 4 or P.dim() != 3 or cache.dim() != 4:
+        raise ValueError("K must be [B,H,N,d], P [H,d,m] and cache [B,H,rows,m]")
+    B, H, N, d = K.shape
+    m = P.shape[2]
+    if P.shape[:2] != (H, d) or cache.shape[:2] != (B, H) or cache.shape[3] != m:
+        raise ValueError("P must be [H,d,m] and cache [B,H,rows,m]")
+    if cache.dtype != torch.float16:
+        raise ValueError("the key cache is float16")
+    if K.dtype != P.dtype:
+        raise ValueError("K and P must share a dtype")
+    check(lib().spa_kcache_append(K.data_ptr(), P.data_ptr(), cache.data_ptr(), B, H, N, d, m,
+                                  cache.shape[2], int(row0), _dtype_code(K.dtype),
+                                  _stream_ptr(K.device)))
+
+
+def spa_attn_decode_workspace_bytes(B, H, Nq, Nk, dv) -> int:
+    return int(lib().spa_attn_decode_workspace_bytes(B, H, Nq, Nk, dv))
+
+
+def spa_attn_decode(Q, cache, Vc, P, Nk: int, scale: float | None = None, causal: bool = True,
+                    out_dtype=None, return_lse: bool = False, workspace=None):
+    """Nq queries against the first Nk rows of a projected-key cache and a value cache.
+
+    Q [B,H,Nq,d] bf16; cache [B,H,rows,m] float16 (spa_kcache_append); Vc [B,H,rows,dv]
+    bf16; P [H,d,m] bf16. causal: query i sits at position Nk - Nq + i. Returns O
+    [B,H,Nq,dv] (out_dtype float32 by default, or bfloat16), and lse if asked. Runs on the
+    current stream.
+    """
+    torch = _torch()
+    for name, x in (("Q", Q), ("cache", cache), ("Vc", Vc), ("P", P)):
+        _device_tensor(x, name)
+    if Q.dim() != 4 or cache.dim() != 4 or Vc.dim() != 4 or P.dim() != 3:
+        raise ValueError("Q, cache, Vc must be 4-D and P [H,d,m]")
+    B, H, Nq, d = Q.shape
+    rows, m = cache.shape[2], cache.shape[3]
+    dv = Vc.shape[3]
+    if cache.shape[:2] != (B, H) or Vc.shape[:3] != (B, H, rows) or P.shape != (H, d, m):
+        raise ValueError("cache [B,H,rows,m], Vc [B,H,rows,dv] and P [H,d,m] must agree")
+    if cache.dtype != torch.float16:
+        raise ValueError("the key cache is float16")
+    if Q.dtype != Vc.dtype or Q.dtype != P.dtype:
+        raise ValueError("Q, Vc and P must share a dtype")
+    odt = torch.float32 if out_dtype is None else out_dtype
+    O = torch.empty((B, H, Nq, dv), dtype=odt, device=Q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=Q.device) if return_lse else None
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _device_tensor(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().spa_attn_decode(Q.data_ptr(), cache.data_ptr(), Vc.data_ptr(), P.data_ptr(),
+                                float(scale), int(bool(causal)), B, H, Nq, int(Nk), rows, d, m,
+                                dv, _dtype_code(Q.dtype), O.data_ptr(), _dtype_code(odt),
+                                lse.data_ptr() if lse is not None else None, ws_ptr, ws_bytes,
+                                _stream_ptr(Q.device)))
+    return (O, lse) if return_lse else O
 
 
 def profile_begin(max_calls: int) -> None:

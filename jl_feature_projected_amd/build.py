@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libspa.so")
-SOURCES = ["spa_api.cpp", "spa_project.hip", "spa_attn_bf16.hip", "spa_bwd.hip", "spa_f32.hip"]
+SOURCES = ["spa_api.cpp", "spa_project.hip", "spa_attn_bf16.hip", "spa_bwd.hip", "spa_decode.hip",
+           "spa_f32.hip"]
 ARCH = "gfx950"
 
 

@@ -332,6 +332,146 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
     return SPA_OK;
 }
 
+spa_status_t spa_kcache_append(const void* K, const void* P, void* cache, int B, int H, int N,
+                               int d, int m, int rows, int row0, spa_dtype_t dtype,
+                               void* stream) {
+    g_err[0] = '\0';
+    const char* fn = "spa_kcache_append";
+    if (!K || !P || !cache) return fail(SPA_ERR_INVALID_ARGUMENT, "%s: null tensor pointer", fn);
+    spa_status_t st = check_dims(fn, B, H, N, d, m, 1);
+    if (st != SPA_OK) return st;
+    if (row0 < 0 || rows < 1 || (long long)row0 + N > rows || rows > kMaxN)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: rows %d .. %lld outside a cache of %d rows",
+                    fn, row0, (long long)row0 + N, rows);
+    if ((long long)B * H * rows >= kMaxRows)
+        return fail(SPA_ERR_UNSUPPORTED, "%s: B*H*rows exceeds 2^31", fn);
+    if (dtype != SPA_BF16)
+        return fail(SPA_ERR_UNSUPPORTED, "%s: the key cache takes bf16 keys", fn);
+    if ((d != 64 && d != 128) || m > 128)
+        return fail(SPA_ERR_UNSUPPORTED, "%s: needs d in {64,128} and m <= 128 (d=%d m=%d)", fn,
+                    d, m);
+    if (!aligned(K, 16) || !aligned(P, 16) || !aligned(cache, 16))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: tensor base not 16-byte aligned", fn);
+    const Range rk = range(K, (size_t)B * H * N * d * 2), rp = range(P, (size_t)H * d * m * 2),
+                rc = range(cache, (size_t)B * H * rows * m * 2);
+    if (overlap(rc, rk) || overlap(rc, rp))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: the cache overlaps an input", fn);
+    char* first = static_cast<char*>(cache) + (size_t)row0 * m * 2;
+    hipError_t e = spa::launch_project_bf16(K, nullptr, P, first, nullptr, 1, B * H, H, N, d, m,
+                                            m, m, 1.0f, 1.0f, /*out_f16=*/true, nullptr,
+                                            nullptr, nullptr, 0,
+                                            static_cast<hipStream_t>(stream), nullptr, nullptr,
+                                            (long long)rows * m);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return SPA_OK;
+}
+
+size_t spa_attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int dv) {
+    if (B < 1 || H < 1 || Nq < 1 || Nk < Nq || Nk > kMaxN || dv < 1 ||
+        (long long)B * H * Nk >= kMaxRows)
+        return 0;
+    const spa::DecodeSplit sp = spa::decode_split(B * H, Nq, Nk);
+    return (size_t)B * H * Nq * sp.nsplit * ((size_t)dv + 2) * sizeof(float) +
+           (size_t)B * H * Nq * 128 * sizeof(float);
+}
+
+spa_status_t spa_attn_decode(const void* Q, const void* cache, const void* Vc, const void* P,
+                             float scale, int causal, int B, int H, int Nq, int Nk, int rows,
+                             int d, int m, int dv, spa_dtype_t dtype, void* O,
+                             spa_dtype_t o_dtype, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    const char* fn = "spa_attn_decode";
+    if (!Q || !cache || !Vc || !P || !O)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: null tensor pointer", fn);
+    spa_status_t st = check_dims(fn, B, H, Nq, d, m, dv);
+    if (st != SPA_OK) return st;
+    if (Nk < Nq || rows < Nk || rows > kMaxN)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: needs 1 <= Nq <= Nk <= rows (Nq=%d Nk=%d rows=%d)",
+                    fn, Nq, Nk, rows);
+    if ((long long)B * H * rows >= kMaxRows)
+        return fail(SPA_ERR_UNSUPPORTED, "%s: B*H*rows exceeds 2^31", fn);
+    if (causal != 0 && causal != 1)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1, got %d", fn, causal);
+    if (!std::isfinite(scale))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: scale must be finite", fn);
+    if (dtype != SPA_BF16)
+        return fail(SPA_ERR_UNSUPPORTED, "%s: the decode path takes bf16 queries and values", fn);
+    if ((d != 64 && d != 128) || m > 128 || (dv != 64 && dv != 128))
+        return fail(SPA_ERR_UNSUPPORTED, "%s: needs d, dv in {64,128} and m <= 128 (d=%d m=%d dv=%d)",
+                    fn, d, m, dv);
+    if (o_dtype != SPA_F32 && o_dtype != SPA_BF16)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: unknown o_dtype %d", fn, (int)o_dtype);
+    if (!aligned(Q, 16) || !aligned(cache, 16) || !aligned(Vc, 16) || !aligned(P, 16) ||
+        !aligned(O, 16))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: tensor base not 16-byte aligned", fn);
+    if (lse && !aligned(lse, 4))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: lse not 4-byte aligned", fn);
+    if (workspace && !aligned(workspace, 16))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace not 16-byte aligned", fn);
+    const size_t need = spa_attn_decode_workspace_bytes(B, H, Nq, Nk, dv);
+    if (workspace && workspace_bytes < need)
+        return fail(SPA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn,
+                    workspace_bytes, need);
+    const long long bh = (long long)B * H;
+    const Range ro = range(O, (size_t)bh * Nq * dv * elem_size(o_dtype));
+    const Range ins[4] = {range(Q, (size_t)bh * Nq * d * 2), range(cache, (size_t)bh * rows * m * 2),
+                          range(Vc, (size_t)bh * rows * dv * 2), range(P, (size_t)H * d * m * 2)};
+    const Range rl = lse ? range(lse, (size_t)bh * Nq * sizeof(float)) : Range{0, 0};
+    for (const Range& r : ins) {
+        if (overlap(ro, r)) return fail(SPA_ERR_INVALID_ARGUMENT, "%s: O overlaps an input", fn);
+        if (lse && overlap(rl, r))
+            return fail(SPA_ERR_INVALID_ARGUMENT, "%s: lse overlaps an input", fn);
+    }
+    if (lse && overlap(rl, ro)) return fail(SPA_ERR_INVALID_ARGUMENT, "%s: lse overlaps O", fn);
+    if (workspace) {
+        const Range rw = range(workspace, need);
+        if (overlap(rw, ro) || (lse && overlap(rw, rl)))
+            return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace overlaps an output", fn);
+        for (const Range& r : ins)
+            if (overlap(rw, r))
+                return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace overlaps an input", fn);
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    if (!ws) {
+        hipError_t e = hipMallocAsync(&ws, need, s);
+        if (e != hipSuccess) return hip_fail("spa_attn_decode: hipMallocAsync", e);
+    }
+    const spa::DecodeSplit sp = spa::decode_split(B * H, Nq, Nk);
+    spa::DecodeArgs a;
+    a.Q = static_cast<const uint16_t*>(Q);
+    a.Kc = static_cast<const uint16_t*>(cache);
+    a.Vc = static_cast<const uint16_t*>(Vc);
+    a.P = static_cast<const uint16_t*>(P);
+    a.O = O;
+    a.lse = lse;
+    a.partO = static_cast<float*>(ws);
+    a.partML = static_cast<float*>(ws) + (size_t)bh * Nq * sp.nsplit * dv;
+    a.qt = a.partML + (size_t)bh * Nq * sp.nsplit * 2;
+    a.qscale = scale * 1.44269504088896340736f;
+    a.causal = causal;
+    a.BH = B * H;
+    a.H = H;
+    a.Nq = Nq;
+    a.Nk = Nk;
+    a.rows = rows;
+    a.d = d;
+    a.m = m;
+    a.dv = dv;
+    a.o_f32 = o_dtype == SPA_F32;
+    a.nsplit = sp.nsplit;
+    a.chunk = sp.chunk;
+    hipError_t e = spa::launch_decode_bf16(a, s);
+    if (!workspace) {
+        hipError_t e2 = hipFreeAsync(ws, s);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return SPA_OK;
+}
+
 size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
                                     spa_dtype_t dtype) {
     if (B < 1 || H < 1 || N < 1 || N > kMaxN || (long long)B * H * N >= kMaxRows) return 0;

@@ -52,13 +52,6 @@ struct Flag {
 // Byte offset that is out of range for every tile resource below (loads read zero).
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// Raw buffer resource over max(bytes, 0) bytes from `base`: loads at offsets past the end
-// return zero instead of touching memory. base and bytes must be wave-uniform.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, max(bytes, 0),
-                                             0x00020000);
-}
-
 // fp32 score-layout values (slots 8*half + j of k-step tt) -> packed pairs
 template <bool F16>
 __device__ __forceinline__ u32x4 pack_kstep(const f32x16& x, int tt) {

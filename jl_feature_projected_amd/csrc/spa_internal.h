@@ -24,7 +24,7 @@ __host__ __device__ inline int vt_padded_keys(int N) { return (N + kVtTileKeys -
 // Y_z[bh, n, c] = out_scale_z * sum_k X_z[bh, n, k] P[h, k, c] for z < nz (nz = 1 or 2,
 // e.g. queries and keys), accumulated in fp32 and rounded once to fp16 (out_f16) or bf16.
 // P is [H, d, m]; columns m <= c < out_cols are written as zeros. Output rows are out_stride
-// elements apart. If kmax is not null, kmax[bh * proj_blocks(N) + b] receives the largest
+// elements apart, heads out_head_stride (default N * out_stride). If kmax is not null, kmax[bh * proj_blocks(N) + b] receives the largest
 // row norm (fp32, before rounding) of Y1 over tokens b*256 .. b*256+255 of head bh. If Vt is
 // not null, the same launch writes V^T of V ([BH, N, dv] bf16) in the layout above. If Yt0
 // (Yt1) is not null, Y0 (Y1) is also written transposed, [BH, out_cols, vt_padded_keys(N)],
@@ -34,7 +34,7 @@ hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, vo
                                int out_stride, int out_cols, float out_scale0,
                                float out_scale1, bool out_f16, float* kmax, const void* V,
                                void* Vt, int dv, hipStream_t stream, void* Yt0 = nullptr,
-                               void* Yt1 = nullptr);
+                               void* Yt1 = nullptr, long long out_head_stride = -1);
 
 // Attention over projected inputs. Qt and Kt are fp16 [BH, N, mp] with zero columns past m
 // (score MFMA in fp16); Qt is pre-scaled by scale*log2(e) so the scores come out in base-2
@@ -86,5 +86,26 @@ hipError_t launch_project_f32(const float* X, const float* P, float* Y, int BH, 
 hipError_t launch_attn_f32(const float* Qt, const float* Kt, const float* V, float* O,
                            float* lse, int BH, int N, int m, int dv, bool causal, float scale,
                            hipStream_t stream);
+
+// Decode: Nq queries against a cache of Nk projected keys (fp16) and values (bf16) with
+// `rows` rows per head; partial results per (query, key split) in fp32.
+struct DecodeArgs {
+    const uint16_t* Q;   // bf16 [BH, Nq, d]
+    const uint16_t* Kc;  // fp16 [BH, rows, m]
+    const uint16_t* Vc;  // bf16 [BH, rows, dv]
+    const uint16_t* P;   // bf16 [H, d, m]
+    void* O;             // [BH, Nq, dv], fp32 or bf16
+    float* lse;          // [BH, Nq] or null
+    float* partO;        // [BH, Nq, nsplit, dv]
+    float* partML;       // [BH, Nq, nsplit, 2]: running max (base 2), sum
+    float* qt;           // [BH, Nq, m]: projected queries times qscale
+    float qscale;        // scale * log2(e)
+    int causal, BH, H, Nq, Nk, rows, d, m, dv, o_f32, nsplit, chunk;
+};
+struct DecodeSplit {
+    int nsplit, chunk;  // key splits per (head, query group) and keys per split
+};
+DecodeSplit decode_split(int BH, int Nq, int Nk);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace spa

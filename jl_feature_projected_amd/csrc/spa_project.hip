@@ -54,6 +54,7 @@ struct PrepArgs {
     uint16_t* Yt1;      // permuted within 16-groups as in Vt
     float* kmax;
     int N, BH, H, m, out_stride, out_cols, nz, nroles, Np;
+    long long out_head_stride;  // elements between heads of Y0 / Y1
     float scale0, scale1;
 };
 
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(kProjThreads) void prep_bf16_kernel(PrepArgs a) {
     }
     __syncthreads();
 
-    uint16_t* Yh = Y + (size_t)bh * a.N * a.out_stride;
+    uint16_t* Yh = Y + (size_t)bh * a.out_head_stride;
     const bool vec_store = (a.out_stride % 4) == 0;
     const bool want_norm = a.kmax != nullptr && z == 1;
     float norm2_max = 0.0f;  // largest squared row norm among this lane's tokens
@@ -305,7 +306,8 @@ hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, vo
                                void* Y1, int nz, int BH, int H, int N, int d, int m,
                                int out_stride, int out_cols, float out_scale0,
                                float out_scale1, bool out_f16, float* kmax, const void* V,
-                               void* Vt, int dv, hipStream_t stream, void* Yt0, void* Yt1) {
+                               void* Vt, int dv, hipStream_t stream, void* Yt0, void* Yt1,
+                               long long out_head_stride) {
     PrepArgs a;
     a.Yt0 = static_cast<uint16_t*>(Yt0);
     a.Yt1 = static_cast<uint16_t*>(Yt1);
@@ -323,6 +325,7 @@ hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, vo
     a.m = m;
     a.out_stride = out_stride;
     a.out_cols = out_cols;
+    a.out_head_stride = out_head_stride < 0 ? (long long)N * out_stride : out_head_stride;
     a.nz = nz;
     a.nroles = nz + (Vt ? 1 : 0);
     a.Np = vt_padded_keys(N);

@@ -161,6 +161,33 @@ def attn_rows(Q, K, V, P, scale: float, causal: bool, row_bh, row_i, with_lse: b
     return (O, lse) if with_lse else O
 
 
+def attn_decode(Q, K, V, P, scale: float, causal: bool, with_lse: bool = False,
+                nthreads: int = 0):
+    """Nq queries against Nk keys, Q [B,H,Nq,d], K [B,H,Nk,d], V [B,H,Nk,dv], Nq <= Nk.
+
+    Reading of a rectangular causal mask (no page defines one): the queries are the last Nq
+    positions of the sequence, query i at position Nk - Nq + i, seeing keys j <= Nk - Nq + i,
+    so the result is rows Nk - Nq .. Nk - 1 of the square forward above. Computed that way:
+    the queries are placed in those rows of an otherwise zero [B,H,Nk,d] query tensor and
+    only those rows are evaluated (attn_rows). Returns O [B,H,Nq,dv] (and lse [B,H,Nq]).
+    """
+    Q, K = _f64(Q), _f64(K)
+    B, H, Nq, d = Q.shape
+    Nk = K.shape[2]
+    if K.shape[:2] != (B, H) or K.shape[3] != d or Nq > Nk:
+        raise ValueError("Q [B,H,Nq,d] and K [B,H,Nk,d] with Nq <= Nk")
+    Qfull = np.zeros((B, H, Nk, d))
+    Qfull[:, :, Nk - Nq:] = Q
+    rb = np.repeat(np.arange(B * H, dtype=np.int64), Nq)
+    ri = np.tile(np.arange(Nk - Nq, Nk, dtype=np.int64), B * H)
+    out = attn_rows(Qfull, K, V, P, scale, causal, rb, ri, with_lse=with_lse,
+                    nthreads=nthreads)
+    dv = _f64(V).shape[3]
+    if with_lse:
+        return out[0].reshape(B, H, Nq, dv), out[1].reshape(B, H, Nq)
+    return out.reshape(B, H, Nq, dv)
+
+
 def _matrix(fn_name: str, Q, K, P, scale: float, causal: bool, nthreads: int) -> np.ndarray:
     Q, K, P = _f64(Q), _f64(K), _f64(P)
     B, H, N, d = Q.shape

@@ -170,3 +170,66 @@ def test_bwd_workspace_bytes(L):
     assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, m, dv, spa.SPA_BF16) == sum(a256(s) for s in sizes)
     assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, 65, dv, spa.SPA_BF16) == 0
     assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, m, dv, spa.SPA_F32) == 0
+
+
+def _decode(L, **kw):
+    a = dict(Q=A, cache=B_, Vc=C, P=D, scale=0.125, causal=1, B=1, H=2, Nq=1, Nk=4096,
+             rows=8192, d=128, m=32, dv=128, dtype=spa.SPA_BF16, O=E, o_dtype=spa.SPA_F32,
+             lse=None, ws=F, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return L.spa_attn_decode(a["Q"], a["cache"], a["Vc"], a["P"], a["scale"], a["causal"],
+                             a["B"], a["H"], a["Nq"], a["Nk"], a["rows"], a["d"], a["m"],
+                             a["dv"], a["dtype"], a["O"], a["o_dtype"], a["lse"], a["ws"],
+                             a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(cache=None), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(Nq=0), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(Nq=5000), spa.SPA_ERR_INVALID_ARGUMENT),          # Nq > Nk
+    (dict(Nk=9000), spa.SPA_ERR_INVALID_ARGUMENT),          # Nk > rows
+    (dict(causal=2), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=spa.SPA_F32), spa.SPA_ERR_UNSUPPORTED),
+    (dict(d=96), spa.SPA_ERR_UNSUPPORTED),
+    (dict(m=129), spa.SPA_ERR_UNSUPPORTED),
+    (dict(dv=96), spa.SPA_ERR_UNSUPPORTED),
+    (dict(o_dtype=7), spa.SPA_ERR_INVALID_ARGUMENT),
+    (dict(Q=A + 8), spa.SPA_ERR_INVALID_ARGUMENT),          # misaligned
+    (dict(O=B_), spa.SPA_ERR_INVALID_ARGUMENT),             # O overlaps the cache
+    (dict(ws_bytes=16), spa.SPA_ERR_WORKSPACE),
+    (dict(ws=E), spa.SPA_ERR_INVALID_ARGUMENT),             # workspace overlaps O
+])
+def test_attn_decode_rejects_on_host(L, kw, code):
+    assert _decode(L, **kw) == code
+    assert len(L.spa_last_error()) > 0
+
+
+def test_kcache_append_rejects_on_host(L):
+    ok = dict(K=A, P=B_, cache=C, B=1, H=2, N=16, d=128, m=32, rows=64, row0=0,
+              dtype=spa.SPA_BF16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.spa_kcache_append(a["K"], a["P"], a["cache"], a["B"], a["H"], a["N"], a["d"],
+                                   a["m"], a["rows"], a["row0"], a["dtype"], None)
+    for kw, code in ((dict(K=None), spa.SPA_ERR_INVALID_ARGUMENT),
+                     (dict(row0=49), spa.SPA_ERR_INVALID_ARGUMENT),   # past the cache end
+                     (dict(row0=-1), spa.SPA_ERR_INVALID_ARGUMENT),
+                     (dict(dtype=spa.SPA_F32), spa.SPA_ERR_UNSUPPORTED),
+                     (dict(d=32), spa.SPA_ERR_UNSUPPORTED),
+                     (dict(m=200), spa.SPA_ERR_UNSUPPORTED),
+                     (dict(cache=A), spa.SPA_ERR_INVALID_ARGUMENT),   # overlaps K
+                     (dict(P=B_ + 4), spa.SPA_ERR_INVALID_ARGUMENT)):
+        assert call(**kw) == code, kw
+
+
+def test_decode_workspace_bytes(L):
+    # B*H*Nq*nsplit*(dv+2) floats; nsplit from the split rule (about 1024 workgroups, at
+    # least 256 keys per split): 32 heads, one query, 32768 keys -> 32 splits of 1024 keys
+    # plus 128 floats per query for its projection
+    assert L.spa_attn_decode_workspace_bytes(1, 32, 1, 32768, 128) == 32 * 1 * 32 * 130 * 4 + 32 * 128 * 4
+    assert L.spa_attn_decode_workspace_bytes(1, 1, 1, 100, 64) == 1 * 1 * 1 * 66 * 4 + 128 * 4
+    assert L.spa_attn_decode_workspace_bytes(1, 2, 17, 16, 128) == 0  # Nq > Nk
