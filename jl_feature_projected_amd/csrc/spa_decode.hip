@@ -7,9 +7,8 @@
 // The causal mask is aligned to the end of the cache: query i (of Nq) sits at position
 // Nk - Nq + i and sees keys j <= Nk - Nq + i.
 //
-// decode_qproj_kernel: the queries' projections, fp32, times scale*log2 e (one workgroup
-//   per head and group of up to 16 queries; Q rows and P staged in LDS).
 // decode_attn_kernel: one workgroup per (head, group of up to QN queries, key split). It
+//   projects its queries (fp32, times scale*log2 e; Q rows and P staged in LDS), then
 //   streams its split of the cache in blocks of 256 keys: one key per thread for the
 //   scores, an exact online softmax per query (running max and sum in base-2 units), and
 //   the weights times V with fp32 FMAs, each thread owning COLS columns of V (16-byte row
@@ -27,61 +26,32 @@ constexpr int kDecThreads = 256;
 constexpr int kDecKeys = 256;  // keys per block: one per thread in the score phase
 constexpr int kDecMaxM = 128;
 
-// qt[bh, q, c] = qscale * sum_k Q[bh, q, k] P[h, k, c]: a workgroup per (head, 16 queries);
-// 8 threads per output, each summing d/8 products, then a shuffle reduction.
-constexpr int kQprojQ = 16;
-__global__ __launch_bounds__(kDecThreads) void decode_qproj_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ P, float qscale, int H,
-    int Nq, int d, int m, int nqb, float* __restrict__ qt) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t sm16[];
-    uint16_t* Ps = sm16;           // [d][m]
-    uint16_t* Qs = sm16 + d * m;   // [kQprojQ][d]
-    const int bh = blockIdx.x / nqb;
-    const int q0 = (blockIdx.x - bh * nqb) * kQprojQ;
-    const int nq = min(kQprojQ, Nq - q0);
-    const int h = bh % H;
-    const int tid = threadIdx.x;
-    const uint16_t* Ph = P + (size_t)h * d * m;
-    for (int i = tid; i < d * m; i += kDecThreads) Ps[i] = Ph[i];
-    const uint16_t* Qh = Q + ((size_t)bh * Nq + q0) * d;
-    for (int i = tid; i < nq * d; i += kDecThreads) Qs[i] = Qh[i];
-    __syncthreads();
-    const int slice = tid & 7, per = d / 8;
-    for (int o0 = 0; o0 < nq * m; o0 += kDecThreads / 8) {
-        const int o = o0 + (tid >> 3);
-        const int q = o / m, c = o - q * m;
-        float acc = 0.0f;
-        if (o < nq * m) {
-            for (int k = slice * per; k < slice * per + per; ++k)
-                acc += __uint_as_float((uint32_t)Qs[q * d + k] << 16) *
-                       __uint_as_float((uint32_t)Ps[k * m + c] << 16);
-        }
-        acc += __shfl_xor(acc, 1, 8);
-        acc += __shfl_xor(acc, 2, 8);
-        acc += __shfl_xor(acc, 4, 8);
-        if (slice == 0 && o < nq * m) qt[((size_t)bh * Nq + q0) * m + o] = acc * qscale;
-    }
-}
-
 template <int DV, int QN>
 __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
-    const float* __restrict__ Qt, const uint16_t* __restrict__ Kc,
-    const uint16_t* __restrict__ Vc, int causal, int Nq, int Nk, int rows, int m, int nqg,
-    int nsplit, int chunk, float* __restrict__ partO, float* __restrict__ partML) {
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
+    const uint16_t* __restrict__ Vc, const uint16_t* __restrict__ P, float qscale, int causal,
+    int H, int Nq, int Nk, int rows, int d, int m, int nqg, int nsplit, int chunk,
+    float* __restrict__ partO, float* __restrict__ partML) {
     constexpr int COLS = QN <= 4 ? 8 : 2;    // V columns per thread
     constexpr int CT = DV / COLS;            // threads per V row
     constexpr int KG = kDecThreads / CT;     // key groups
     constexpr int KPG = kDecKeys / KG;       // keys per group per block
     static_assert(KPG % 4 == 0, "weights are read four keys at a time");
-    __shared__ __attribute__((aligned(16))) float qt[QN][kDecMaxM];  // projected queries
-    __shared__ __attribute__((aligned(16))) float S[QN][kDecKeys];   // scores, then weights
+    // LDS (dynamic, decode_lds_bytes): the projected queries [QN][kDecMaxM], then either the
+    // projection's staging (P [d][m] and the Q rows [QN][d], bf16) or the score / weight tile
+    // [QN][kDecKeys] followed by the key groups' partial outputs [KG][QN][DV].
+    extern __shared__ __attribute__((aligned(16))) char dsm[];
+    float(*qt)[kDecMaxM] = reinterpret_cast<float(*)[kDecMaxM]>(dsm);
+    char* un = dsm + QN * kDecMaxM * sizeof(float);
+    float(*S)[kDecKeys] = reinterpret_cast<float(*)[kDecKeys]>(un);
+    float(*red)[QN][DV] = reinterpret_cast<float(*)[QN][DV]>(un + QN * kDecKeys * sizeof(float));
     __shared__ float Mrun[QN], Lrun[QN], alpha[QN];
-    __shared__ __attribute__((aligned(16))) float red[KG][QN][DV];
 
     const int sp = blockIdx.x % nsplit;
     const int rest = blockIdx.x / nsplit;
     const int qg = rest % nqg;
     const int bh = rest / nqg;
+    const int h = bh % H;
     const int q0 = qg * QN;
     const int nq = min(QN, Nq - q0);
     const int kbeg = sp * chunk;
@@ -90,10 +60,33 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     const int ct = tid % CT, kgi = tid / CT;
     const int last = Nk - Nq + q0;  // absolute position of query q0 (causal limit)
 
-    // projected queries (zero rows past nq)
-    for (int i = tid; i < QN * m; i += kDecThreads) {
-        const int q = i / m, c = i - q * m;
-        qt[q][c] = q < nq ? Qt[((size_t)bh * Nq + q0 + q) * m + c] : 0.0f;
+    // projected queries (zero rows past nq): Q rows and P staged in LDS (in the space of the
+    // score tile and of the final reduction, not yet in use), then 8 threads per output,
+    // each summing d/8 products, and a shuffle reduction
+    {
+        uint16_t* Ps = reinterpret_cast<uint16_t*>(un);  // [d][m]
+        uint16_t* Qs = Ps + d * m;                         // [QN][d]
+        const uint16_t* Ph = P + (size_t)h * d * m;
+        for (int i = tid; i < d * m; i += kDecThreads) Ps[i] = Ph[i];
+        const uint16_t* Qh = Q + ((size_t)bh * Nq + q0) * d;
+        for (int i = tid; i < nq * d; i += kDecThreads) Qs[i] = Qh[i];
+        __syncthreads();
+        const int slice = tid & 7, per = d / 8;
+        for (int o0 = 0; o0 < QN * m; o0 += kDecThreads / 8) {
+            const int o = o0 + (tid >> 3);
+            const int q = o / m, c = o - q * m;
+            float a = 0.0f;
+            if (o < nq * m) {
+                for (int k = slice * per; k < slice * per + per; ++k)
+                    a += __uint_as_float((uint32_t)Qs[q * d + k] << 16) *
+                         __uint_as_float((uint32_t)Ps[k * m + c] << 16);
+            }
+            a += __shfl_xor(a, 1, 8);
+            a += __shfl_xor(a, 2, 8);
+            a += __shfl_xor(a, 4, 8);
+            if (slice == 0 && o < QN * m) qt[q][c] = a * qscale;
+        }
+        __syncthreads();  // the staging space is reused below
     }
     if (tid < QN) {
         Mrun[tid] = -INFINITY;
@@ -241,23 +234,46 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     }
 }
 
-// One workgroup of DV threads per (head, query): the splits merged in order.
+// One workgroup of DV threads per (head, query): the splits merged in split order. The
+// per-split maxima and sums are loaded by all threads at once and their weights staged in
+// LDS, so only the DV-wide partial outputs are read in the (unrolled) loop.
+constexpr int kCombineMaxSplits = 1024;
 template <int DV>
 __global__ __launch_bounds__(DV) void decode_combine_kernel(
     const float* __restrict__ partO, const float* __restrict__ partML, void* __restrict__ O,
     int o_f32, float* __restrict__ lse, int nsplit) {
+    __shared__ float wsp[kCombineMaxSplits];
+    __shared__ float wmax[DV / 64], wsum[DV / 64];
     const size_t row = blockIdx.x;
-    const int c = threadIdx.x;
+    const int c = threadIdx.x, wave = c >> 6, lane = c & 63;
     const float* ml = partML + row * nsplit * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.0f, o = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
+    float mx = -INFINITY;
+    for (int s = c; s < nsplit; s += DV) mx = fmaxf(mx, ml[2 * s]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) wmax[wave] = mx;
+    __syncthreads();
+    float M = wmax[0];
+#pragma unroll
+    for (int w = 1; w < DV / 64; ++w) M = fmaxf(M, wmax[w]);
+    float ls = 0.0f;
+    for (int s = c; s < nsplit; s += DV) {
         const float ms = ml[2 * s];
         const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-        L += w * ml[2 * s + 1];
-        o += w * partO[(row * nsplit + s) * DV + c];
+        wsp[s] = w;
+        ls += w * ml[2 * s + 1];
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o, 64);
+    if (lane == 0) wsum[wave] = ls;
+    __syncthreads();
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < DV / 64; ++w) L += wsum[w];
+    const float* po = partO + row * nsplit * DV + c;
+    float o = 0.0f;
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s) o += wsp[s] * po[(size_t)s * DV];
     o /= L;
     if (o_f32)
         static_cast<float*>(O)[row * DV + c] = o;
@@ -267,21 +283,24 @@ __global__ __launch_bounds__(DV) void decode_combine_kernel(
 }
 
 template <int DV, int QN>
+size_t decode_lds_bytes(int d, int m) {
+    constexpr int COLS = QN <= 4 ? 8 : 2;
+    constexpr int KG = kDecThreads / (DV / COLS);
+    const size_t main = sizeof(float) * ((size_t)QN * kDecKeys + (size_t)KG * QN * DV);
+    const size_t stage = sizeof(uint16_t) * ((size_t)d * m + (size_t)QN * d);
+    return sizeof(float) * QN * kDecMaxM + (main > stage ? main : stage);
+}
+
+template <int DV, int QN>
 hipError_t launch_qn(const DecodeArgs& a, hipStream_t s) {
     const int nqg = (a.Nq + QN - 1) / QN;
     const long long grid = (long long)a.BH * nqg * a.nsplit;
-    const int nqb = (a.Nq + kQprojQ - 1) / kQprojQ;
-    if (grid > 0x7fffffffLL || (long long)a.BH * nqb > 0x7fffffffLL)
-        return hipErrorInvalidConfiguration;
-    const size_t sm = sizeof(uint16_t) * ((size_t)a.d * a.m + (size_t)kQprojQ * a.d);
-    decode_qproj_kernel<<<dim3((unsigned)(a.BH * nqb)), kDecThreads, sm, s>>>(
-        a.Q, a.P, a.qscale, a.H, a.Nq, a.d, a.m, nqb, a.qt);
+    if (grid > 0x7fffffffLL || a.nsplit > kCombineMaxSplits) return hipErrorInvalidConfiguration;
+    const size_t lds = decode_lds_bytes<DV, QN>(a.d, a.m);
+    decode_attn_kernel<DV, QN><<<dim3((unsigned)grid), kDecThreads, lds, s>>>(
+        a.Q, a.Kc, a.Vc, a.P, a.qscale, a.causal, a.H, a.Nq, a.Nk, a.rows, a.d, a.m, nqg,
+        a.nsplit, a.chunk, a.partO, a.partML);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    decode_attn_kernel<DV, QN><<<dim3((unsigned)grid), kDecThreads, 0, s>>>(
-        a.qt, a.Kc, a.Vc, a.causal, a.Nq, a.Nk, a.rows, a.m, nqg, a.nsplit, a.chunk, a.partO,
-        a.partML);
-    e = hipGetLastError();
     if (e != hipSuccess) return e;
     decode_combine_kernel<DV><<<dim3((unsigned)((long long)a.BH * a.Nq)), DV, 0, s>>>(
         a.partO, a.partML, a.O, a.o_f32, a.lse, a.nsplit);
