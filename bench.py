@@ -164,6 +164,37 @@ def time_decode(w, x, P, steps, warmup, dev) -> dict:
             "k_cache_vs_k_bytes": round(w.m / w.d, 4), "queries_per_head": 1}
 
 
+def time_sfa(w, Q, K, V, topk, steps, warmup, dev) -> dict:
+    """spa_sfa_fwd on the workload's Q, K, V with topk features per row, timed between
+    events on the launch stream. Its attention kernel runs the score MFMA over all d
+    features (the zeros included), so the rate is quoted on c N^2 (2d + 2dv) flops per head."""
+    O = torch.empty((w.B, w.H, w.N, w.dv), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(spa.spa_sfa_fwd_workspace_bytes(w.B, w.H, w.N, w.d, w.dv),
+                     dtype=torch.uint8, device=dev)
+
+    def sstep():
+        spa.spa_sfa_fwd(Q, K, V, topk, w.scale, w.causal, out_dtype=torch.bfloat16,
+                        workspace=ws)
+
+    for _ in range(warmup):
+        sstep()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        sstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    c = 0.5 if w.causal else 1.0
+    flops = c * w.N * w.N * (2 * w.d + 2 * w.dv) * w.B * w.H
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"topk": topk, "ms_per_call": round(ms, 5), "value": round(tf, 3), "unit": "TFLOP/s",
+            "pct_of_bf16_peak": round(100.0 * tf / accounting.PEAK_BF16_DENSE_TFLOPS, 2),
+            "flops_per_call": flops}
+
+
 def calibrate_copy(dev) -> None:
     n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -187,6 +218,9 @@ def main() -> int:
     ap.add_argument("--decode", action="store_true",
                     help="also time one decode step (spa_attn_decode, one query per head "
                          "against the whole cache) and report it in a 'decode' object")
+    ap.add_argument("--sfa", type=int, default=0, metavar="K",
+                    help="also time sparse feature attention (spa_sfa_fwd) with K features "
+                         "per row and report it in an 'sfa' object")
     ap.add_argument("--backward", action="store_true",
                     help="also time spa_attn_bwd (bf16 workloads) and report it in a "
                          "'backward' object")
@@ -289,6 +323,8 @@ def main() -> int:
     }
     if args.backward and w.dtype == "bf16":
         res["backward"] = time_backward(w, x, Q, K, V, P, args.steps, args.warmup, dev)
+    if args.sfa and w.dtype == "bf16":
+        res["sfa"] = time_sfa(w, Q, K, V, args.sfa, args.steps, args.warmup, dev)
     if args.decode and w.dtype == "bf16":
         res["decode"] = time_decode(w, x, P, args.steps, args.warmup, dev)
     if not args.no_cpu_baseline:

@@ -166,6 +166,33 @@ spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const voi
                           void* stream);
 
 /*
+ * spa_sfa_fwd_workspace_bytes -- workspace bytes for spa_sfa_fwd (selected queries and keys,
+ * fp16 [B,H,N,d] each; key-norm maxima; V^T), 0 if the shape is invalid or unsupported.
+ */
+size_t spa_sfa_fwd_workspace_bytes(int B, int H, int N, int d, int dv);
+
+/*
+ * spa_sfa_fwd -- sparse feature attention ("Scaling Attention via Feature Sparsity", key
+ * designs 1 and 3): every row of Q and K keeps its topk features of largest magnitude
+ * (ties: lower feature index first), the rest set to zero, and
+ *
+ *   O = softmax(scale * Topk(Q) Topk(K)^T [+ causal mask]) V       (exact)
+ *
+ *   Q, K   [B,H,N,d] bf16 (dtype SPA_BF16), d in {64, 128}; V [B,H,N,dv] bf16, dv in
+ *          {64, 128}; 1 <= topk <= d.
+ *   O, o_dtype, lse, workspace, workspace_bytes, stream: as for spa_attn_fwd (workspace
+ *          sized by spa_sfa_fwd_workspace_bytes).
+ *
+ * Three launches: the Top-k selection (fp16 operands, queries times scale*log2 e), the V
+ * transpose, and the streamed attention kernel of spa_attn_fwd with m = d. Errors as for
+ * spa_attn_fwd; topk outside [1, d] is SPA_ERR_INVALID_ARGUMENT.
+ */
+spa_status_t spa_sfa_fwd(const void* Q, const void* K, const void* V, int topk, float scale,
+                         int causal, int B, int H, int N, int d, int dv, spa_dtype_t dtype,
+                         void* O, spa_dtype_t o_dtype, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * spa_kcache_append -- write projected keys into a key cache (SPA page Sec. 3.1.2: keys
  * enter the scores only through Kt = K P, so a cache of Kt serves every later query):
  *

@@ -27,7 +27,7 @@ SPA_BF16 = 1
 
 EXPORTS = ("spa_version", "spa_status_string", "spa_last_error", "spa_project",
            "spa_attn_fwd_workspace_bytes", "spa_attn_fwd", "spa_attn_bwd_workspace_bytes",
-           "spa_attn_bwd", "spa_kcache_append", "spa_attn_decode_workspace_bytes",
+           "spa_attn_bwd", "spa_sfa_fwd_workspace_bytes", "spa_sfa_fwd", "spa_kcache_append", "spa_attn_decode_workspace_bytes",
            "spa_attn_decode", "spa_profile_begin", "spa_profile_end")
 
 
@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
     L.spa_attn_bwd.restype = st
     L.spa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, vp, vp,
                                vp, vp, i, vp, z, vp]
+    L.spa_sfa_fwd_workspace_bytes.restype = z
+    L.spa_sfa_fwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.spa_sfa_fwd.restype = st
+    L.spa_sfa_fwd.argtypes = [vp, vp, vp, i, f, i, i, i, i, i, i, i, vp, i, vp, vp, z, vp]
     L.spa_kcache_append.restype = st
     L.spa_kcache_append.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, vp]
     L.spa_attn_decode_workspace_bytes.restype = z
@@ -235,6 +239,37 @@ def spa_attn_bwd(Q, K, V, P, O, dO, lse, scale: float | None = None, causal: boo
                              dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), dP.data_ptr(),
                              _dtype_code(gdt), ws_ptr, ws_bytes, _stream_ptr(Q.device)))
     return dQ, dK, dV, dP
+
+
+def spa_sfa_fwd(Q, K, V, topk: int, scale: float | None = None, causal: bool = False,
+                out_dtype=None, return_lse: bool = False, workspace=None):
+    """Sparse feature attention: softmax(scale Topk(Q) Topk(K)^T [+causal]) V on the
+    current stream. Q, K [B,H,N,d] and V [B,H,N,dv] bf16; returns O [B,H,N,dv] (float32 by
+    default, or out_dtype) and lse [B,H,N] if asked."""
+    torch = _torch()
+    for name, x in (("Q", Q), ("K", K), ("V", V)):
+        _device_tensor(x, name)
+    if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3]:
+        raise ValueError("Q, K must be [B,H,N,d] and V [B,H,N,dv]")
+    B, H, N, d = Q.shape
+    dv = V.shape[3]
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise ValueError("Q, K and V must share a dtype")
+    odt = torch.float32 if out_dtype is None else out_dtype
+    O = torch.empty((B, H, N, dv), dtype=odt, device=Q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=Q.device) if return_lse else None
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _device_tensor(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    check(lib().spa_sfa_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), int(topk), float(scale),
+                            int(bool(causal)), B, H, N, d, dv, _dtype_code(Q.dtype),
+                            O.data_ptr(), _dtype_code(odt),
+                            lse.data_ptr() if lse is not None else None, ws_ptr, ws_bytes,
+                            _stream_ptr(Q.device)))
+    return (O, lse) if return_lse else O
 
 
 def spa_kcache_append(K, P, cache, row0: int) -> None:

@@ -472,6 +472,93 @@ spa_status_t spa_attn_decode(const void* Q, const void* cache, const void* Vc, c
     return SPA_OK;
 }
 
+size_t spa_sfa_fwd_workspace_bytes(int B, int H, int N, int d, int dv) {
+    if (check_dims("spa_sfa_fwd_workspace_bytes", B, H, N, d, d, dv) != SPA_OK ||
+        (d != 64 && d != 128) || (dv != 64 && dv != 128)) {
+        g_err[0] = '\0';
+        return 0;
+    }
+    return workspace_layout(B * H, N, d, dv, SPA_BF16).total;
+}
+
+spa_status_t spa_sfa_fwd(const void* Q, const void* K, const void* V, int topk, float scale,
+                         int causal, int B, int H, int N, int d, int dv, spa_dtype_t dtype,
+                         void* O, spa_dtype_t o_dtype, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    const char* fn = "spa_sfa_fwd";
+    if (!Q || !K || !V || !O) return fail(SPA_ERR_INVALID_ARGUMENT, "%s: null tensor pointer", fn);
+    spa_status_t st = check_dims(fn, B, H, N, d, d, dv);
+    if (st != SPA_OK) return st;
+    if (topk < 1 || topk > d)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: topk must be in [1, d], got %d", fn, topk);
+    if (causal != 0 && causal != 1)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1, got %d", fn, causal);
+    if (!std::isfinite(scale))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: scale must be finite", fn);
+    if (dtype != SPA_BF16)
+        return fail(SPA_ERR_UNSUPPORTED, "%s: sparse feature attention takes bf16 inputs", fn);
+    if ((d != 64 && d != 128) || (dv != 64 && dv != 128))
+        return fail(SPA_ERR_UNSUPPORTED, "%s: needs d, dv in {64,128} (d=%d dv=%d)", fn, d, dv);
+    if (o_dtype != SPA_F32 && o_dtype != SPA_BF16)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: unknown o_dtype %d", fn, (int)o_dtype);
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: tensor base not 16-byte aligned", fn);
+    if (lse && !aligned(lse, 4))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: lse not 4-byte aligned", fn);
+    if (workspace && !aligned(workspace, 16))
+        return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace not 16-byte aligned", fn);
+    const WorkspaceLayout wl = workspace_layout(B * H, N, d, dv, SPA_BF16);
+    if (workspace && workspace_bytes < wl.total)
+        return fail(SPA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn,
+                    workspace_bytes, wl.total);
+    const long long rows = (long long)B * H * N;
+    const Range ro = range(O, rows * dv * elem_size(o_dtype));
+    const Range ins[3] = {range(Q, rows * d * 2), range(K, rows * d * 2), range(V, rows * dv * 2)};
+    const Range rl = lse ? range(lse, rows * sizeof(float)) : Range{0, 0};
+    for (const Range& r : ins) {
+        if (overlap(ro, r)) return fail(SPA_ERR_INVALID_ARGUMENT, "%s: O overlaps an input", fn);
+        if (lse && overlap(rl, r))
+            return fail(SPA_ERR_INVALID_ARGUMENT, "%s: lse overlaps an input", fn);
+    }
+    if (lse && overlap(rl, ro)) return fail(SPA_ERR_INVALID_ARGUMENT, "%s: lse overlaps O", fn);
+    if (workspace) {
+        const Range rw = range(workspace, wl.total);
+        if (overlap(rw, ro) || (lse && overlap(rw, rl)))
+            return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace overlaps an output", fn);
+        for (const Range& r : ins)
+            if (overlap(rw, r))
+                return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace overlaps an input", fn);
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = workspace;
+    if (!ws) {
+        hipError_t e = hipMallocAsync(&ws, wl.total, s);
+        if (e != hipSuccess) return hip_fail("spa_sfa_fwd: hipMallocAsync", e);
+    }
+    char* wsb = static_cast<char*>(ws);
+    void* Qt = wsb;
+    void* Kt = wsb + wl.k_offset;
+    float* kmax = reinterpret_cast<float*>(wsb + wl.kmax_offset);
+    void* Vt = wsb + wl.vt_offset;
+    hipError_t e = spa::launch_sfa_topk(Q, K, Qt, Kt, kmax, B * H, N, d, topk,
+                                        scale * 1.44269504088896340736f, s);
+    // V^T through the preparation kernel's transpose role alone (no projection roles)
+    if (e == hipSuccess)
+        e = spa::launch_project_bf16(nullptr, nullptr, nullptr, nullptr, nullptr, 0, B * H, H,
+                                     N, d, 1, 1, 1, 1.0f, 1.0f, true, nullptr, V, Vt, dv, s);
+    if (e == hipSuccess)
+        e = spa::launch_attn_bf16(Qt, Kt, Vt, kmax, O, lse, B * H, N, d, dv, causal == 1,
+                                  o_dtype == SPA_F32, s);
+    if (!workspace) {
+        hipError_t e2 = hipFreeAsync(ws, s);
+        if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return SPA_OK;
+}
+
 size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
                                     spa_dtype_t dtype) {
     if (B < 1 || H < 1 || N < 1 || N > kMaxN || (long long)B * H * N >= kMaxRows) return 0;

@@ -108,4 +108,10 @@ struct DecodeSplit {
 DecodeSplit decode_split(int BH, int Nq, int Nk);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// Sparse feature attention operands: Topk_k of every row of Q and K (bf16 [BH, N, d],
+// d in {64, 128}) into fp16 [BH, N, d] (queries times qscale), the largest selected key norm
+// per 256-key block into kmax [BH, proj_blocks(N)].
+hipError_t launch_sfa_topk(const void* Q, const void* K, void* Qt, void* Kt, float* kmax,
+                           int BH, int N, int d, int k, float qscale, hipStream_t stream);
+
 }  // namespace spa

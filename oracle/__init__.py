@@ -188,6 +188,31 @@ def attn_decode(Q, K, V, P, scale: float, causal: bool, with_lse: bool = False,
     return out.reshape(B, H, Nq, dv)
 
 
+def topk_features(X, k: int) -> np.ndarray:
+    """Row-wise Top-k along the last axis (Scaling Attention via Feature Sparsity, key design
+    1): keep x_u where u is among the k coordinates of largest |x|, zero elsewhere. Reading
+    for ties in |x| (the page does not break them): the lower coordinate index wins."""
+    X = _f64(X)
+    d = X.shape[-1]
+    if not 1 <= k <= d:
+        raise ValueError("k must be in [1, d]")
+    # a stable sort by -|x| keeps equal magnitudes in index order
+    keep = np.argsort(-np.abs(X), axis=-1, kind="stable")[..., :k]
+    out = np.zeros_like(X)
+    np.put_along_axis(out, keep, np.take_along_axis(X, keep, axis=-1), axis=-1)
+    return out
+
+
+def sfa_fwd(Q, K, V, k: int, scale: float, causal: bool, with_lse: bool = False,
+            nthreads: int = 0):
+    """Sparse feature attention: softmax(scale Topk_k(Q) Topk_k(K)^T [+causal]) V, exact,
+    computed as the forward above with P = I on the Top-k rows."""
+    Qs, Ks = topk_features(Q, k), topk_features(K, k)
+    H, d = Qs.shape[1], Qs.shape[3]
+    eye = np.broadcast_to(np.eye(d), (H, d, d)).copy()
+    return attn_fwd(Qs, Ks, V, eye, scale, causal, with_lse=with_lse, nthreads=nthreads)
+
+
 def _matrix(fn_name: str, Q, K, P, scale: float, causal: bool, nthreads: int) -> np.ndarray:
     Q, K, P = _f64(Q), _f64(K), _f64(P)
     B, H, N, d = Q.shape

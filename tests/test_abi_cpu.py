@@ -233,3 +233,31 @@ def test_decode_workspace_bytes(L):
     assert L.spa_attn_decode_workspace_bytes(1, 32, 1, 32768, 128) == 32 * 1 * 32 * 130 * 4 + 32 * 128 * 4
     assert L.spa_attn_decode_workspace_bytes(1, 1, 1, 100, 64) == 1 * 1 * 1 * 66 * 4 + 128 * 4
     assert L.spa_attn_decode_workspace_bytes(1, 2, 17, 16, 128) == 0  # Nq > Nk
+
+
+def test_sfa_fwd_rejects_on_host(L):
+    ok = dict(Q=A, K=B_, V=C, topk=16, scale=0.125, causal=1, B=1, H=2, N=256, d=128, dv=128,
+              dtype=spa.SPA_BF16, O=E, o_dtype=spa.SPA_F32, lse=None, ws=F, ws_bytes=1 << 30)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.spa_sfa_fwd(a["Q"], a["K"], a["V"], a["topk"], a["scale"], a["causal"], a["B"],
+                             a["H"], a["N"], a["d"], a["dv"], a["dtype"], a["O"], a["o_dtype"],
+                             a["lse"], a["ws"], a["ws_bytes"], None)
+    for kw, code in ((dict(Q=None), spa.SPA_ERR_INVALID_ARGUMENT),
+                     (dict(topk=0), spa.SPA_ERR_INVALID_ARGUMENT),
+                     (dict(topk=129), spa.SPA_ERR_INVALID_ARGUMENT),
+                     (dict(causal=3), spa.SPA_ERR_INVALID_ARGUMENT),
+                     (dict(dtype=spa.SPA_F32), spa.SPA_ERR_UNSUPPORTED),
+                     (dict(d=96, topk=8), spa.SPA_ERR_UNSUPPORTED),
+                     (dict(dv=32), spa.SPA_ERR_UNSUPPORTED),
+                     (dict(O=A), spa.SPA_ERR_INVALID_ARGUMENT),
+                     (dict(ws_bytes=100), spa.SPA_ERR_WORKSPACE),
+                     (dict(V=C + 2), spa.SPA_ERR_INVALID_ARGUMENT)):
+        assert call(**kw) == code, kw
+        assert len(L.spa_last_error()) > 0
+    # the forward's workspace with m = d
+    assert L.spa_sfa_fwd_workspace_bytes(1, 2, 256, 128, 128) == \
+        L.spa_attn_fwd_workspace_bytes(1, 2, 256, 128, 128, 128, spa.SPA_BF16)
+    assert L.spa_sfa_fwd_workspace_bytes(1, 2, 256, 96, 128) == 0
