@@ -241,6 +241,10 @@ def spa_attn_bwd(Q, K, V, P, O, dO, lse, scale: float | None = None, causal: boo
     return dQ, dK, dV, dP
 
 
+def spa_sfa_fwd_workspace_bytes(B, H, N, d, dv) -> int:
+    return int(lib().spa_sfa_fwd_workspace_bytes(B, H, N, d, dv))
+
+
 def spa_sfa_fwd(Q, K, V, topk: int, scale: float | None = None, causal: bool = False,
                 out_dtype=None, return_lse: bool = False, workspace=None):
     """Sparse feature attention: softmax(scale Topk(Q) Topk(K)^T [+causal]) V on the

@@ -10,7 +10,8 @@
 // results). Dense 32x32x16 MFMAs over d <= 128 features cost d/16 instructions per 32x32
 // score tile, far less than scattering the support intersections.
 //
-// One wave per row: the lanes hold d/64 consecutive features each; the k-th largest
+// A workgroup of 16 waves per (head, 256 tokens), each wave 16 rows whose loads are all
+// issued first. Per row the lanes hold d/64 consecutive features each; the k-th largest
 // magnitude T is found by a bitwise search over the 15 magnitude bits of bf16 with wave
 // ballots counting the features at or above a candidate (wave-uniform, scalar counts);
 // features above T are kept, and of those equal to T the (k - #above) of lowest index.
@@ -20,7 +21,8 @@
 namespace spa {
 namespace {
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkRows = kProjBlockTokens / (kTopkThreads / 64);  // rows per wave
 
 __device__ __forceinline__ int popc64(uint64_t x) { return __builtin_popcountll(x); }
 
@@ -41,17 +43,23 @@ __global__ __launch_bounds__(kTopkThreads) void sfa_topk_kernel(
     const uint64_t below = (1ull << lane) - 1ull;
     float nmax = 0.0f;  // largest squared norm of a selected key row in this wave
 
-    for (int r = 0; r < kProjBlockTokens / 4; ++r) {
-        const int tok = blk * kProjBlockTokens + wave * (kProjBlockTokens / 4) + r;
+    const int tok0 = blk * kProjBlockTokens + wave * kTopkRows;
+    uint32_t raw[kTopkRows];  // the wave's rows: this lane's d/64 features of each
+#pragma unroll
+    for (int r = 0; r < kTopkRows; ++r) {
+        const int tok = tok0 + r;
+        raw[r] = 0u;
+        if (tok < N)
+            raw[r] = E == 2 ? *reinterpret_cast<const uint32_t*>(X + (size_t)tok * D + 2 * lane)
+                            : (uint32_t)X[(size_t)tok * D + lane];
+    }
+#pragma unroll
+    for (int r = 0; r < kTopkRows; ++r) {  // unrolled: raw[] stays in registers
+        const int tok = tok0 + r;
         if (tok >= N) break;  // wave-uniform
         uint16_t x[E];
-        if (E == 2) {
-            const uint32_t v = *reinterpret_cast<const uint32_t*>(X + (size_t)tok * D + 2 * lane);
-            x[0] = (uint16_t)(v & 0xffffu);
-            x[E - 1] = (uint16_t)(v >> 16);
-        } else {
-            x[0] = X[(size_t)tok * D + lane];
-        }
+        x[0] = (uint16_t)(raw[r] & 0xffffu);
+        if (E == 2) x[E - 1] = (uint16_t)(raw[r] >> 16);
         uint32_t mag[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) mag[e] = x[e] & 0x7fffu;
