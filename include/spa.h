@@ -152,7 +152,7 @@ size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
  *   workspace / workspace_bytes: as for spa_attn_fwd, sized by
  *        spa_attn_bwd_workspace_bytes (NULL: allocated and freed stream-ordered).
  *
- * Supported: dtype SPA_BF16, d in {64, 128}, dv in {64, 128}, 1 <= m <= 64
+ * Supported: dtype SPA_BF16, d in {64, 128}, dv in {64, 128}, 1 <= m <= 128
  * (SPA_ERR_UNSUPPORTED otherwise). The projected queries and keys are prepared exactly as
  * in the forward (fp16), so the recomputed scores match the forward's bit for bit; the
  * weights meet dO in bf16 and dS meets the projected operands in fp16, all on MFMA with fp32

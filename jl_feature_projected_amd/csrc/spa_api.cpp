@@ -562,7 +562,7 @@ spa_status_t spa_sfa_fwd(const void* Q, const void* K, const void* V, int topk, 
 size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
                                     spa_dtype_t dtype) {
     if (B < 1 || H < 1 || N < 1 || N > kMaxN || (long long)B * H * N >= kMaxRows) return 0;
-    if (dtype != SPA_BF16 || (d != 64 && d != 128) || m < 1 || m > 64 || (dv != 64 && dv != 128))
+    if (dtype != SPA_BF16 || (d != 64 && d != 128) || m < 1 || m > 128 || (dv != 64 && dv != 128))
         return 0;
     return bwd_layout(B * H, N, d, m, dv).total;
 }
@@ -589,9 +589,9 @@ spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const voi
         return fail(SPA_ERR_INVALID_ARGUMENT, "%s: unknown g_dtype %d", fn, (int)g_dtype);
     if (dtype != SPA_BF16)
         return fail(SPA_ERR_UNSUPPORTED, "%s: only the bf16 path has a backward", fn);
-    if ((d != 64 && d != 128) || m > 64 || (dv != 64 && dv != 128))
+    if ((d != 64 && d != 128) || m > 128 || (dv != 64 && dv != 128))
         return fail(SPA_ERR_UNSUPPORTED,
-                    "%s: backward needs d in {64,128}, m <= 64, dv in {64,128} (d=%d m=%d dv=%d)",
+                    "%s: backward needs d in {64,128}, m <= 128, dv in {64,128} (d=%d m=%d dv=%d)",
                     fn, d, m, dv);
     const void* al16[] = {Q, K, V, P, O, dO, dQ, dK, dV};
     for (const void* p : al16)

@@ -783,6 +783,7 @@ hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
         case 16: e = launch_dv<16>(a, stream); break;
         case 32: e = launch_dv<32>(a, stream); break;
         case 64: e = launch_dv<64>(a, stream); break;
+        case 128: e = launch_dv<128>(a, stream); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
@@ -796,11 +797,13 @@ hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
     if (a.d == 128) {
         if (a.mp == 16) SPA_PG(128, 16);
         else if (a.mp == 32) SPA_PG(128, 32);
-        else SPA_PG(128, 64);
+        else if (a.mp == 64) SPA_PG(128, 64);
+        else SPA_PG(128, 128);
     } else {
         if (a.mp == 16) SPA_PG(64, 16);
         else if (a.mp == 32) SPA_PG(64, 32);
-        else SPA_PG(64, 64);
+        else if (a.mp == 64) SPA_PG(64, 64);
+        else SPA_PG(64, 128);
     }
 #undef SPA_PG
     e = hipGetLastError();

@@ -151,7 +151,7 @@ def _bwd(L, **kw):
     (dict(dV=A + 0x40), spa.SPA_ERR_INVALID_ARGUMENT),           # overlaps Q
     (dict(ws_bytes=100), spa.SPA_ERR_WORKSPACE),
     (dict(dtype=spa.SPA_F32), spa.SPA_ERR_UNSUPPORTED),
-    (dict(m=65), spa.SPA_ERR_UNSUPPORTED),
+    (dict(m=129), spa.SPA_ERR_UNSUPPORTED),
     (dict(d=96), spa.SPA_ERR_UNSUPPORTED),
     (dict(dv=32), spa.SPA_ERR_UNSUPPORTED),
 ])
@@ -168,7 +168,7 @@ def test_bwd_workspace_bytes(L):
     sizes = [rows * mp * 2, rows * mp * 2, BH * mp * np_ * 2, BH * mp * np_ * 2, BH * dv * np_ * 2,
              BH * np_ * 2 * 4, rows * mp * 4, rows * mp * 4, BH * 1 * d * m * 4]
     assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, m, dv, spa.SPA_BF16) == sum(a256(s) for s in sizes)
-    assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, 65, dv, spa.SPA_BF16) == 0
+    assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, 129, dv, spa.SPA_BF16) == 0
     assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, m, dv, spa.SPA_F32) == 0
 
 

@@ -70,6 +70,9 @@ SMALL = [  # B, H, N, d, m, dv, causal
     (1, 3, 64, 128, 8, 128, False),
     (2, 1, 1000, 128, 32, 128, True),
     (1, 2, 777, 128, 5, 64, True),
+    (1, 2, 300, 128, 128, 128, True),
+    (2, 1, 333, 64, 100, 64, False),
+    (1, 1, 200, 128, 128, 64, False),
 ]
 
 
@@ -91,6 +94,16 @@ def test_backward_headline_recipe_reduced_length(dev, oracle_mod):
     ref = oracle.attn_bwd(x.Q, x.K, V, x.P, dO, w.scale, True)
     for name, a, b in zip(("dQ", "dK", "dV", "dP"), got, ref):
         compare(f"c3-recipe N=2048 {name}", a, b)
+
+
+def test_backward_identity_projection_d128(dev, oracle_mod):
+    """m = d = 128 with P = I: the gradients of exact attention (the P = I workload's shape)."""
+    w = inputs.Workload("bwd-identity-128", 1, 2, 300, 128, 128, 128, True, proj="identity",
+                        seed=6)
+    x, V, dO, got = run_bwd(w, dev, seed=7)
+    ref = oracle.attn_bwd(x.Q, x.K, V, x.P, dO, w.scale, True)
+    for name, g, r in zip(("dQ", "dK", "dV", "dP"), got, ref):
+        compare("identity-128 " + name, g, r)
 
 
 def test_backward_identity_projection(dev, oracle_mod):
