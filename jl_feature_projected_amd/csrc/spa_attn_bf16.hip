@@ -139,10 +139,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     // (At MP = DV = 128 the pipelined loop does not fit the register budget of two
     // workgroups per CU; that shape runs every tile through tile_loop.)
     constexpr bool PIPELINED = !(MP == 128 && DV == 128);
-    const int nfull = !PIPELINED ? 0 : CAUSAL ? min(ntiles, q0 / kBC) : N / kBC;
+    // Tiles with no masked key for any query of the workgroup.
+    const int nfull = CAUSAL ? min(ntiles, q0 / kBC) : N / kBC;
     copy_k(0, 0);
     copy_v(0, 0);
-    if (nfull > 0 && ntiles > 1) copy_k(kBC, 1);
+    if (PIPELINED && ntiles > 1) copy_k(kBC, 1);
 
     // This lane's query as the B operand of the score MFMA (zero past N).
     f16x8 qf[KS];
@@ -213,10 +214,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         }
     };
     // Weights of k-step tt of key block kb, pair j (keys 2j, 2j+1 of the lane's 8 slots):
-    // exp2, rounded to bf16, packed, and added to the normaliser.
-    auto weight_pair = [&](const f32x16 (&s)[2], int kb, int tt, int j) -> uint32_t {
-        const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j]);
-        const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * tt + 2 * j + 1]);
+    // exp2, rounded to bf16, packed, and added to the normaliser. With a mask, slot i of
+    // key block kb (key k0 + kb*32 + 8*(i/4) + 4*half + i%4) is dropped when kb*32 + 8*(i/4)
+    // + i%4 > rel, rel being the lane's last admissible key minus k0 + 4*half.
+    auto weight_pair = [&](const f32x16 (&s)[2], int kb, int tt, int j, auto masked,
+                           int rel) -> uint32_t {
+        constexpr bool MASKED = decltype(masked)::value;
+        float x0 = s[kb][8 * tt + 2 * j], x1 = s[kb][8 * tt + 2 * j + 1];
+        if constexpr (MASKED) {
+            const int i0 = 8 * tt + 2 * j;
+            if (kb * 32 + 8 * (i0 >> 2) + (i0 & 3) > rel) x0 = -INFINITY;
+            if (kb * 32 + 8 * (i0 >> 2) + (i0 & 3) + 1 > rel) x1 = -INFINITY;
+        }
+        const float p0 = __builtin_amdgcn_exp2f(x0);
+        const float p1 = __builtin_amdgcn_exp2f(x1);
         const uint32_t w = pack_bf16x2(p0, p1);
         lsum = add_bf16x2(w, lsum);
         return w;
@@ -243,7 +254,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) p[kb][tt][j] = weight_pair(s, kb, tt, j);
+                for (int j = 0; j < 4; ++j)
+                    p[kb][tt][j] = weight_pair(s, kb, tt, j, std::false_type{}, 0);
     };
     // One pipelined step: scores of the next tile (K tile Kn) and PV of this one (V^T tile
     // Vs, weights p), with the next tile's weights (out pn) computed while the PV MFMAs run.
@@ -254,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     // WSTART PV MFMAs after the score MFMAs (their inputs are ready by then) and are spread
     // evenly over the remaining PV MFMAs.
     auto pipelined_step = [&](const char* Kn, const char* Vs, const u32x4 (&p)[2][2],
-                              u32x4 (&pn)[2][2]) {
+                              u32x4 (&pn)[2][2], auto masked, int rel) {
         constexpr int NPV = 4 * DB;  // PV MFMAs per tile
         constexpr int PF = 4;        // V operand prefetch distance, in MFMAs
         constexpr int WSTART = 3;    // first PV MFMA that weight work is placed after
@@ -291,7 +303,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 #pragma unroll
                 for (int u = (i - WSTART) * 16 / NW; u < (i - WSTART + 1) * 16 / NW; ++u)
                     pn[u >> 3][(u >> 2) & 1][u & 3] =
-                        weight_pair(sn, u >> 3, (u >> 2) & 1, u & 3);
+                        weight_pair(sn, u >> 3, (u >> 2) & 1, u & 3, masked, rel);
             }
             // Slot fence: the compiler keeps this order (it would otherwise bunch the exps).
             __builtin_amdgcn_sched_barrier(0);
@@ -373,69 +385,105 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         }
     };
 
-    // Fast path, tiles [0, nfull): no key of them is masked for any query of the workgroup,
-    // so they are software pipelined: the score MFMAs of tile t+1 are issued, then the PV
-    // MFMAs of tile t run while the wave computes tile t+1's weights. K and V copies are
-    // issued separately, each one step before the step that reads it:
+    // Fast path (every tile when the shape is pipelined): the score MFMAs of tile t+1 are
+    // issued, then the PV MFMAs of tile t run while the wave computes tile t+1's weights. K
+    // and V copies are issued separately, each one step before the step that reads it:
     //   step t reads K[t+1] (buffer (t+1)&1) and V[t] (buffer t&1), and copies V[t+1] into
     //   buffer (t+1)&1 and K[t+2] into buffer t&1.
-    // Returns nfull with tile nfull's K and V in buffer nfull&1, as tile_loop expects. The
-    // copies of tile 0 (and of tile 1's keys) were issued at the top of the kernel.
+    // Tiles [0, nfull) have no masked key for any query of the workgroup; their steps run in
+    // a loop of two steps with the buffer parity as a template constant (every LDS offset an
+    // immediate) and no branch around the MFMAs. The at most three steps after it mask the
+    // keys past N and past each query (causal) as the weights are formed, and a wave skips
+    // the score or PV half of a step whose tile lies wholly after its queries. Returns the
+    // number of tiles done (all, or none for the shapes that are not pipelined). The copies
+    // of tile 0 (and of tile 1's keys) were issued at the top of the kernel.
     auto fast_phase = [&]() -> int {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (!PIPELINED || nfull == 0) return 0;
-        if constexpr (!PIPELINED) return 0;
-        u32x4 pa[2][2], pb[2][2];
-        {
-            f32x16 s[2];
-            scores(lds, s);
-            weights(s, pa);
-        }
-        __syncthreads();  // K[0] read by every wave before step 0 refills buffer 0
-        // Step t with the buffer parity t & 1 as a template constant, so every LDS offset of
-        // the step is an immediate. Weights p of tile t in, weights pn of tile t+1 out. Every
-        // step but the last is pipelined; the last (PV of tile nfull-1 only) is peeled off
-        // so the loop body has no branch around its MFMAs.
-        auto step = [&](auto parity, int t, const u32x4 (&p)[2][2], u32x4 (&pn)[2][2]) {
-            constexpr int PAR = decltype(parity)::value;
-            copy_v((t + 1) * kBC, 1 - PAR);  // t + 1 < nfull <= ntiles
-            if (t + 2 < ntiles) copy_k((t + 2) * kBC, PAR);
-            pipelined_step(lds + (1 - PAR) * BUF, lds + PAR * BUF + K_BYTES, p, pn);
-            // The weights are plain register arithmetic, which the compiler may sink past the
-            // barrier to their use in the next step; pin them here, beside the MFMAs they are
-            // meant to overlap.
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt) asm volatile("" : "+v"(pn[kb][tt]));
-            asm volatile("" : "+v"(lsum));
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        };
-        auto last_step = [&](auto parity, int t, const u32x4 (&p)[2][2]) {
-            constexpr int PAR = decltype(parity)::value;
-            if (t + 1 < ntiles) copy_v((t + 1) * kBC, 1 - PAR);
-            if (t + 2 < ntiles) copy_k((t + 2) * kBC, PAR);
-            pv(lds + PAR * BUF + K_BYTES, p);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        };
-        using P0 = std::integral_constant<int, 0>;
-        using P1 = std::integral_constant<int, 1>;
-        int t = 0;
-#pragma unroll 1
-        for (; t + 2 < nfull; t += 2) {
-            step(P0{}, t, pa, pb);
-            step(P1{}, t + 1, pb, pa);
-        }
-        if (t + 1 < nfull) {
-            step(P0{}, t, pa, pb);
-            last_step(P1{}, t + 1, pb);
+        if constexpr (!PIPELINED) {
+            return 0;
         } else {
-            last_step(P0{}, t, pa);
+            // The lane's last admissible key (ragged tail, causal diagonal).
+            const int klim = CAUSAL ? min(myq, N - 1) : N - 1;
+            auto rel_of = [&](int k0) { return klim - k0 - 4 * half; };
+            // Does this wave have an admissible key in tile t?
+            auto wave_needs = [&](int t) { return !CAUSAL || t * kBC <= qw0 + 31; };
+            u32x4 pa[2][2], pb[2][2];
+            {
+                f32x16 s[2];
+                scores(lds, s);
+                if (nfull == 0) {
+                    const int rel = rel_of(0);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                pa[kb][tt][j] = weight_pair(s, kb, tt, j, std::true_type{}, rel);
+                } else {
+                    weights(s, pa);
+                }
+            }
+            __syncthreads();  // K[0] read by every wave before step 0 refills buffer 0
+            // Step t of the unmasked loop, weights p of tile t in, pn of tile t+1 out.
+            auto step = [&](auto parity, int t, const u32x4 (&p)[2][2], u32x4 (&pn)[2][2]) {
+                constexpr int PAR = decltype(parity)::value;
+                copy_v((t + 1) * kBC, 1 - PAR);  // t + 1 < nfull <= ntiles
+                if (t + 2 < ntiles) copy_k((t + 2) * kBC, PAR);
+                pipelined_step(lds + (1 - PAR) * BUF, lds + PAR * BUF + K_BYTES, p, pn,
+                               std::false_type{}, 0);
+                // The weights are plain register arithmetic, which the compiler may sink past
+                // the barrier to their use in the next step; pin them here, beside the MFMAs
+                // they are meant to overlap.
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) asm volatile("" : "+v"(pn[kb][tt]));
+                asm volatile("" : "+v"(lsum));
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            };
+            using P0 = std::integral_constant<int, 0>;
+            using P1 = std::integral_constant<int, 1>;
+            int t = 0;
+#pragma unroll 1
+            for (; t + 2 < nfull; t += 2) {
+                step(P0{}, t, pa, pb);
+                step(P1{}, t + 1, pb, pa);
+            }
+            // The rest, t .. ntiles - 1 (at most three steps and the last PV: t + 2 >= nfull,
+            // ntiles <= nfull + 2), with the buffer parity at run time and tile t's weights
+            // always in pa.
+#pragma unroll 1
+            for (; t + 1 < ntiles; ++t) {
+                const int par = t & 1;
+                const char* Kn = lds + (1 - par) * BUF;
+                const char* Vs = lds + par * BUF + K_BYTES;
+                copy_v((t + 1) * kBC, 1 - par);
+                if (t + 2 < ntiles) copy_k((t + 2) * kBC, par);
+                if (wave_needs(t + 1)) {
+                    if (t + 1 < nfull)
+                        pipelined_step(Kn, Vs, pa, pb, std::false_type{}, 0);
+                    else
+                        pipelined_step(Kn, Vs, pa, pb, std::true_type{}, rel_of((t + 1) * kBC));
+                } else {
+                    if (wave_needs(t)) pv(Vs, pa);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt) pb[kb][tt] = u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) pa[kb][tt] = pb[kb][tt];
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
+            if (wave_needs(t)) pv(lds + (t & 1) * BUF + K_BYTES, pa);
+            return ntiles;
         }
-        return nfull;
     };
 
     init_state(bound);
