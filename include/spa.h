@@ -126,10 +126,11 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
 
 /*
  * Workspace bytes spa_attn_bwd needs for these sizes (0 for arguments it would reject).
- * Contents (each region 256-byte aligned): the projected queries (scaled by
+ * Contents (each region 256-byte aligned), bf16 path: the projected queries (scaled by
  * scale*log2(e)) and keys, fp16, row-major and transposed; dO transposed (bf16); the row
  * terms D_i = <dO_i, O_i> (fp32); the gradients of the projected queries and keys (fp32);
- * the projection gradient's per-256-row partial sums (fp32).
+ * the projection gradient's per-256-row partial sums (fp32). fp32 path: the projected
+ * queries and keys and their gradients (fp32 [B,H,N,m] each) and the row terms D (fp32).
  */
 size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
                                     spa_dtype_t dtype);
@@ -145,18 +146,22 @@ size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
  *   dP_h = sum over batches of Q^T (scale dS Kt) + K^T (scale dS^T Qt)
  *
  *   Q, K, V, P, scale, causal, B, H, N, d, m, dv, dtype: as passed to spa_attn_fwd.
- *   O    [B,H,N,dv] the forward's output, bf16; dO [B,H,N,dv] bf16.
+ *   O    [B,H,N,dv] the forward's output; dO [B,H,N,dv]; both in dtype.
  *   lse  [B,H,N] fp32, the forward's lse output (the weights are recomputed from it).
- *   dQ, dK [B,H,N,d] and dV [B,H,N,dv] in g_dtype (SPA_BF16 or SPA_F32); dP [H,d,m] fp32.
+ *   dQ, dK [B,H,N,d] and dV [B,H,N,dv] in g_dtype (SPA_BF16 or SPA_F32; SPA_F32 only when
+ *        dtype is SPA_F32); dP [H,d,m] fp32.
  *        No output may overlap an input, another output or the workspace.
  *   workspace / workspace_bytes: as for spa_attn_fwd, sized by
  *        spa_attn_bwd_workspace_bytes (NULL: allocated and freed stream-ordered).
  *
- * Supported: dtype SPA_BF16, d in {64, 128}, dv in {64, 128}, 1 <= m <= 128
- * (SPA_ERR_UNSUPPORTED otherwise). The projected queries and keys are prepared exactly as
- * in the forward (fp16), so the recomputed scores match the forward's bit for bit; the
- * weights meet dO in bf16 and dS meets the projected operands in fp16, all on MFMA with fp32
- * accumulation. Five launches on `stream`; results are deterministic (no atomics).
+ * Supported: dtype SPA_BF16 with d in {64, 128}, dv in {64, 128}, 1 <= m <= 128; dtype
+ * SPA_F32 with d <= 256, dv <= 128, m <= 128 (SPA_ERR_UNSUPPORTED otherwise). bf16: the
+ * projected queries and keys are prepared exactly as in the forward (fp16), so the
+ * recomputed scores match the forward's bit for bit; the weights meet dO in bf16 and dS
+ * meets the projected operands in fp16, all on MFMA with fp32 accumulation; five launches.
+ * fp32: every product and sum in fp32 on the VALU (the projections, a query-major and a
+ * key-major pass, the gradients mapped back through P, and dP); seven launches. Both run
+ * on `stream` and are deterministic (no atomics).
  */
 spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const void* P,
                           const void* O, const void* dO, const float* lse, float scale,

@@ -200,9 +200,10 @@ def spa_attn_bwd(Q, K, V, P, O, dO, lse, scale: float | None = None, causal: boo
                  grad_dtype=None, workspace=None):
     """Gradients (dQ, dK, dV, dP) of a loss through spa_attn_fwd, given dO = dL/dO.
 
-    Q, K, V, P as passed to spa_attn_fwd (bf16); O the forward's output (bf16) and lse its
-    log-sum-exp (fp32 [B,H,N], spa_attn_fwd(..., return_lse=True)); dO bf16 like O.
-    grad_dtype: torch.float32 or torch.bfloat16 for dQ, dK, dV (default float32); dP is
+    Q, K, V, P as passed to spa_attn_fwd (bf16, or float32 for the fp32 path); O the
+    forward's output and lse its log-sum-exp (fp32 [B,H,N], spa_attn_fwd(...,
+    return_lse=True)); O and dO in the inputs' dtype. grad_dtype: torch.float32 or
+    torch.bfloat16 for dQ, dK, dV (default float32; float32 only on the fp32 path); dP is
     fp32 [H,d,m]. Runs on the current stream.
     """
     torch = _torch()
@@ -220,8 +221,8 @@ def spa_attn_bwd(Q, K, V, P, O, dO, lse, scale: float | None = None, causal: boo
     if lse.dtype != torch.float32:
         raise ValueError("lse must be float32")
     dt = Q.dtype
-    if any(x.dtype != dt for x in (K, V, P)):
-        raise ValueError("Q, K, V and P must share a dtype")
+    if any(x.dtype != dt for x in (K, V, P, O, dO)):
+        raise ValueError("Q, K, V, P, O and dO must share a dtype")
     gdt = torch.float32 if grad_dtype is None else grad_dtype
     dQ = torch.empty((B, H, N, d), dtype=gdt, device=Q.device)
     dK = torch.empty((B, H, N, d), dtype=gdt, device=Q.device)

@@ -107,6 +107,29 @@ BwdLayout bwd_layout(int BH, int N, int d, int m, int dv) {
     return w;
 }
 
+// fp32 backward workspace: the projected queries and keys, their gradients (fp32 [B*H, N, m]
+// each) and the row terms D (fp32 [B*H, N]), each region 256-byte aligned.
+struct BwdF32Layout {
+    size_t qt, kt, dqt, dkt, dd, total;
+};
+BwdF32Layout bwd_f32_layout(int BH, int N, int m) {
+    const size_t rows = (size_t)BH * N;
+    BwdF32Layout w;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    w.qt = take(rows * m * 4);
+    w.kt = take(rows * m * 4);
+    w.dqt = take(rows * m * 4);
+    w.dkt = take(rows * m * 4);
+    w.dd = take(rows * 4);
+    w.total = o;
+    return w;
+}
+
 spa_status_t check_dims(const char* fn, int B, int H, int N, int d, int m, int dv) {
     if (B < 1 || H < 1 || N < 1 || d < 1 || m < 1 || dv < 1)
         return fail(SPA_ERR_INVALID_ARGUMENT,
@@ -562,6 +585,10 @@ spa_status_t spa_sfa_fwd(const void* Q, const void* K, const void* V, int topk, 
 size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
                                     spa_dtype_t dtype) {
     if (B < 1 || H < 1 || N < 1 || N > kMaxN || (long long)B * H * N >= kMaxRows) return 0;
+    if (dtype == SPA_F32) {
+        if (d < 1 || d > 256 || m < 1 || m > 128 || dv < 1 || dv > 128) return 0;
+        return bwd_f32_layout(B * H, N, m).total;
+    }
     if (dtype != SPA_BF16 || (d != 64 && d != 128) || m < 1 || m > 128 || (dv != 64 && dv != 128))
         return 0;
     return bwd_layout(B * H, N, d, m, dv).total;
@@ -587,12 +614,18 @@ spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const voi
         return fail(SPA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dtype);
     if (g_dtype != SPA_BF16 && g_dtype != SPA_F32)
         return fail(SPA_ERR_INVALID_ARGUMENT, "%s: unknown g_dtype %d", fn, (int)g_dtype);
-    if (dtype != SPA_BF16)
-        return fail(SPA_ERR_UNSUPPORTED, "%s: only the bf16 path has a backward", fn);
-    if ((d != 64 && d != 128) || m > 128 || (dv != 64 && dv != 128))
+    if (dtype == SPA_F32) {
+        if (d > 256 || m > 128 || dv > 128)
+            return fail(SPA_ERR_UNSUPPORTED,
+                        "%s: fp32 backward needs d <= 256, m <= 128, dv <= 128 (d=%d m=%d dv=%d)",
+                        fn, d, m, dv);
+        if (g_dtype != SPA_F32)
+            return fail(SPA_ERR_UNSUPPORTED, "%s: the fp32 path writes fp32 gradients only", fn);
+    } else if ((d != 64 && d != 128) || m > 128 || (dv != 64 && dv != 128)) {
         return fail(SPA_ERR_UNSUPPORTED,
                     "%s: backward needs d in {64,128}, m <= 128, dv in {64,128} (d=%d m=%d dv=%d)",
                     fn, d, m, dv);
+    }
     const void* al16[] = {Q, K, V, P, O, dO, dQ, dK, dV};
     for (const void* p : al16)
         if (!aligned(p, 16))
@@ -602,15 +635,19 @@ spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const voi
     if (workspace && !aligned(workspace, 16))
         return fail(SPA_ERR_INVALID_ARGUMENT, "%s: workspace not 16-byte aligned", fn);
     const long long rows = (long long)B * H * N;
+    const bool f32 = dtype == SPA_F32;
     const BwdLayout wl = bwd_layout(B * H, N, d, m, dv);
-    if (workspace && workspace_bytes < wl.total)
+    const BwdF32Layout wl32 = bwd_f32_layout(B * H, N, m);
+    const size_t need = f32 ? wl32.total : wl.total;
+    if (workspace && workspace_bytes < need)
         return fail(SPA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn,
-                    workspace_bytes, wl.total);
+                    workspace_bytes, need);
     const size_t ge = g_dtype == SPA_F32 ? 4 : 2;
-    const Range ins[8] = {range(Q, rows * d * 2),  range(K, rows * d * 2),
-                          range(V, rows * dv * 2), range(P, (size_t)H * d * m * 2),
-                          range(O, rows * dv * 2), range(dO, rows * dv * 2),
-                          range(lse, rows * 4),    range(workspace, workspace ? wl.total : 0)};
+    const size_t ie = f32 ? 4 : 2;
+    const Range ins[8] = {range(Q, rows * d * ie),  range(K, rows * d * ie),
+                          range(V, rows * dv * ie), range(P, (size_t)H * d * m * ie),
+                          range(O, rows * dv * ie), range(dO, rows * dv * ie),
+                          range(lse, rows * 4),     range(workspace, workspace ? need : 0)};
     const Range outs[4] = {range(dQ, rows * d * ge), range(dK, rows * d * ge),
                            range(dV, rows * dv * ge), range(dP, (size_t)H * d * m * 4)};
     for (int i = 0; i < 4; ++i) {
@@ -630,10 +667,44 @@ spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const voi
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* ws = workspace;
     if (!ws) {
-        hipError_t e = hipMallocAsync(&ws, wl.total, s);
+        hipError_t e = hipMallocAsync(&ws, need, s);
         if (e != hipSuccess) return hip_fail("spa_attn_bwd: hipMallocAsync", e);
     }
     char* w = static_cast<char*>(ws);
+    if (f32) {
+        spa::BwdF32Args a;
+        a.Q = static_cast<const float*>(Q);
+        a.K = static_cast<const float*>(K);
+        a.V = static_cast<const float*>(V);
+        a.P = static_cast<const float*>(P);
+        a.O = static_cast<const float*>(O);
+        a.dO = static_cast<const float*>(dO);
+        a.lse = lse;
+        a.Qt = reinterpret_cast<float*>(w + wl32.qt);
+        a.Kt = reinterpret_cast<float*>(w + wl32.kt);
+        a.dQt = reinterpret_cast<float*>(w + wl32.dqt);
+        a.dKt = reinterpret_cast<float*>(w + wl32.dkt);
+        a.D = reinterpret_cast<float*>(w + wl32.dd);
+        a.dQ = static_cast<float*>(dQ);
+        a.dK = static_cast<float*>(dK);
+        a.dV = static_cast<float*>(dV);
+        a.dP = dP;
+        a.B = B;
+        a.H = H;
+        a.N = N;
+        a.d = d;
+        a.m = m;
+        a.dv = dv;
+        a.causal = causal;
+        a.scale = scale;
+        hipError_t e = spa::launch_attn_bwd_f32(a, s);
+        if (!workspace) {
+            hipError_t e2 = hipFreeAsync(ws, s);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return hip_fail(fn, e);
+        return SPA_OK;
+    }
     const int mp = spa::padded_m(m);
     const float qscale = scale * 1.44269504088896340736f;
     hipError_t e = spa::launch_project_bf16(Q, K, P, w + wl.qs, w + wl.kt, 2, B * H, H, N, d, m,

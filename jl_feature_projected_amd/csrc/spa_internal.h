@@ -87,6 +87,18 @@ hipError_t launch_attn_f32(const float* Qt, const float* Kt, const float* V, flo
                            float* lse, int BH, int N, int m, int dv, bool causal, float scale,
                            hipStream_t stream);
 
+// Backward of the fp32 path (all fp32, row-major): inputs as passed to spa_attn_fwd plus
+// O, dO and the forward's natural-log lse; workspace Qt, Kt, dQt, dKt [B*H, N, m] and D
+// [B*H, N]; outputs dQ, dK [B*H, N, d], dV [B*H, N, dv], dP [H, d, m].
+struct BwdF32Args {
+    const float *Q, *K, *V, *P, *O, *dO, *lse;
+    float *Qt, *Kt, *D, *dQt, *dKt;
+    float *dQ, *dK, *dV, *dP;
+    int B, H, N, d, m, dv, causal;
+    float scale;
+};
+hipError_t launch_attn_bwd_f32(const BwdF32Args& a, hipStream_t stream);
+
 // Decode: Nq queries against a cache of Nk projected keys (fp16) and values (bf16) with
 // `rows` rows per head; partial results per (query, key split) in fp32.
 struct DecodeArgs {

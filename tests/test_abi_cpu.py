@@ -150,7 +150,12 @@ def _bwd(L, **kw):
     (dict(dK=E + 0x10), spa.SPA_ERR_INVALID_ARGUMENT),           # overlaps dQ
     (dict(dV=A + 0x40), spa.SPA_ERR_INVALID_ARGUMENT),           # overlaps Q
     (dict(ws_bytes=100), spa.SPA_ERR_WORKSPACE),
-    (dict(dtype=spa.SPA_F32), spa.SPA_ERR_UNSUPPORTED),
+    (dict(dtype=spa.SPA_F32, g_dtype=spa.SPA_BF16), spa.SPA_ERR_UNSUPPORTED),  # fp32: fp32 grads
+    (dict(dtype=spa.SPA_F32, d=300), spa.SPA_ERR_UNSUPPORTED),
+    (dict(dtype=spa.SPA_F32, dv=129), spa.SPA_ERR_UNSUPPORTED),
+    (dict(dtype=spa.SPA_F32, m=129), spa.SPA_ERR_UNSUPPORTED),
+    (dict(dtype=spa.SPA_F32, ws_bytes=100), spa.SPA_ERR_WORKSPACE),
+    (dict(dtype=spa.SPA_F32, dV=A + 0x40), spa.SPA_ERR_INVALID_ARGUMENT),  # overlaps Q (fp32)
     (dict(m=129), spa.SPA_ERR_UNSUPPORTED),
     (dict(d=96), spa.SPA_ERR_UNSUPPORTED),
     (dict(dv=32), spa.SPA_ERR_UNSUPPORTED),
@@ -169,7 +174,13 @@ def test_bwd_workspace_bytes(L):
              BH * np_ * 2 * 4, rows * mp * 4, rows * mp * 4, BH * 1 * d * m * 4]
     assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, m, dv, spa.SPA_BF16) == sum(a256(s) for s in sizes)
     assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, 129, dv, spa.SPA_BF16) == 0
-    assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, m, dv, spa.SPA_F32) == 0
+    # fp32 path: projected queries, keys and their gradients (fp32, m wide), then D
+    f32 = [rows * m * 4] * 4 + [rows * 4]
+    assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, m, dv, spa.SPA_F32) == sum(a256(s) for s in f32)
+    assert L.spa_attn_bwd_workspace_bytes(1, 2, N, 96, 5, 40, spa.SPA_F32) == \
+        sum(a256(s) for s in [rows * 5 * 4] * 4 + [rows * 4])
+    assert L.spa_attn_bwd_workspace_bytes(1, 2, N, 300, m, dv, spa.SPA_F32) == 0
+    assert L.spa_attn_bwd_workspace_bytes(1, 2, N, d, 129, dv, spa.SPA_F32) == 0
 
 
 def _decode(L, **kw):
