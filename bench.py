@@ -103,11 +103,11 @@ def cpu_baseline(w: inputs.Workload, x: inputs.Inputs, budget_s: float = 12.0) -
 def time_backward(w, x, Q, K, V, P, steps, warmup, dev) -> dict:
     """spa_attn_bwd on the forward's own output and lse, dO a seeded N(0, 1) draw; steps
     calls timed between events on the launch stream after warmup calls."""
-    O, lse = spa.spa_attn_fwd(Q, K, V, P, w.scale, w.causal, out_dtype=torch.bfloat16,
-                              return_lse=True)
+    f32 = Q.dtype == torch.float32  # the fp32 path: fp32 O, dO and gradients
+    O, lse = spa.spa_attn_fwd(Q, K, V, P, w.scale, w.causal,
+                              out_dtype=torch.float32 if f32 else torch.bfloat16, return_lse=True)
     dO = inputs.draw_grad_output(w, seed=w.seed + 1).to(dev)
-    ws = torch.empty(spa.spa_attn_bwd_workspace_bytes(w.B, w.H, w.N, w.d, w.m, w.dv,
-                                                      torch.bfloat16),
+    ws = torch.empty(spa.spa_attn_bwd_workspace_bytes(w.B, w.H, w.N, w.d, w.m, w.dv, Q.dtype),
                      dtype=torch.uint8, device=dev)
 
     def bstep():
@@ -126,10 +126,12 @@ def time_backward(w, x, Q, K, V, P, steps, warmup, dev) -> dict:
     ms = e0.elapsed_time(e1) / steps
     bw = accounting.bwd_work(w.B, w.H, w.N, w.d, w.m, w.dv, w.causal)
     tf = bw.total_flops / (ms * 1e-3) / 1e12
+    peak = accounting.PEAK_FP32_VECTOR_TFLOPS if f32 else accounting.PEAK_BF16_DENSE_TFLOPS
     return {"ms_per_call": round(ms, 5), "value": round(tf, 3), "unit": "TFLOP/s",
-            "pct_of_bf16_peak": round(100.0 * tf / accounting.PEAK_BF16_DENSE_TFLOPS, 2),
-            "flops_per_call": bw.total_flops, "executed_n2_flops_per_call": bw.executed_n2_flops,
-            "grad_dtype": "f32"}
+            "dtype": "f32" if f32 else "bf16",
+            "pct_of_peak": round(100.0 * tf / peak, 2),
+            "peak": peak, "flops_per_call": bw.total_flops,
+            "executed_n2_flops_per_call": bw.executed_n2_flops, "grad_dtype": "f32"}
 
 
 def time_decode(w, x, P, steps, warmup, dev) -> dict:
@@ -282,7 +284,7 @@ def main() -> int:
     work = accounting.work(w.B, w.H, w.N, w.d, w.m, w.dv, w.causal)
     ms_per_step = max(wall * 1e3, ev_ms) / args.steps
     value = work.total_flops / (ms_per_step * 1e-3) / 1e12
-    peak = accounting.PEAK_BF16_DENSE_TFLOPS if w.dtype == "bf16" else accounting.PEAK_FP32_MATRIX_TFLOPS
+    peak = accounting.PEAK_BF16_DENSE_TFLOPS if w.dtype == "bf16" else accounting.PEAK_FP32_VECTOR_TFLOPS
     attn_avg_ms = attn_ms / calls
     achieved = work.attn_flops / (attn_avg_ms * 1e-3) / 1e12
     bytes_ = accounting.path_bytes(w.B, w.H, w.N, w.d, w.m, w.dv,
@@ -312,7 +314,7 @@ def main() -> int:
                     "calls": len(per_call)},
         "roofline": {
             "kernel": "attn_bf16_kernel" if w.dtype == "bf16" else "attn_f32_kernel",
-            "bound": "mfma",
+            "bound": "mfma" if w.dtype == "bf16" else "alu",
             "achieved": round(achieved, 3),
             "peak": peak,
             "unit": "TFLOP/s",
@@ -321,7 +323,7 @@ def main() -> int:
             "algorithmic_bytes": bytes_["attn"],
         },
     }
-    if args.backward and w.dtype == "bf16":
+    if args.backward:
         res["backward"] = time_backward(w, x, Q, K, V, P, args.steps, args.warmup, dev)
     if args.sfa and w.dtype == "bf16":
         res["sfa"] = time_sfa(w, Q, K, V, args.sfa, args.steps, args.warmup, dev)

@@ -102,5 +102,5 @@ def materialised_logits_bytes(N: int, bytes_per_logit: int = 4) -> int:
 
 # MI355X published peaks used as roofline denominators.
 PEAK_BF16_DENSE_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk/CU
-PEAK_FP32_MATRIX_TFLOPS = 157.3
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # 256 CU x 2.4 GHz x 256 flop/clk/CU (128 fp32 FMA lanes)
 PEAK_HBM_GBS = 8000.0
