@@ -216,8 +216,8 @@ spa_status_t spa_kcache_append(const void* K, const void* P, void* cache, int B,
 
 /*
  * spa_attn_decode_workspace_bytes -- bytes of scratch spa_attn_decode needs (per query and
- * key split dv + 2 floats, per query 128 floats for its projection), 0 if the shape is
- * invalid or unsupported.
+ * key split dv + 2 floats: the split's unnormalised output, running maximum and sum), 0 if
+ * the shape is invalid or unsupported.
  */
 size_t spa_attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int dv);
 

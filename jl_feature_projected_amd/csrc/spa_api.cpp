@@ -394,8 +394,7 @@ size_t spa_attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int dv) {
         (long long)B * H * Nk >= kMaxRows)
         return 0;
     const spa::DecodeSplit sp = spa::decode_split(B * H, Nq, Nk);
-    return (size_t)B * H * Nq * sp.nsplit * ((size_t)dv + 2) * sizeof(float) +
-           (size_t)B * H * Nq * 128 * sizeof(float);
+    return (size_t)B * H * Nq * sp.nsplit * ((size_t)dv + 2) * sizeof(float);
 }
 
 spa_status_t spa_attn_decode(const void* Q, const void* cache, const void* Vc, const void* P,
@@ -472,7 +471,6 @@ spa_status_t spa_attn_decode(const void* Q, const void* cache, const void* Vc, c
     a.lse = lse;
     a.partO = static_cast<float*>(ws);
     a.partML = static_cast<float*>(ws) + (size_t)bh * Nq * sp.nsplit * dv;
-    a.qt = a.partML + (size_t)bh * Nq * sp.nsplit * 2;
     a.qscale = scale * 1.44269504088896340736f;
     a.causal = causal;
     a.BH = B * H;

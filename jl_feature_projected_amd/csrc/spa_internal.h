@@ -110,7 +110,6 @@ struct DecodeArgs {
     float* lse;          // [BH, Nq] or null
     float* partO;        // [BH, Nq, nsplit, dv]
     float* partML;       // [BH, Nq, nsplit, 2]: running max (base 2), sum
-    float* qt;           // [BH, Nq, m]: projected queries times qscale
     float qscale;        // scale * log2(e)
     int causal, BH, H, Nq, Nk, rows, d, m, dv, o_f32, nsplit, chunk;
 };
