@@ -229,7 +229,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: every (batch, head) is independent and this build "
+        print("bench.py measures one GPU: every (batch, head) is independent, and the library "
               "has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
