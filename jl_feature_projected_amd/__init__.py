@@ -119,6 +119,13 @@ def _device_tensor(x, name: str):
     return x
 
 
+def _same_device(ref, *others) -> None:
+    """Every tensor (None skipped) must live on ref's device: the kernels run there."""
+    for x in others:
+        if x is not None and x.device != ref.device:
+            raise ValueError(f"all tensors must be on {ref.device}; got one on {x.device}")
+
+
 def _stream_ptr(device) -> int:
     return _torch().cuda.current_stream(device).cuda_stream
 
@@ -183,6 +190,7 @@ def spa_attn_fwd(Q, K, V, P, scale: float | None = None, causal: bool = False,
     if workspace is not None:
         _device_tensor(workspace, "workspace")
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _same_device(Q, out, workspace)
     check(lib().spa_attn_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(), P.data_ptr(),
                              float(scale), int(bool(causal)), B, H, N, d, m, dv,
                              _dtype_code(dt), out.data_ptr(), _dtype_code(odt),
@@ -223,6 +231,7 @@ def spa_attn_bwd(Q, K, V, P, O, dO, lse, scale: float | None = None, causal: boo
     dt = Q.dtype
     if any(x.dtype != dt for x in (K, V, P, O, dO)):
         raise ValueError("Q, K, V, P, O and dO must share a dtype")
+    _same_device(Q, K, V, P, O, dO, lse, workspace)
     gdt = torch.float32 if grad_dtype is None else grad_dtype
     dQ = torch.empty((B, H, N, d), dtype=gdt, device=Q.device)
     dK = torch.empty((B, H, N, d), dtype=gdt, device=Q.device)
@@ -260,6 +269,7 @@ def spa_sfa_fwd(Q, K, V, topk: int, scale: float | None = None, causal: bool = F
     dv = V.shape[3]
     if K.dtype != Q.dtype or V.dtype != Q.dtype:
         raise ValueError("Q, K and V must share a dtype")
+    _same_device(Q, K, V, workspace)
     odt = torch.float32 if out_dtype is None else out_dtype
     O = torch.empty((B, H, N, dv), dtype=odt, device=Q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=Q.device) if return_lse else None
@@ -296,6 +306,7 @@ def spa_kcache_append(K, P, cache, row0: int) -> None:
         raise ValueError("the key cache is float16")
     if K.dtype != P.dtype:
         raise ValueError("K and P must share a dtype")
+    _same_device(K, P, cache)
     check(lib().spa_kcache_append(K.data_ptr(), P.data_ptr(), cache.data_ptr(), B, H, N, d, m,
                                   cache.shape[2], int(row0), _dtype_code(K.dtype),
                                   _stream_ptr(K.device)))
@@ -328,6 +339,7 @@ def spa_attn_decode(Q, cache, Vc, P, Nk: int, scale: float | None = None, causal
         raise ValueError("the key cache is float16")
     if Q.dtype != Vc.dtype or Q.dtype != P.dtype:
         raise ValueError("Q, Vc and P must share a dtype")
+    _same_device(Q, cache, Vc, P, workspace)
     odt = torch.float32 if out_dtype is None else out_dtype
     O = torch.empty((B, H, Nq, dv), dtype=odt, device=Q.device)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=Q.device) if return_lse else None

@@ -271,3 +271,11 @@ def test_sfa_fwd_rejects_on_host(L):
     assert L.spa_sfa_fwd_workspace_bytes(1, 2, 256, 128, 128) == \
         L.spa_attn_fwd_workspace_bytes(1, 2, 256, 128, 128, 128, spa.SPA_BF16)
     assert L.spa_sfa_fwd_workspace_bytes(1, 2, 256, 96, 128) == 0
+
+
+def test_binding_rejects_tensors_on_other_devices():
+    """The kernels run on the first tensor's device; the binding refuses any other."""
+    from types import SimpleNamespace as T
+    spa._same_device(T(device="cuda:0"), T(device="cuda:0"), None)
+    with pytest.raises(ValueError):
+        spa._same_device(T(device="cuda:0"), T(device="cuda:0"), T(device="cuda:1"))
