@@ -10,11 +10,12 @@
 // results). Dense 32x32x16 MFMAs over d <= 128 features cost d/16 instructions per 32x32
 // score tile, far less than scattering the support intersections.
 //
-// A workgroup of 16 waves per (head, 256 tokens), each wave 16 rows whose loads are all
-// issued first. Per row the lanes hold d/64 consecutive features each; the k-th largest
-// magnitude T is found by a bitwise search over the 15 magnitude bits of bf16 with wave
-// ballots counting the features at or above a candidate (wave-uniform, scalar counts);
-// features above T are kept, and of those equal to T the (k - #above) of lowest index.
+// A workgroup of 16 waves per (head, 256 tokens), each wave 16 rows, loaded eight at a
+// time. Per row the lanes hold d/64 consecutive features each; the k-th largest magnitude T
+// is found by a bitwise search over the 15 magnitude bits of bf16 with wave ballots
+// counting the features at or above a candidate (wave-uniform, scalar counts), eight rows'
+// searches interleaved; features above T are kept, and of those equal to T the
+// (k - #above) of lowest index.
 #include "spa_device.h"
 #include "spa_internal.h"
 
@@ -44,68 +45,82 @@ __global__ __launch_bounds__(kTopkThreads) void sfa_topk_kernel(
     float nmax = 0.0f;  // largest squared norm of a selected key row in this wave
 
     const int tok0 = blk * kProjBlockTokens + wave * kTopkRows;
-    uint32_t raw[kTopkRows];  // the wave's rows: this lane's d/64 features of each
+    // Rows in groups of RG: the groups' bitwise searches run side by side, so their chains
+    // of wave-uniform counts and selects overlap instead of waiting on each other.
+    constexpr int RG = 8;
+    static_assert(kTopkRows % RG == 0, "row groups");
+#pragma unroll 1
+    for (int r0 = 0; r0 < kTopkRows; r0 += RG) {
+        if (tok0 + r0 >= N) break;  // wave-uniform
+        uint32_t raw[RG];           // this lane's d/64 features of each row of the group
 #pragma unroll
-    for (int r = 0; r < kTopkRows; ++r) {
-        const int tok = tok0 + r;
-        raw[r] = 0u;
-        if (tok < N)
-            raw[r] = E == 2 ? *reinterpret_cast<const uint32_t*>(X + (size_t)tok * D + 2 * lane)
-                            : (uint32_t)X[(size_t)tok * D + lane];
-    }
+        for (int g = 0; g < RG; ++g) {
+            const int tok = tok0 + r0 + g;
+            raw[g] = 0u;
+            if (tok < N)
+                raw[g] = E == 2 ? *reinterpret_cast<const uint32_t*>(X + (size_t)tok * D + 2 * lane)
+                                : (uint32_t)X[(size_t)tok * D + lane];
+        }
+        uint16_t x[RG][E];
+        uint32_t mag[RG][E], t[RG];
 #pragma unroll
-    for (int r = 0; r < kTopkRows; ++r) {  // unrolled: raw[] stays in registers
-        const int tok = tok0 + r;
-        if (tok >= N) break;  // wave-uniform
-        uint16_t x[E];
-        x[0] = (uint16_t)(raw[r] & 0xffffu);
-        if (E == 2) x[E - 1] = (uint16_t)(raw[r] >> 16);
-        uint32_t mag[E];
+        for (int g = 0; g < RG; ++g) {
+            x[g][0] = (uint16_t)(raw[g] & 0xffffu);
+            if (E == 2) x[g][E - 1] = (uint16_t)(raw[g] >> 16);
 #pragma unroll
-        for (int e = 0; e < E; ++e) mag[e] = x[e] & 0x7fffu;
-        // T = the largest t with #{mag >= t} >= k
-        uint32_t t = 0;
+            for (int e = 0; e < E; ++e) mag[g][e] = x[g][e] & 0x7fffu;
+            t[g] = 0;
+        }
+        // T = the largest t with #{mag >= t} >= k, per row
 #pragma unroll 1
         for (int bit = 14; bit >= 0; --bit) {
-            const uint32_t cand = t | (1u << bit);
-            int cnt = 0;
 #pragma unroll
-            for (int e = 0; e < E; ++e) cnt += popc64(__ballot(mag[e] >= cand));
-            if (cnt >= k) t = cand;
+            for (int g = 0; g < RG; ++g) {
+                const uint32_t cand = t[g] | (1u << bit);
+                int cnt = 0;
+#pragma unroll
+                for (int e = 0; e < E; ++e) cnt += popc64(__ballot(mag[g][e] >= cand));
+                t[g] = __builtin_amdgcn_readfirstlane(cnt >= k ? cand : t[g]);
+            }
         }
-        int above = 0;
-        uint64_t tie[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            above += popc64(__ballot(mag[e] > t));
-            tie[e] = __ballot(mag[e] == t);
-        }
-        const int need = k - above;  // ties to keep, lowest feature index first
-        int rank = 0;                // ties at lower feature indices than this lane's first
+        for (int g = 0; g < RG; ++g) {
+            const int tok = tok0 + r0 + g;
+            if (tok >= N) break;  // wave-uniform
+            int above = 0;
+            uint64_t tie[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) rank += popc64(tie[e] & below);
-        float n2 = 0.0f;
-        uint16_t out[E];
+            for (int e = 0; e < E; ++e) {
+                above += popc64(__ballot(mag[g][e] > t[g]));
+                tie[e] = __ballot(mag[g][e] == t[g]);
+            }
+            const int need = k - above;  // ties to keep, lowest feature index first
+            int rank = 0;                // ties at lower feature indices than this lane's first
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const bool is_tie = mag[e] == t;
-            const bool keep = mag[e] > t || (is_tie && rank < need);
-            rank += is_tie ? 1 : 0;
-            const float v = keep ? __uint_as_float((uint32_t)x[e] << 16) * sc : 0.0f;
-            const uint32_t h = pack_f16x2(v, 0.0f) & 0xffffu;
-            out[e] = (uint16_t)h;
-            const float hv = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-            n2 += hv * hv;
-        }
-        if (E == 2)
-            *reinterpret_cast<uint32_t*>(Y + (size_t)tok * D + 2 * lane) =
-                (uint32_t)out[0] | ((uint32_t)out[E - 1] << 16);
-        else
-            Y[(size_t)tok * D + lane] = out[0];
-        if (z) {
+            for (int e = 0; e < E; ++e) rank += popc64(tie[e] & below);
+            float n2 = 0.0f;
+            uint16_t out[E];
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) n2 += __shfl_xor(n2, o, 64);
-            nmax = fmaxf(nmax, n2);
+            for (int e = 0; e < E; ++e) {
+                const bool is_tie = mag[g][e] == t[g];
+                const bool keep = mag[g][e] > t[g] || (is_tie && rank < need);
+                rank += is_tie ? 1 : 0;
+                const float v = keep ? __uint_as_float((uint32_t)x[g][e] << 16) * sc : 0.0f;
+                const uint32_t h = pack_f16x2(v, 0.0f) & 0xffffu;
+                out[e] = (uint16_t)h;
+                const float hv = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+                n2 += hv * hv;
+            }
+            if (E == 2)
+                *reinterpret_cast<uint32_t*>(Y + (size_t)tok * D + 2 * lane) =
+                    (uint32_t)out[0] | ((uint32_t)out[E - 1] << 16);
+            else
+                Y[(size_t)tok * D + lane] = out[0];
+            if (z) {
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) n2 += __shfl_xor(n2, o, 64);
+                nmax = fmaxf(nmax, n2);
+            }
         }
     }
     if (z) {
