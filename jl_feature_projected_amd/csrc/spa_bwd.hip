@@ -541,7 +541,7 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
 }
 
 template <int D, int MP>
-__global__ __launch_bounds__(kThreads, 2) void proj_grad_kernel(
+__global__ __launch_bounds__(kThreads, MP >= 128 ? 1 : 2) void proj_grad_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const float* __restrict__ dQt,
     const float* __restrict__ dKt, const uint16_t* __restrict__ P, void* __restrict__ dQ,
     void* __restrict__ dK, int out_f32, float* __restrict__ part, int N, int H, int m, int nch) {

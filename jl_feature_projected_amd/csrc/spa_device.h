@@ -97,6 +97,10 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
 // otherwise wait for the copy before the first read. The copy's completion is awaited
 // explicitly (vmcnt) before the barrier that hands the buffer over. Device pass only: the
 // host pass does not parse AMDGPU assembly constraints.
+// The copies set M0 themselves and list it as clobbered, which is what tells the compiler
+// not to keep a value there across them; clang notes that M0 is a reserved register.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void copy16_to_lds(u32x4 rsrc, uint32_t m0, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
@@ -135,6 +139,7 @@ __device__ __forceinline__ void copy4_to_lds(u32x4 rsrc, uint32_t m0, uint32_t v
                  : "m0");
 #endif
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
 // (expcnt and lgkmcnt left at their maxima, i.e. not waited on).
