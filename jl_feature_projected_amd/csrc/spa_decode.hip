@@ -320,11 +320,13 @@ DecodeSplit decode_split(int BH, int Nq, int Nk) {
     const int qn = Nq == 1 ? 1 : Nq <= 4 ? 4 : 16;
     const long long base = (long long)BH * ((Nq + qn - 1) / qn);
     const int blocks = (Nk + kDecKeys - 1) / kDecKeys;
-    // about four workgroups per CU in total, at least one key block per split
+    // about four workgroups per CU in total, at least two key blocks per split (a split's
+    // second block of rows is requested while its first is reduced), one if there is one
     long long want = (1024 + base - 1) / base;
     if (want > blocks) want = blocks;
     if (want < 1) want = 1;
-    const int per = (int)((blocks + want - 1) / want);
+    int per = (int)((blocks + want - 1) / want);
+    if (per < 2) per = blocks < 2 ? blocks : 2;
     DecodeSplit r;
     r.chunk = per * kDecKeys;
     r.nsplit = (Nk + r.chunk - 1) / r.chunk;

@@ -239,8 +239,10 @@ def test_kcache_append_rejects_on_host(L):
 
 def test_decode_workspace_bytes(L):
     # B*H*Nq*nsplit*(dv+2) floats; nsplit from the split rule (about 1024 workgroups, at
-    # least 256 keys per split): 32 heads, one query, 32768 keys -> 32 splits of 1024 keys
+    # least two 256-key blocks per split when the cache has two): 32 heads, one query,
+    # 32768 keys -> 32 splits of 1024 keys; 8192 keys -> 16 splits of 512 (not 32 of 256)
     assert L.spa_attn_decode_workspace_bytes(1, 32, 1, 32768, 128) == 32 * 1 * 32 * 130 * 4
+    assert L.spa_attn_decode_workspace_bytes(2, 16, 1, 8192, 128) == 32 * 1 * 16 * 130 * 4
     assert L.spa_attn_decode_workspace_bytes(1, 1, 1, 100, 64) == 1 * 1 * 1 * 66 * 4
     assert L.spa_attn_decode_workspace_bytes(1, 2, 17, 16, 128) == 0  # Nq > Nk
 
