@@ -10,121 +10,123 @@
 // results). Dense 32x32x16 MFMAs over d <= 128 features cost d/16 instructions per 32x32
 // score tile, far less than scattering the support intersections.
 //
-// A workgroup of 16 waves per (head, 256 tokens), each wave 16 rows, loaded eight at a
-// time. Per row the lanes hold d/64 consecutive features each; the k-th largest magnitude T
-// is found by a bitwise search over the 15 magnitude bits of bf16 with wave ballots
-// counting the features at or above a candidate (wave-uniform, scalar counts), eight rows'
-// searches interleaved; features above T are kept, and of those equal to T the
-// (k - #above) of lowest index.
+// A workgroup of 256 threads per (head, 256 tokens), one thread per row: the row's d
+// features sit in the thread's registers as packed bf16 pairs, so every count below is plain
+// vector arithmetic (the earlier layout, a row spread over a wave with ballot counts, was
+// bound by the one scalar unit per CU that summed the ballots). The k-th largest magnitude T
+// is found by a bitwise search over the 15 magnitude bits of bf16; features above T are
+// kept, and of those equal to T the (k - #above) of lowest index.
 #include "spa_device.h"
 #include "spa_internal.h"
 
 namespace spa {
 namespace {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkRows = kProjBlockTokens / (kTopkThreads / 64);  // rows per wave
+constexpr int kTopkThreads = kProjBlockTokens;  // one thread per row of a 256-row block
 
-__device__ __forceinline__ int popc64(uint64_t x) { return __builtin_popcountll(x); }
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Number of features among the packed pairs mag[0 .. W) whose magnitude is >= cand, times 8.
+// Per 16-bit half, mag + (0x8000 - cand) has bit 15 set exactly when mag >= cand (both terms
+// are below 0x8000, so nothing carries out of the half); the permute's sign-replicating
+// selectors turn the four indicator bits of two pairs into four 0x00 / 0xff bytes, and one
+// bit count with accumulate adds them.
+template <int W>
+__device__ __forceinline__ uint32_t count_ge8(const uint32_t (&mag)[W], uint32_t cand) {
+    const uint32_t c = (0x8000u - cand) * 0x10001u;
+    const u16x2 cv = __builtin_bit_cast(u16x2, c);
+    uint32_t n = 0;
+#pragma unroll
+    for (int j = 0; j < W; j += 2) {
+        const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, mag[j]) + cv);
+        const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, mag[j + 1]) + cv);
+        n += __builtin_popcount(__builtin_amdgcn_perm(b, a, 0x0b0a0908u));
+    }
+    return n;
+}
 
 template <int D>
 __global__ __launch_bounds__(kTopkThreads) void sfa_topk_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, uint16_t* __restrict__ Qt,
     uint16_t* __restrict__ Kt, float* __restrict__ kmax, int N, int k, float qscale, int nblk) {
-    constexpr int E = D / 64;  // features per lane
+    constexpr int W = D / 2;   // packed bf16 pairs per row
+    constexpr int L = D / 8;   // 16-byte pieces per row
+    static_assert(W % 4 == 0, "rows move in 16-byte pieces");
     __shared__ float wave_max[kTopkThreads / 64];
     const int z = blockIdx.x & 1;  // 0: queries, 1: keys
     const int rest = blockIdx.x >> 1;
     const int blk = rest % nblk;
     const int bh = rest / nblk;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const uint16_t* X = (z ? K : Q) + (size_t)bh * N * D;
-    uint16_t* Y = (z ? Kt : Qt) + (size_t)bh * N * D;
+    const int tok = blk * kProjBlockTokens + (int)threadIdx.x;
+    const bool live = tok < N;
+    const size_t row = ((size_t)bh * N + (live ? tok : 0)) * D;
     const float sc = z ? 1.0f : qscale;
-    const uint64_t below = (1ull << lane) - 1ull;
-    float nmax = 0.0f;  // largest squared norm of a selected key row in this wave
 
-    const int tok0 = blk * kProjBlockTokens + wave * kTopkRows;
-    // Rows in groups of RG: the groups' bitwise searches run side by side, so their chains
-    // of wave-uniform counts and selects overlap instead of waiting on each other.
-    constexpr int RG = 8;
-    static_assert(kTopkRows % RG == 0, "row groups");
+    uint32_t raw[W], mag[W];
+    if (live) {
+        const uint4* src = reinterpret_cast<const uint4*>((z ? K : Q) + row);
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const uint4 v = src[i];
+            raw[4 * i] = v.x;
+            raw[4 * i + 1] = v.y;
+            raw[4 * i + 2] = v.z;
+            raw[4 * i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < W; ++j) raw[j] = 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < W; ++j) mag[j] = raw[j] & 0x7fff7fffu;
+
+    // T = the largest t with #{features with magnitude >= t} >= k; n8 = 8 * that count.
+    const uint32_t k8 = 8u * (uint32_t)k;
+    uint32_t t = 0, n8 = 8u * D;
 #pragma unroll 1
-    for (int r0 = 0; r0 < kTopkRows; r0 += RG) {
-        if (tok0 + r0 >= N) break;  // wave-uniform
-        uint32_t raw[RG];           // this lane's d/64 features of each row of the group
+    for (int bit = 14; bit >= 0; --bit) {
+        const uint32_t cand = t | (1u << bit);
+        const uint32_t n = count_ge8(mag, cand);
+        const bool take = n >= k8;
+        t = take ? cand : t;
+        n8 = take ? n : n8;
+    }
+
+    // Keep every feature of magnitude >= T except the last (#{>= T} - k) of those equal to T,
+    // i.e. the ties of highest index: walk the features from the end with that many drops.
+    int drop = (int)((n8 - k8) >> 3);
+    const int ti = (int)t;
+    uint32_t outw[W];
+    float n2 = 0.0f;
 #pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            const int tok = tok0 + r0 + g;
-            raw[g] = 0u;
-            if (tok < N)
-                raw[g] = E == 2 ? *reinterpret_cast<const uint32_t*>(X + (size_t)tok * D + 2 * lane)
-                                : (uint32_t)X[(size_t)tok * D + lane];
-        }
-        uint16_t x[RG][E];
-        uint32_t mag[RG][E], t[RG];
-#pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            x[g][0] = (uint16_t)(raw[g] & 0xffffu);
-            if (E == 2) x[g][E - 1] = (uint16_t)(raw[g] >> 16);
-#pragma unroll
-            for (int e = 0; e < E; ++e) mag[g][e] = x[g][e] & 0x7fffu;
-            t[g] = 0;
-        }
-        // T = the largest t with #{mag >= t} >= k, per row
-#pragma unroll 1
-        for (int bit = 14; bit >= 0; --bit) {
-#pragma unroll
-            for (int g = 0; g < RG; ++g) {
-                const uint32_t cand = t[g] | (1u << bit);
-                int cnt = 0;
-#pragma unroll
-                for (int e = 0; e < E; ++e) cnt += popc64(__ballot(mag[g][e] >= cand));
-                t[g] = __builtin_amdgcn_readfirstlane(cnt >= k ? cand : t[g]);
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            const int tok = tok0 + r0 + g;
-            if (tok >= N) break;  // wave-uniform
-            int above = 0;
-            uint64_t tie[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                above += popc64(__ballot(mag[g][e] > t[g]));
-                tie[e] = __ballot(mag[g][e] == t[g]);
-            }
-            const int need = k - above;  // ties to keep, lowest feature index first
-            int rank = 0;                // ties at lower feature indices than this lane's first
-#pragma unroll
-            for (int e = 0; e < E; ++e) rank += popc64(tie[e] & below);
-            float n2 = 0.0f;
-            uint16_t out[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const bool is_tie = mag[g][e] == t[g];
-                const bool keep = mag[g][e] > t[g] || (is_tie && rank < need);
-                rank += is_tie ? 1 : 0;
-                const float v = keep ? __uint_as_float((uint32_t)x[g][e] << 16) * sc : 0.0f;
-                const uint32_t h = pack_f16x2(v, 0.0f) & 0xffffu;
-                out[e] = (uint16_t)h;
-                const float hv = (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-                n2 += hv * hv;
-            }
-            if (E == 2)
-                *reinterpret_cast<uint32_t*>(Y + (size_t)tok * D + 2 * lane) =
-                    (uint32_t)out[0] | ((uint32_t)out[E - 1] << 16);
-            else
-                Y[(size_t)tok * D + lane] = out[0];
-            if (z) {
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) n2 += __shfl_xor(n2, o, 64);
-                nmax = fmaxf(nmax, n2);
-            }
+    for (int j = W - 1; j >= 0; --j) {
+        const int shi = (int)(mag[j] >> 16) - ti;
+        const int keep_hi = shi - min(max(drop, 0), 1);  // >= 0: kept
+        drop -= shi == 0 ? 1 : 0;
+        const int slo = (int)(mag[j] & 0xffffu) - ti;
+        const int keep_lo = slo - min(max(drop, 0), 1);
+        drop -= slo == 0 ? 1 : 0;
+        const float vlo = keep_lo >= 0 ? __uint_as_float(raw[j] << 16) * sc : 0.0f;
+        const float vhi = keep_hi >= 0 ? __uint_as_float(raw[j] & 0xffff0000u) * sc : 0.0f;
+        outw[j] = pack_f16x2(vlo, vhi);
+        if (z) {
+            const float hlo = (float)__builtin_bit_cast(_Float16, (uint16_t)(outw[j] & 0xffffu));
+            const float hhi = (float)__builtin_bit_cast(_Float16, (uint16_t)(outw[j] >> 16));
+            n2 += hlo * hlo + hhi * hhi;
         }
     }
+    if (live) {
+        uint4* dst = reinterpret_cast<uint4*>((z ? Kt : Qt) + row);
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+            dst[i] = make_uint4(outw[4 * i], outw[4 * i + 1], outw[4 * i + 2], outw[4 * i + 3]);
+    }
     if (z) {
-        if (lane == 0) wave_max[wave] = nmax;
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        if (!live) n2 = 0.0f;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) n2 = fmaxf(n2, __shfl_xor(n2, o, 64));
+        if (lane == 0) wave_max[wave] = n2;
         __syncthreads();
         if (threadIdx.x == 0) {
             float b = wave_max[0];
