@@ -742,9 +742,22 @@ __global__ __launch_bounds__(kThreads) void dp_reduce_kernel(const float* __rest
     const int i = blockIdx.x * kThreads + threadIdx.x;
     if (i >= H * nout) return;
     const int h = i / nout, e = i - h * nout;
+    // Sixteen loads in flight before their adds (same order of the sums): the partials come
+    // from L2 or HBM, and one wave per SIMD cannot hide one latency per add.
+    constexpr int U = 16;
     float acc = 0.0f;
-    for (int b = 0; b < B; ++b)
-        for (int ch = 0; ch < nch; ++ch) acc += part[(((size_t)(b * H + h)) * nch + ch) * nout + e];
+    for (int b = 0; b < B; ++b) {
+        const float* p = part + ((size_t)(b * H + h) * nch) * nout + e;
+        int ch = 0;
+        for (; ch + U <= nch; ch += U) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = p[(size_t)(ch + u) * nout];
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc += v[u];
+        }
+        for (; ch < nch; ++ch) acc += p[(size_t)ch * nout];
+    }
     dP[i] = acc;
 }
 
