@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     const uint16_t* __restrict__ Vc, const uint16_t* __restrict__ P, float qscale, int causal,
     int H, int Nq, int Nk, int rows, int d, int m, int nqg, int nsplit, int chunk,
     float* __restrict__ partO, float* __restrict__ partML) {
-    constexpr int COLS = QN <= 4 ? 8 : 2;    // V columns per thread
+    constexpr int COLS = QN <= 4 ? 8 : QN <= 8 ? 4 : 2;  // V columns per thread
     constexpr int CT = DV / COLS;            // threads per V row
     constexpr int KG = kDecThreads / CT;     // key groups
     constexpr int KPG = kDecKeys / KG;       // keys per group per block
@@ -109,11 +109,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
 #pragma unroll
         for (int j = 0; j < KPG; ++j) {
             const int key = kb0 + kgi * KPG + j;
-            if (COLS == 8) {
+            if constexpr (COLS == 8) {
                 u32x4 v = {0u, 0u, 0u, 0u};
                 if (key < kend) v = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * DV + COLS * ct);
 #pragma unroll
                 for (int e = 0; e < COLS / 2; ++e) vb[j][e] = v[e];
+            } else if constexpr (COLS == 4) {
+                u32x2 v = {0u, 0u};
+                if (key < kend) v = *reinterpret_cast<const u32x2*>(Vh + (size_t)key * DV + COLS * ct);
+                vb[j][0] = v[0];
+                vb[j][1] = v[1];
             } else {
                 vb[j][0] = key < kend ? *reinterpret_cast<const uint32_t*>(Vh + (size_t)key * DV + COLS * ct) : 0u;
             }
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(DV) void decode_combine_kernel(
 
 template <int DV, int QN>
 size_t decode_lds_bytes(int d, int m) {
-    constexpr int COLS = QN <= 4 ? 8 : 2;
+    constexpr int COLS = QN <= 4 ? 8 : QN <= 8 ? 4 : 2;
     constexpr int KG = kDecThreads / (DV / COLS);
     const size_t main = sizeof(float) * ((size_t)QN * kDecKeys + (size_t)KG * QN * DV);
     const size_t stage = sizeof(uint16_t) * ((size_t)d * m + (size_t)QN * d);
@@ -311,13 +316,14 @@ template <int DV>
 hipError_t launch_dv(const DecodeArgs& a, hipStream_t s) {
     if (a.Nq == 1) return launch_qn<DV, 1>(a, s);
     if (a.Nq <= 4) return launch_qn<DV, 4>(a, s);
+    if (a.Nq <= 8) return launch_qn<DV, 8>(a, s);
     return launch_qn<DV, 16>(a, s);
 }
 
 }  // namespace
 
 DecodeSplit decode_split(int BH, int Nq, int Nk) {
-    const int qn = Nq == 1 ? 1 : Nq <= 4 ? 4 : 16;
+    const int qn = Nq == 1 ? 1 : Nq <= 4 ? 4 : Nq <= 8 ? 8 : 16;
     const long long base = (long long)BH * ((Nq + qn - 1) / qn);
     const int blocks = (Nk + kDecKeys - 1) / kDecKeys;
     // about four workgroups per CU in total, at least two key blocks per split (a split's

@@ -61,6 +61,8 @@ CASES = [  # B, H, Nq, Nk, rows, d, m, dv, causal
     (1, 2, 4, 4096, 4096, 64, 64, 64, False),
     (1, 2, 2, 65536, 65536, 128, 32, 128, True),
     (1, 1, 1, 3000, 3000, 128, 128, 128, True),
+    (1, 2, 8, 1500, 1600, 128, 32, 128, True),
+    (2, 1, 5, 700, 700, 64, 16, 64, False),
 ]
 
 
