@@ -240,11 +240,15 @@ size_t spa_attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int dv);
  *   workspace / workspace_bytes: spa_attn_decode_workspace_bytes(B, H, Nq, Nk, dv) bytes,
  *          or NULL (allocated and freed stream-ordered).
  *
- * Queries are projected in fp32; scores, an exact online softmax and the weights x V are
- * fp32 (HBM-bound: each cache byte is read once per head and group of up to 16 queries).
+ * Queries are projected in fp32. Up to four queries per head (or m not a multiple of 8):
+ * scores, an exact online softmax and the weights x V in fp32 on the vector units. More
+ * (m a multiple of 8): queries rounded to fp16 and weights to bf16 on the matrix cores,
+ * fp32 accumulation and softmax state. Each cache byte is read once per head and group of
+ * up to 16 queries.
  * Keys are split across workgroups and the splits merged in a fixed order: deterministic.
  * Errors: SPA_ERR_INVALID_ARGUMENT (nulls, dimensions, alignment, overlaps, Nq > Nk > rows),
- * SPA_ERR_UNSUPPORTED (dtype, d, m, dv), SPA_ERR_WORKSPACE, SPA_ERR_HIP. Three launches.
+ * SPA_ERR_UNSUPPORTED (dtype, d, m, dv), SPA_ERR_WORKSPACE, SPA_ERR_HIP. Two launches: the
+ * attention over the key splits, then the merge of the splits.
  */
 spa_status_t spa_attn_decode(const void* Q, const void* cache, const void* Vc, const void* P,
                              float scale, int causal, int B, int H, int Nq, int Nk, int rows,

@@ -14,8 +14,13 @@
 //   the weights times V with fp32 FMAs, each thread owning COLS columns of V (16-byte row
 //   loads for COLS = 8). Writes per (query, split) the unnormalised output, the running
 //   max and the sum.
+// decode_mq_kernel: the same work and outputs for more than four queries per head when m is
+//   a multiple of 8, on 16x16x32 MFMAs (scores against the fp16 cache rows, weights times the
+//   V rows through transposing LDS reads), 16 queries per workgroup.
 // decode_combine_kernel: per query, merges the splits in a fixed order (log-sum-exp).
 // Both are HBM-bound: every cache byte is read once per (head, query group).
+#include <algorithm>
+
 #include "spa_device.h"
 #include "spa_internal.h"
 
@@ -25,6 +30,41 @@ namespace {
 constexpr int kDecThreads = 256;
 constexpr int kDecKeys = 256;  // keys per block: one per thread in the score phase
 constexpr int kDecMaxM = 128;
+
+// The group's projected queries, qt[q][c] = scale*log2(e) * sum_k Q[q][k] P[k][c] in fp32
+// (rows past nq zero): the Q rows and P staged in LDS at `stage` (free space of the caller),
+// then 8 threads per output, each summing d/8 products, and a shuffle reduction. Ends with
+// a barrier (the staging space may be reused at once).
+template <int QN>
+__device__ __forceinline__ void project_queries(float (*qt)[kDecMaxM], char* stage,
+                                                const uint16_t* __restrict__ Q,
+                                                const uint16_t* __restrict__ P, float qscale,
+                                                int bh, int h, int Nq, int q0, int nq, int d,
+                                                int m, int tid) {
+    uint16_t* Ps = reinterpret_cast<uint16_t*>(stage);  // [d][m]
+    uint16_t* Qs = Ps + d * m;                            // [QN][d]
+    const uint16_t* Ph = P + (size_t)h * d * m;
+    for (int i = tid; i < d * m; i += kDecThreads) Ps[i] = Ph[i];
+    const uint16_t* Qh = Q + ((size_t)bh * Nq + q0) * d;
+    for (int i = tid; i < nq * d; i += kDecThreads) Qs[i] = Qh[i];
+    __syncthreads();
+    const int slice = tid & 7, per = d / 8;
+    for (int o0 = 0; o0 < QN * m; o0 += kDecThreads / 8) {
+        const int o = o0 + (tid >> 3);
+        const int q = o / m, c = o - q * m;
+        float a = 0.0f;
+        if (o < nq * m) {
+            for (int k = slice * per; k < slice * per + per; ++k)
+                a += __uint_as_float((uint32_t)Qs[q * d + k] << 16) *
+                     __uint_as_float((uint32_t)Ps[k * m + c] << 16);
+        }
+        a += __shfl_xor(a, 1, 8);
+        a += __shfl_xor(a, 2, 8);
+        a += __shfl_xor(a, 4, 8);
+        if (slice == 0 && o < QN * m) qt[q][c] = a * qscale;
+    }
+    __syncthreads();
+}
 
 template <int DV, int QN>
 __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
@@ -60,34 +100,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     const int ct = tid % CT, kgi = tid / CT;
     const int last = Nk - Nq + q0;  // absolute position of query q0 (causal limit)
 
-    // projected queries (zero rows past nq): Q rows and P staged in LDS (in the space of the
-    // score tile and of the final reduction, not yet in use), then 8 threads per output,
-    // each summing d/8 products, and a shuffle reduction
-    {
-        uint16_t* Ps = reinterpret_cast<uint16_t*>(un);  // [d][m]
-        uint16_t* Qs = Ps + d * m;                         // [QN][d]
-        const uint16_t* Ph = P + (size_t)h * d * m;
-        for (int i = tid; i < d * m; i += kDecThreads) Ps[i] = Ph[i];
-        const uint16_t* Qh = Q + ((size_t)bh * Nq + q0) * d;
-        for (int i = tid; i < nq * d; i += kDecThreads) Qs[i] = Qh[i];
-        __syncthreads();
-        const int slice = tid & 7, per = d / 8;
-        for (int o0 = 0; o0 < QN * m; o0 += kDecThreads / 8) {
-            const int o = o0 + (tid >> 3);
-            const int q = o / m, c = o - q * m;
-            float a = 0.0f;
-            if (o < nq * m) {
-                for (int k = slice * per; k < slice * per + per; ++k)
-                    a += __uint_as_float((uint32_t)Qs[q * d + k] << 16) *
-                         __uint_as_float((uint32_t)Ps[k * m + c] << 16);
-            }
-            a += __shfl_xor(a, 1, 8);
-            a += __shfl_xor(a, 2, 8);
-            a += __shfl_xor(a, 4, 8);
-            if (slice == 0 && o < QN * m) qt[q][c] = a * qscale;
-        }
-        __syncthreads();  // the staging space is reused below
-    }
+    project_queries<QN>(qt, un, Q, P, qscale, bh, h, Nq, q0, nq, d, m, tid);
     if (tid < QN) {
         Mrun[tid] = -INFINITY;
         Lrun[tid] = 0.0f;
@@ -239,6 +252,230 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     }
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// 16-key x 16-query block products on the 16x16x32 MFMAs. Operand layouts (wave64, lane l,
+// j = l % 16, g = l / 16): A (16 x 32) lane l holds A[j][8g .. 8g+7]; B (32 x 16) lane l holds
+// B[8g .. 8g+7][j]; D (16 x 16) lane l holds D[4g + r][j] at index r.
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// decode_mq_kernel: the work and the outputs of decode_attn_kernel<DV, 16> (a workgroup per
+// head, group of 16 queries and key split) on the matrix cores, for m a multiple of 8 (MK =
+// m rounded up to 32, over 32). Each wave streams its own 32-key chunks of the split (chunk
+// w, w + 4, ...) with its own exact online softmax, and the four waves' results are merged
+// at the end. Per chunk, on fp16/bf16 16x16x32 MFMAs with fp32 accumulation:
+//   S^T (16 keys x 16 queries) = Kt rows . qt^T   (per 16-key half, MK k-steps)
+//   O^T (DV x 16 queries)     += V^T . P^T       (32 keys as one k-step)
+// The score accumulator gives lane (g, j) keys 4g .. 4g+3 of each half for query j, which is
+// used directly as the B operand of the value product in that key order (half 0's four keys,
+// then half 1's). The V^T operand in the same order comes from the V rows staged in LDS
+// row-major, by transposing reads (ds_read_b64_tr_b16: within each 16 lanes, output lane j
+// gets element j % 4 of the 8 bytes addressed by lanes 4e + j / 4, e = 0..3). The chunk's Kt
+// and V rows are copied HBM -> LDS into a buffer of the wave's own (a second buffer, to copy
+// the next chunk during this one, was slower: the larger footprint costs more workgroups per
+// CU than the overlap gains); rows at or past the split's end read as zero.
+template <int DV, int MK>
+__global__ __launch_bounds__(kDecThreads) void decode_mq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
+    const uint16_t* __restrict__ Vc, const uint16_t* __restrict__ P, float qscale, int causal,
+    int H, int Nq, int Nk, int rows, int d, int m, int nqg, int nsplit, int chunk,
+    float* __restrict__ partO, float* __restrict__ partML) {
+    constexpr int QN = 16;
+    constexpr int CK = 32;                      // keys per wave step
+    constexpr int VB = CK * DV * 2;             // V rows of a chunk (bytes)
+    constexpr int NVC = VB / 1024;              // their 64-lane x 16-byte copies
+    constexpr int DB = DV / 16;
+    constexpr int NW = kDecThreads / 64;
+    extern __shared__ __attribute__((aligned(16))) char dsm[];
+    float(*qt)[kDecMaxM] = reinterpret_cast<float(*)[kDecMaxM]>(dsm);
+    char* un = dsm + QN * kDecMaxM * sizeof(float);
+
+    const int sp = blockIdx.x % nsplit;
+    const int rest = blockIdx.x / nsplit;
+    const int qg = rest % nqg;
+    const int bh = rest / nqg;
+    const int h = bh % H;
+    const int q0 = qg * QN;
+    const int nq = min(QN, Nq - q0);
+    const int kbeg = sp * chunk;
+    const int kend = min(Nk, kbeg + chunk);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, j = lane & 15, g = lane >> 4;
+    const int last = Nk - Nq + q0;  // absolute position of query q0 (causal limit)
+
+    project_queries<QN>(qt, un, Q, P, qscale, bh, h, Nq, q0, nq, d, m, tid);
+    // B operands of the scores: features 32 kk + 8g .. +7 of query j (fp16, zero past m)
+    f16x8 qb[MK];
+#pragma unroll
+    for (int kk = 0; kk < MK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = 32 * kk + 8 * g + e;
+            qb[kk][e] = (_Float16)(c < m ? qt[j][c] : 0.0f);
+        }
+    __syncthreads();  // qt and the staging space are reused below
+
+    // this wave's two buffers: [Kt rows of a chunk (KB bytes)][V rows (VB bytes)], from the
+    // start of the shared space (the projected queries are in registers now)
+    // Kt rows of a chunk: CK * m * 2 <= 2048 * MK bytes in 2 * MK copies; copies past the
+    // chunk's last kilobyte repeat it (same bytes to the same place), so every wave issues
+    // the same number of copies per chunk and the waits below are constants
+    constexpr int NKC = 2 * MK;
+    constexpr int KB = 1024 * NKC;
+    const int nkc = (CK * m * 2 + 1023) / 1024;
+    const uint32_t wbuf = lds_address(dsm) + (uint32_t)(wave * (KB + VB));
+    const char* wbuf_p = dsm + wave * (KB + VB);
+    const uint16_t* Kh = Kc + (size_t)bh * rows * m;
+    const uint16_t* Vh = Vc + (size_t)bh * rows * DV;
+    const u32x4 kr = make_rsrc(Kh, (uint32_t)kend * (uint32_t)m * 2u);
+    const u32x4 vr = make_rsrc(Vh, (uint32_t)kend * (uint32_t)DV * 2u);
+    auto copy_chunk = [&](int key0, int b) {
+        const uint32_t base = wbuf + (uint32_t)(b * (KB + VB));
+#pragma unroll
+        for (int i = 0; i < NKC; ++i) {
+            const int c = min(i, nkc - 1);
+            copy16_to_lds(kr, base + 1024 * c, (uint32_t)key0 * m * 2 + 1024 * c + 16 * lane);
+        }
+#pragma unroll
+        for (int i = 0; i < NVC; ++i) {
+            const int c = 64 * i + lane;
+            copy16_to_lds(vr, base + KB + 1024 * i,
+                          (uint32_t)(key0 + c / (DV / 8)) * DV * 2 + 16 * (c % (DV / 8)));
+        }
+    };
+
+    float mrun = -INFINITY, lrun = 0.0f;  // query j, this wave's keys
+    f32x4 acc[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int first = kbeg + CK * wave;
+    const int nck = first < kend ? (kend - first + NW * CK - 1) / (NW * CK) : 0;
+#pragma unroll 1
+    for (int i = 0; i < nck; ++i) {
+        const int key0 = first + NW * CK * i;
+        // the buffer was last read a step ago, by reads the MFMAs have consumed
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::: "memory");
+        copy_chunk(key0, 0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("" ::: "memory");
+        typedef __attribute__((address_space(3))) const char lds_char;
+        lds_char* kb = (lds_char*)wbuf_p;
+        lds_char* vb = kb + KB;
+
+        // scores (base 2) of keys key0 + 16 hf + 4g + r, query j
+        f32x4 s[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            s[hf] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < MK; ++kk) {
+                u32x4 a = {0u, 0u, 0u, 0u};
+                if (32 * kk + 8 * g < m)
+                    a = *(const __attribute__((address_space(3))) u32x4*)(kb + (16 * hf + j) * m * 2 + (32 * kk + 8 * g) * 2);
+                s[hf] = mfma16(__builtin_bit_cast(f16x8, a), qb[kk], s[hf]);
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = key0 + 16 * hf + 4 * g + r;
+                if (key >= kend || j >= nq || (causal && key > last + j)) s[hf][r] = -INFINITY;
+                mx = fmaxf(mx, s[hf][r]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(mrun, mx);
+        // weights (bf16, as the value product consumes them) and their sum
+        bf16x8 pw;
+        float ps = 0.0f;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = s[hf][r];
+                const float p = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - mn);
+                const bf16_t pb = (bf16_t)p;
+                pw[4 * hf + r] = pb;
+                ps += (float)pb;
+            }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        const float al = mrun == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mrun - mn);
+        lrun = lrun * al + ps;
+        mrun = mn;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) acc[b] *= al;
+        // V^T operand of dv block b: lane (g, 4e + q) addresses row 16 hf + 4g + e, columns
+        // 16b + 4q .. +3 of the staged V rows; hf = 0 gives the operand's first four keys
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            const int e = j >> 2, q = j & 3;
+            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vb + ((4 * g + e) * DV + 16 * b + 4 * q) * 2));
+            const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vb + ((16 + 4 * g + e) * DV + 16 * b + 4 * q) * 2));
+            // whole registers reinterpreted (inserting the 16-bit elements one by one has
+            // been compiled into a wrong permute)
+            const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+            const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{w0.x, w0.y, w1.x, w1.y});
+            acc[b] = mfma16(va, pw, acc[b]);
+        }
+    }
+
+    // merge the four waves: M = max, L = sum of l 2^(m - M), O = sum of O 2^(m - M)
+    __syncthreads();  // every wave is done with its buffers
+    float* wm = reinterpret_cast<float*>(dsm);      // [NW][QN]
+    float* wl = wm + NW * QN;                        // [NW][QN]
+    float* wo = wl + NW * QN;                        // [NW][QN][DV]
+    if (g == 0) {
+        wm[wave * QN + j] = mrun;
+        wl[wave * QN + j] = lrun;
+    }
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wo[(wave * QN + j) * DV + 16 * b + 4 * g + r] = acc[b][r];
+    __syncthreads();
+    for (int i = tid; i < QN * DV; i += kDecThreads) {
+        const int q = i / DV, c = i - q * DV;
+        if (q < nq) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w * QN + q]);
+            float o = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float mw = wm[w * QN + q];
+                const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+                o += f * wo[(w * QN + q) * DV + c];
+            }
+            partO[(((size_t)bh * Nq + q0 + q) * nsplit + sp) * DV + c] = o;
+        }
+    }
+    if (tid < nq) {
+        float M = -INFINITY, L = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, wm[w * QN + tid]);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float mw = wm[w * QN + tid];
+            L += mw == -INFINITY ? 0.0f : wl[w * QN + tid] * __builtin_amdgcn_exp2f(mw - M);
+        }
+        float* ml = partML + (((size_t)bh * Nq + q0 + tid) * nsplit + sp) * 2;
+        ml[0] = M;
+        ml[1] = L;
+    }
+}
+
 // One workgroup of DV threads per (head, query): the splits merged in split order. The
 // per-split maxima and sums are loaded by all threads at once and their weights staged in
 // LDS, so only the DV-wide partial outputs are read in the (unrolled) loop.
@@ -312,8 +549,45 @@ hipError_t launch_qn(const DecodeArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Shared bytes of decode_mq_kernel: the projection's (queries and staging), the four waves'
+// buffers, or the final merge, whichever is largest (64 KiB at most: d = m = dv = 128).
+template <int DV>
+size_t decode_mq_lds_bytes(int d, int m) {
+    const size_t proj = sizeof(float) * 16 * kDecMaxM + sizeof(uint16_t) * ((size_t)d * m + 16 * (size_t)d);
+    const size_t kb = 2048 * (size_t)((m + 31) / 32);
+    const size_t bufs = 4 * (kb + (size_t)32 * DV * 2);
+    const size_t merge = sizeof(float) * (2 * 4 * 16 + 4 * 16 * (size_t)DV);
+    return std::max(proj, std::max(bufs, merge));
+}
+
+template <int DV, int MK>
+hipError_t launch_mq(const DecodeArgs& a, hipStream_t s) {
+    const int nqg = (a.Nq + 15) / 16;
+    const long long grid = (long long)a.BH * nqg * a.nsplit;
+    if (grid > 0x7fffffffLL || a.nsplit > kCombineMaxSplits) return hipErrorInvalidConfiguration;
+    const size_t lds = decode_mq_lds_bytes<DV>(a.d, a.m);
+    if (lds > 64 * 1024) return hipErrorInvalidConfiguration;  // at most 64 KiB for d, m <= 128
+    decode_mq_kernel<DV, MK><<<dim3((unsigned)grid), kDecThreads, lds, s>>>(
+        a.Q, a.Kc, a.Vc, a.P, a.qscale, a.causal, a.H, a.Nq, a.Nk, a.rows, a.d, a.m, nqg,
+        a.nsplit, a.chunk, a.partO, a.partML);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    decode_combine_kernel<DV><<<dim3((unsigned)((long long)a.BH * a.Nq)), DV, 0, s>>>(
+        a.partO, a.partML, a.O, a.o_f32, a.lse, a.nsplit);
+    return hipGetLastError();
+}
+
 template <int DV>
 hipError_t launch_dv(const DecodeArgs& a, hipStream_t s) {
+    // more than four queries per head and m a multiple of 8: the matrix-core kernel
+    if (a.Nq > 4 && a.m % 8 == 0) {
+        switch ((a.m + 31) / 32) {
+            case 1: return launch_mq<DV, 1>(a, s);
+            case 2: return launch_mq<DV, 2>(a, s);
+            case 3: return launch_mq<DV, 3>(a, s);
+            default: return launch_mq<DV, 4>(a, s);
+        }
+    }
     if (a.Nq == 1) return launch_qn<DV, 1>(a, s);
     if (a.Nq <= 4) return launch_qn<DV, 4>(a, s);
     if (a.Nq <= 8) return launch_qn<DV, 8>(a, s);

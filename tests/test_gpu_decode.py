@@ -63,6 +63,11 @@ CASES = [  # B, H, Nq, Nk, rows, d, m, dv, causal
     (1, 1, 1, 3000, 3000, 128, 128, 128, True),
     (1, 2, 8, 1500, 1600, 128, 32, 128, True),
     (2, 1, 5, 700, 700, 64, 16, 64, False),
+    (1, 2, 24, 1000, 1100, 128, 64, 64, True),
+    (2, 1, 33, 3000, 3000, 128, 128, 128, True),
+    (1, 2, 16, 777, 800, 64, 48, 128, False),
+    (1, 1, 20, 500, 500, 64, 24, 64, True),
+    (1, 1, 7, 600, 640, 128, 5, 128, False),
 ]
 
 
