@@ -600,9 +600,12 @@ DecodeSplit decode_split(int BH, int Nq, int Nk) {
     const int qn = Nq == 1 ? 1 : Nq <= 4 ? 4 : Nq <= 8 ? 8 : 16;
     const long long base = (long long)BH * ((Nq + qn - 1) / qn);
     const int blocks = (Nk + kDecKeys - 1) / kDecKeys;
-    // about four workgroups per CU in total, at least two key blocks per split (a split's
-    // second block of rows is requested while its first is reduced), one if there is one
-    long long want = (1024 + base - 1) / base;
+    // about four workgroups per CU in total (two for more than four queries per head, whose
+    // matrix-core kernel does more per workgroup), at least two key blocks per split (a
+    // split's second block of rows is requested while its first is reduced), one if there
+    // is one
+    const long long target = Nq > 4 ? 512 : 1024;
+    long long want = (target + base - 1) / base;
     if (want > blocks) want = blocks;
     if (want < 1) want = 1;
     int per = (int)((blocks + want - 1) / want);
