@@ -134,15 +134,16 @@ def time_backward(w, x, Q, K, V, P, steps, warmup, dev) -> dict:
             "executed_n2_flops_per_call": bw.executed_n2_flops, "grad_dtype": "f32"}
 
 
-def time_decode(w, x, P, steps, warmup, dev) -> dict:
-    """One decode step per call: the last query of every head against the whole cache of
-    projected keys (fp16) and values, spa_attn_decode timed between events on the launch
-    stream. HBM-bound: the reported rate is the cache bytes read per second."""
+def time_decode(w, x, P, steps, warmup, dev, nq: int = 1) -> dict:
+    """One decode step per call: the last nq queries of every head against the whole cache
+    of projected keys (fp16) and values, spa_attn_decode timed between events on the launch
+    stream. The reported rate is the cache bytes read per second (the bound at few queries);
+    the flops of the step are reported beside it."""
     K, V = x.K.to(dev), x.V.to(dev)
     cache = torch.empty((w.B, w.H, w.N, w.m), dtype=torch.float16, device=dev)
     spa.spa_kcache_append(K, P, cache, 0)
-    Q = x.Q[:, :, -1:].contiguous().to(dev)
-    ws = torch.empty(spa.spa_attn_decode_workspace_bytes(w.B, w.H, 1, w.N, w.dv),
+    Q = x.Q[:, :, -nq:].contiguous().to(dev)
+    ws = torch.empty(spa.spa_attn_decode_workspace_bytes(w.B, w.H, nq, w.N, w.dv),
                      dtype=torch.uint8, device=dev)
 
     def dstep():
@@ -161,9 +162,12 @@ def time_decode(w, x, P, steps, warmup, dev) -> dict:
     ms = e0.elapsed_time(e1) / steps
     cache_bytes = w.B * w.H * w.N * (2 * w.m + 2 * w.dv)
     gbs = cache_bytes / (ms * 1e-3) / 1e9
+    # every query against all N keys (the causal mask drops about nq^2 / 2 of those pairs)
+    flops = w.B * w.H * nq * w.N * (2 * w.m + 2 * w.dv)
     return {"ms_per_step": round(ms, 5), "cache_bytes": cache_bytes,
             "value": round(gbs, 1), "unit": "GB/s", "frac_of_hbm_peak": round(gbs / 8000.0, 4),
-            "k_cache_vs_k_bytes": round(w.m / w.d, 4), "queries_per_head": 1}
+            "k_cache_vs_k_bytes": round(w.m / w.d, 4), "queries_per_head": nq,
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
 
 
 def time_sfa(w, Q, K, V, topk, steps, warmup, dev) -> dict:
@@ -218,8 +222,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--decode", action="store_true",
-                    help="also time one decode step (spa_attn_decode, one query per head "
-                         "against the whole cache) and report it in a 'decode' object")
+                    help="also time one decode step (spa_attn_decode, the last query of every "
+                         "head against the whole cache) and report it in a 'decode' object")
+    ap.add_argument("--decode-queries", type=int, default=1,
+                    help="queries per head of the decode step (more than four take the "
+                         "matrix-core kernel when m is a multiple of 8)")
     ap.add_argument("--sfa", type=int, default=0, metavar="K",
                     help="also time sparse feature attention (spa_sfa_fwd) with K features "
                          "per row and report it in an 'sfa' object")
@@ -328,7 +335,9 @@ def main() -> int:
     if args.sfa and w.dtype == "bf16":
         res["sfa"] = time_sfa(w, Q, K, V, args.sfa, args.steps, args.warmup, dev)
     if args.decode and w.dtype == "bf16":
-        res["decode"] = time_decode(w, x, P, args.steps, args.warmup, dev)
+        if not 1 <= args.decode_queries <= w.N:
+            ap.error("--decode-queries must be between 1 and the workload's N")
+        res["decode"] = time_decode(w, x, P, args.steps, args.warmup, dev, args.decode_queries)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(res), flush=True)
