@@ -234,6 +234,8 @@ def main() -> int:
                     help="also time spa_attn_bwd (bf16 workloads) and report it in a "
                          "'backward' object")
     args = ap.parse_args()
+    if not 1 <= args.decode_queries <= inputs.WORKLOADS[args.workload].N:
+        ap.error("--decode-queries must be between 1 and the workload's N")
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every (batch, head) is independent, and the library "
@@ -335,8 +337,6 @@ def main() -> int:
     if args.sfa and w.dtype == "bf16":
         res["sfa"] = time_sfa(w, Q, K, V, args.sfa, args.steps, args.warmup, dev)
     if args.decode and w.dtype == "bf16":
-        if not 1 <= args.decode_queries <= w.N:
-            ap.error("--decode-queries must be between 1 and the workload's N")
         res["decode"] = time_decode(w, x, P, args.steps, args.warmup, dev, args.decode_queries)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x)
