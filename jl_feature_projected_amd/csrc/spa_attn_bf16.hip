@@ -505,20 +505,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         const size_t row = (size_t)bh * N + myq;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
+            if (out_f32) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c0 = db * 32 + 8 * g + 4 * half;
-                const float o0 = acc[db][4 * g + 0] * inv, o1 = acc[db][4 * g + 1] * inv;
-                const float o2 = acc[db][4 * g + 2] * inv, o3 = acc[db][4 * g + 3] * inv;
-                if (out_f32) {
+                for (int g = 0; g < 4; ++g) {
+                    const int c0 = db * 32 + 8 * g + 4 * half;
                     float* dst = static_cast<float*>(O) + row * DV + c0;
-                    *reinterpret_cast<float4*>(dst) = make_float4(o0, o1, o2, o3);
-                } else {
-                    bf16_t* dst = static_cast<bf16_t*>(O) + row * DV + c0;
-                    u32x2 w;
-                    w.x = pack_bf16x2(o0, o1);
-                    w.y = pack_bf16x2(o2, o3);
-                    *reinterpret_cast<u32x2*>(dst) = w;
+                    *reinterpret_cast<float4*>(dst) =
+                        make_float4(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
+                                    acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+                }
+            } else {
+                // 16-byte stores: of each pair of 8-column groups (g0, g1) the lower half-wave
+                // writes g0 and the upper g1, each taking the partner's four columns of it
+#pragma unroll
+                for (int g0 = 0; g0 < 4; g0 += 2) {
+                    u32x2 a, b;
+                    a.x = pack_bf16x2(acc[db][4 * g0] * inv, acc[db][4 * g0 + 1] * inv);
+                    a.y = pack_bf16x2(acc[db][4 * g0 + 2] * inv, acc[db][4 * g0 + 3] * inv);
+                    b.x = pack_bf16x2(acc[db][4 * g0 + 4] * inv, acc[db][4 * g0 + 5] * inv);
+                    b.y = pack_bf16x2(acc[db][4 * g0 + 6] * inv, acc[db][4 * g0 + 7] * inv);
+                    const u32x2 send = half ? a : b;
+                    u32x2 recv;
+                    recv.x = __shfl_xor(send.x, 32, 64);
+                    recv.y = __shfl_xor(send.y, 32, 64);
+                    const u32x4 v = half ? u32x4{recv.x, recv.y, b.x, b.y} : u32x4{a.x, a.y, recv.x, recv.y};
+                    bf16_t* dst = static_cast<bf16_t*>(O) + row * DV + db * 32 + 8 * (g0 + half);
+                    *reinterpret_cast<u32x4*>(dst) = v;
                 }
             }
         }
