@@ -116,8 +116,15 @@ size_t spa_attn_fwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
  * normaliser sums those rounded weights). Each row's exponent offset is the Cauchy-Schwarz
  * bound |q| * max |k| rather than a running maximum; rows for which that bound is so loose
  * that the normaliser would fall below 2^-64 are recomputed with an exact online maximum.
- * Supported: d in {64, 128}, dv in {64, 128}, 1 <= m <= 128. The fp32 path computes in fp32 throughout: 1 <= d <= 256, 1 <= m <= 128,
- * 1 <= dv <= 128. N may be any size from 1 to 2^22; tails are masked.
+ * Supported: d in {64, 128}, dv in {64, 128}, 1 <= m <= 128. Input range of the bf16
+ * path: every projected key entry (K P)[j,c] and every scaled projected query entry
+ * scale * log2(e) * (Q P)[i,c] must lie inside the fp16 range, |x| <= 65504 (bf16 inputs of
+ * ordinary attention magnitudes are far inside it; entries beyond it become infinite and
+ * the affected rows come out non-finite, or, where such a key's score is -infinity, with
+ * that key's weight correctly zero -- never a finite value built on a clipped score). Use
+ * the fp32 path for inputs outside that range. The fp32 path computes in fp32 throughout:
+ * 1 <= d <= 256, 1 <= m <= 128, 1 <= dv <= 128. N may be any size from 1 to 2^22; tails are
+ * masked.
  */
 spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const void* P,
                           float scale, int causal, int B, int H, int N, int d, int m, int dv,
@@ -137,9 +144,10 @@ size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
 
 /*
  * spa_attn_bwd -- gradients of a loss L through spa_attn_fwd, given dO = dL/dO: the chain
- * rule of the forward's definition (SPA page Sec. 3.1.3 and Algorithm 1; Sec. 3.2 and
- * Algorithm 2 learn the projection by backpropagation and write the query term of its
- * gradient, the key term entering the same way). With A the forward's row softmax:
+ * rule of the forward's definition (SPA page Sec. 3.1.3 and Algorithm 1; its Sec. 3.4.1
+ * Gradient Flow writes the query term of the projection's gradient, and Algorithm 2 trains
+ * the projection with it; the key term enters the same way). With A the forward's row
+ * softmax:
  *
  *   D_i = <dO_i, O_i>,  dS_ij = A_ij (<dO_i, V_j> - D_i)
  *   dV_j = sum_i A_ij dO_i,  dQ = scale * (dS Kt) P^T,  dK = scale * (dS^T Qt) P^T
@@ -266,6 +274,18 @@ spa_status_t spa_attn_decode(const void* Q, const void* cache, const void* Vc, c
  */
 spa_status_t spa_profile_begin(int max_calls);
 spa_status_t spa_profile_end(double* project_ms, double* attn_ms, int* calls);
+
+/*
+ * Rate probes for the benchmark's roofline context (not part of the attention path): the
+ * sustained rate of the bf16 matrix core (32x32x16 MFMAs, one wave per SIMD, every CU) and
+ * of fp32 VALU FMAs (four waves per SIMD), in TFLOP/s, each with the mean engine clock in
+ * GHz while it ran (shader-clock counter against the 100 MHz counter). Runs synchronously
+ * on `stream` (about 10 ms) and allocates a few KB of device memory for the duration of
+ * the call. Every output pointer must be non-NULL (else SPA_ERR_INVALID_ARGUMENT);
+ * SPA_ERR_HIP if a HIP call fails.
+ */
+spa_status_t spa_probe_rates(double* mfma_tflops, double* mfma_ghz, double* fma_tflops,
+                             double* fma_ghz, void* stream);
 
 #ifdef __cplusplus
 }

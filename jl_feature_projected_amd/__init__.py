@@ -28,7 +28,7 @@ SPA_BF16 = 1
 EXPORTS = ("spa_version", "spa_status_string", "spa_last_error", "spa_project",
            "spa_attn_fwd_workspace_bytes", "spa_attn_fwd", "spa_attn_bwd_workspace_bytes",
            "spa_attn_bwd", "spa_sfa_fwd_workspace_bytes", "spa_sfa_fwd", "spa_kcache_append", "spa_attn_decode_workspace_bytes",
-           "spa_attn_decode", "spa_profile_begin", "spa_profile_end")
+           "spa_attn_decode", "spa_profile_begin", "spa_profile_end", "spa_probe_rates")
 
 
 class SpaError(RuntimeError):
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
     dp = ctypes.POINTER(ctypes.c_double)
     L.spa_profile_end.restype = st
     L.spa_profile_end.argtypes = [dp, dp, ctypes.POINTER(ctypes.c_int)]
+    L.spa_probe_rates.restype = st
+    L.spa_probe_rates.argtypes = [dp, dp, dp, dp, vp]
     _lib = L
     return L
 
@@ -360,6 +362,17 @@ def spa_attn_decode(Q, cache, Vc, P, Nk: int, scale: float | None = None, causal
 def profile_begin(max_calls: int) -> None:
     """Start recording per-launch HIP events for the next max_calls spa_attn_fwd calls."""
     check(lib().spa_profile_begin(int(max_calls)))
+
+
+def probe_rates(device=None) -> dict:
+    """Measured bf16 MFMA and fp32 VALU FMA rates (TFLOP/s) with the engine clock (GHz) while
+    each ran, on the current stream (spa_probe_rates)."""
+    torch = _torch()
+    dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+    out = [ctypes.c_double() for _ in range(4)]
+    check(lib().spa_probe_rates(*(ctypes.byref(o) for o in out), _stream_ptr(dev)))
+    return {"mfma_bf16_tflops": out[0].value, "mfma_clock_ghz": out[1].value,
+            "fp32_fma_tflops": out[2].value, "fp32_clock_ghz": out[3].value}
 
 
 def profile_end() -> tuple[float, float, int]:

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libspa.so")
 SOURCES = ["spa_api.cpp", "spa_project.hip", "spa_attn_bf16.hip", "spa_bwd.hip", "spa_decode.hip",
-           "spa_sfa.hip", "spa_f32.hip", "spa_bwd_f32.hip"]
+           "spa_sfa.hip", "spa_f32.hip", "spa_bwd_f32.hip", "spa_probe.hip"]
 ARCH = "gfx950"
 
 

@@ -751,6 +751,18 @@ spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const voi
     return SPA_OK;
 }
 
+spa_status_t spa_probe_rates(double* mfma_tflops, double* mfma_ghz, double* fma_tflops,
+                             double* fma_ghz, void* stream) {
+    g_err[0] = '\0';
+    if (!mfma_tflops || !mfma_ghz || !fma_tflops || !fma_ghz)
+        return fail(SPA_ERR_INVALID_ARGUMENT, "spa_probe_rates: null output pointer");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = spa::run_probe(0, 3, s, mfma_tflops, mfma_ghz);
+    if (e == hipSuccess) e = spa::run_probe(1, 3, s, fma_tflops, fma_ghz);
+    if (e != hipSuccess) return hip_fail("spa_probe_rates", e);
+    return SPA_OK;
+}
+
 spa_status_t spa_profile_begin(int max_calls) {
     g_err[0] = '\0';
     if (max_calls < 1 || max_calls > 65536)

@@ -9,13 +9,16 @@
 // the FlashSFA description in the "Scaling Attention via Feature Sparsity" notes, Key
 // design 3, with the dense projected contraction in place of the sparse intersection.
 //
-// Work decomposition: a workgroup of 4 waves owns 128 queries of one (batch, head); each
-// wave owns 32 of them. Key tiles of 64 (projected keys, and the matching 64 columns of
-// V^T) are copied HBM -> LDS by buffer loads that write LDS directly (no registers, no VALU;
-// rows past the end read as zero), double buffered: a copy is issued one step before the
-// step that reads it. Per tile and wave:
+// Work decomposition: a workgroup of 4 waves owns 128 * QB queries of one (batch, head);
+// each wave owns QB blocks of 32 of them. QB = 1: two workgroups per CU (two waves per
+// SIMD, <= 256 registers each). QB = 2: one workgroup per CU, one wave per SIMD with the
+// whole register file; every LDS operand read and every tile copy then serves two query
+// blocks (half the LDS and L2 traffic per MFMA). Key tiles of 64 (projected keys, and the
+// matching 64 columns of V^T) are copied HBM -> LDS by buffer loads that write LDS directly
+// (no registers, no VALU; rows past the end read as zero), double buffered: a copy is
+// issued one step before the step that reads it. Per tile, wave and query block:
 //   scores^T (64 keys x 32 queries) = Kt_tile . Qt^T on 32x32x16 MFMA. The accumulator starts
-//     at -mu (the running row maximum), so the MFMA output is already score - mu; a lane
+//     at -mu (the row's score bound), so the MFMA output is already score - mu; a lane
 //     owns one query and 16 keys per 32-key block, so row reductions are in-lane plus one
 //     exchange with lane l xor 32.
 //   softmax without a running maximum: by Cauchy-Schwarz every score of a row is at most
@@ -47,15 +50,16 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBR = 128;  // queries per workgroup (4 waves x 32)
 constexpr int kBC = 64;   // keys per tile
 constexpr float kTau = 8.0f;
 
-template <int MP, int DV, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
+template <int MP, int DV, bool CAUSAL, int QB>
+__global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Kt, const bf16_t* __restrict__ Vt,
     const float* __restrict__ kmax, void* __restrict__ O, float* __restrict__ lse, int N, int nqb,
     int out_f32) {
+    constexpr int kBR = kWaves * 32 * QB;    // queries per workgroup
+    constexpr int WQ = 32 * QB;              // queries per wave
     constexpr int KS = MP / 16;              // score MFMA k-steps
     constexpr int KCH = MP / 8;              // 16-byte chunks per projected-key row
     constexpr int K_BYTES = kBC * MP * 2;    // one K tile
@@ -65,8 +69,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     constexpr int VINS = V_BYTES / 1024;     // ... per V tile (8 or 16)
     constexpr int DB = DV / 32;              // 32-row blocks of V^T / O^T
     static_assert(KINS >= 2 && VINS % kWaves == 0, "tile copy split");
+    static_assert(QB == 1 || QB == 2, "query blocks per wave");
+    // With one wave per SIMD the weight stages (exp, pack, sum) of a pair are spread over
+    // consecutive MFMA slots; with two, the other wave fills their latency.
+    constexpr bool kSkewWeights = QB != 1;
+    // With one wave per SIMD the normaliser of the pipelined steps is summed on the matrix
+    // core (16x16x32 MFMAs over the packed weights), off the VALU.
+    constexpr bool kNormMfma = QB != 1;
 
-    __shared__ __attribute__((aligned(16))) char lds[2 * BUF];
+    // QB = 1: two buffers, each one K tile and one V^T tile. QB = 2: rings of three K tiles
+    // (at offset 0) and three V^T tiles (at RING_V), so that a step can read the operands of
+    // the next one before its closing barrier. The exact fallback uses the two-buffer layout.
+    constexpr int NBUF = QB == 1 ? 2 : 3;
+    constexpr int RING_V = 3 * K_BYTES;
+    __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF];
 
     // Workgroup -> (head, query block). Workgroups are handed to the 8 XCDs round-robin;
     // when the grid divides evenly, XCD x gets a contiguous range of (head, block) pairs so
@@ -77,13 +93,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     if ((total & 7) == 0) li = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
     const int bh = li / nqb;
     const int qbi = li - bh * nqb;
-    const int qb = CAUSAL ? (nqb - 1 - qbi) : qbi;
-    const int q0 = qb * kBR;
+    const int qb_ = CAUSAL ? (nqb - 1 - qbi) : qbi;
+    const int q0 = qb_ * kBR;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
-    const int qw0 = q0 + wave * 32;
-    const int myq = qw0 + col;
+    const int qw0 = q0 + wave * WQ;
+    int myq[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) myq[b] = qw0 + 32 * b + col;
 
     const uint16_t* Qh = Qt + (size_t)bh * N * MP;
     const uint16_t* Kh = Kt + (size_t)bh * N * MP;
@@ -118,41 +136,59 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     // values below are this plus constants).
     const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds + 1024 * wave);
-    auto copy_k = [&](int k0, int buf) {
+    // Copies of the K tile at key k0 to LDS byte offset `at`, and of the V^T tile.
+    auto copy_k_to = [&](int k0, int at) {
         const u32x4 kr = make_rsrc(Kh + (size_t)k0 * MP, (uint32_t)(N - k0) * MP * 2);
 #pragma unroll
         for (int i = 0; i < KPW; ++i) {
             const int j = wave + kWaves * i;
-            if (j < KINS) copy16_to_lds(kr, lds_wave + buf * BUF + 1024 * kWaves * i, koff[i]);
+            if (j < KINS) copy16_to_lds(kr, lds_wave + at + 1024 * kWaves * i, koff[i]);
         }
     };
-    auto copy_v = [&](int k0, int buf) {
+    auto copy_v_to = [&](int k0, int at) {
         const u32x4 vr = make_rsrc(Vh + k0, (uint32_t)(DV * Np - k0) * 2);
 #pragma unroll
-        for (int i = 0; i < VPW; ++i)
-            copy16_to_lds(vr, lds_wave + buf * BUF + K_BYTES + 1024 * kWaves * i, voff[i]);
+        for (int i = 0; i < VPW; ++i) copy16_to_lds(vr, lds_wave + at + 1024 * kWaves * i, voff[i]);
     };
+    auto copy_k = [&](int k0, int buf) { copy_k_to(k0, buf * BUF); };
+    auto copy_v = [&](int k0, int buf) { copy_v_to(k0, buf * BUF + K_BYTES); };
+    // Ring slots (QB = 2): tile t's keys at kslot(t % 3), its V^T at vslot(t % 3).
+    auto kslot = [](int r) { return r * K_BYTES; };
+    auto vslot = [](int r) { return RING_V + r * V_BYTES; };
 
     // The first tiles' copies go out before anything else is loaded, so their latency
     // overlaps that of the query and key-norm loads below (the fast path starts from tile 0
     // in buffer 0 and, when pipelined, the keys of tile 1 in buffer 1).
     // (At MP = DV = 128 the pipelined loop does not fit the register budget of two
     // workgroups per CU; that shape runs every tile through tile_loop.)
-    constexpr bool PIPELINED = !(MP == 128 && DV == 128);
+    constexpr bool PIPELINED = !(QB == 1 && MP == 128 && DV == 128);
     // Tiles with no masked key for any query of the workgroup.
     const int nfull = CAUSAL ? min(ntiles, q0 / kBC) : N / kBC;
-    copy_k(0, 0);
-    copy_v(0, 0);
-    if (PIPELINED && ntiles > 1) copy_k(kBC, 1);
-
-    // This lane's query as the B operand of the score MFMA (zero past N).
-    f16x8 qf[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (myq < N) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)myq * MP + ks * 16 + half * 8);
-        qf[ks] = __builtin_bit_cast(f16x8, v);
+    if constexpr (QB == 1) {
+        copy_k(0, 0);
+        copy_v(0, 0);
+        if (PIPELINED && ntiles > 1) copy_k(kBC, 1);
+    } else {
+        copy_k_to(0, kslot(0));
+        copy_v_to(0, vslot(0));
+        if (ntiles > 1) {
+            copy_k_to(kBC, kslot(1));
+            copy_v_to(kBC, vslot(1));
+        }
+        if (ntiles > 2) copy_k_to(2 * kBC, kslot(2));
     }
+
+    // This lane's queries as the B operand of the score MFMA (zero past N).
+    f16x8 qf[QB][KS];
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (myq[b] < N)
+                v = *reinterpret_cast<const u32x4*>(Qh + (size_t)myq[b] * MP + ks * 16 + half * 8);
+            qf[b][ks] = __builtin_bit_cast(f16x8, v);
+        }
 
     // Per-lane LDS read offsets, fixed across tiles.
     // Score operand: key row kb*32 + col, global chunk 2*ks + half.
@@ -183,44 +219,67 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o, 64));
     }
-    float qn2 = 0.0f;  // squared norm of the query as the MFMA sees it (fp16 values)
+    float bound[QB];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int b = 0; b < QB; ++b) {
+        float qn2 = 0.0f;  // squared norm of the query as the MFMA sees it (fp16 values)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float v = (float)qf[ks][i];
-            qn2 += v * v;
-        }
-    // The slack covers fp16 rounding of the keys and fp32 rounding of norms and sums.
-    const float bound = sqrtf(halves_sum(qn2)) * kmx * (1.0f + 0x1p-8f) + 0x1p-8f;
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = (float)qf[b][ks][i];
+                qn2 += v * v;
+            }
+        // The slack covers fp16 rounding of the keys and fp32 rounding of norms and sums.
+        bound[b] = sqrtf(halves_sum(qn2)) * kmx * (1.0f + 0x1p-8f) + 0x1p-8f;
+    }
+    // QB = 2: a lane's two queries share one offset (the larger bound), so the pipelined
+    // steps need one accumulator start value, not two. Any offset at least the row maximum
+    // gives the same softmax; the exact fallback covers an offset that overshoots too far.
+    if constexpr (QB == 2) bound[0] = bound[1] = fmaxf(bound[0], bound[1]);
 
-    // ---- per-lane softmax state (query myq) --------------------------------------------
-    f32x16 acc[DB];
-    float mu;        // the exponent offset (base-2 units), identical in both half-waves
-    float lsum;      // partial normaliser over this half-wave's keys
-    f32x16 cinit;    // the score accumulator's start value, -mu
+    // ---- per-lane softmax state (queries myq[b]) ----------------------------------------
+    f32x16 acc[QB][DB];
+    float mu[QB];        // the exponent offset (base-2 units), identical in both half-waves
+    float lsum[QB];      // partial normaliser over this half-wave's keys
+    f32x16 cinit[QB];    // the score accumulator's start value, -mu
+    // Matrix-core normaliser (kNormMfma): lacc[b] rows 0 and 1 of lanes 0-15 hold the sums
+    // for queries 32b + lane and 32b + 16 + lane.
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    f32x4_t lacc[QB];
+    bf16x8 lsel;
+    {
+        const int m = lane & 15, g = lane >> 4;
+        const bool one = (m == 0 && (g & 1) == 0) || (m == 1 && (g & 1) == 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lsel[i] = one ? (__bf16)1.0f : (__bf16)0.0f;
+    }
 
-    // Scores^T of one key tile (64 keys x this wave's 32 queries), minus mu.
-    auto scores = [&](const char* Ks, f32x16 (&s)[2]) {
+    // Scores^T of one key tile (64 keys x 32 queries per block), minus mu. Each key operand
+    // read serves every query block.
+    auto scores = [&](const char* Ks, f32x16 (&s)[QB][2]) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = cinit;
+#pragma unroll
+            for (int b = 0; b < QB; ++b) s[b][kb] = cinit[b];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const f16x8 a = __builtin_bit_cast(
                     f16x8, *reinterpret_cast<const u32x4*>(Ks + kread[kb][ks]));
-                s[kb] = mfma32x32x16(a, qf[ks], s[kb]);
+#pragma unroll
+                for (int b = 0; b < QB; ++b) s[b][kb] = mfma32x32x16(a, qf[b][ks], s[b][kb]);
             }
         }
     };
-    // Weights of k-step tt of key block kb, pair j (keys 2j, 2j+1 of the lane's 8 slots):
-    // exp2, rounded to bf16, packed, and added to the normaliser. With a mask, slot i of
-    // key block kb (key k0 + kb*32 + 8*(i/4) + 4*half + i%4) is dropped when kb*32 + 8*(i/4)
-    // + i%4 > rel, rel being the lane's last admissible key minus k0 + 4*half.
-    auto weight_pair = [&](const f32x16 (&s)[2], int kb, int tt, int j, auto masked,
+    // Weights of query block b, k-step tt of key block kb, pair j (keys 2j, 2j+1 of the
+    // lane's 8 slots): exp2, rounded to bf16, packed, and added to the normaliser. With a
+    // mask, slot i of key block kb (key k0 + kb*32 + 8*(i/4) + 4*half + i%4) is dropped when
+    // kb*32 + 8*(i/4) + i%4 > rel, rel being the lane's last admissible key minus
+    // k0 + 4*half.
+    auto weight_pair = [&](const f32x16 (&s)[QB][2], int b, int kb, int tt, int j, auto masked,
                            int rel) -> uint32_t {
         constexpr bool MASKED = decltype(masked)::value;
-        float x0 = s[kb][8 * tt + 2 * j], x1 = s[kb][8 * tt + 2 * j + 1];
+        float x0 = s[b][kb][8 * tt + 2 * j], x1 = s[b][kb][8 * tt + 2 * j + 1];
         if constexpr (MASKED) {
             const int i0 = 8 * tt + 2 * j;
             if (kb * 32 + 8 * (i0 >> 2) + (i0 & 3) > rel) x0 = -INFINITY;
@@ -229,18 +288,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
         const float p0 = __builtin_amdgcn_exp2f(x0);
         const float p1 = __builtin_amdgcn_exp2f(x1);
         const uint32_t w = pack_bf16x2(p0, p1);
-        lsum = add_bf16x2(w, lsum);
+        lsum[b] = add_bf16x2(w, lsum[b]);
         return w;
     };
-    // One PV MFMA: O^T block db += V^T_tile(key block kb, k-step tt) . p^T. Slot 8*half + j
-    // of k-step tt in key block kb holds key kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, in the
-    // score accumulator and in the V^T tile alike.
-    auto pv_step = [&](const char* Vs, const u32x4 (&p)[2][2], int db, int kb, int tt) {
+    // The exps of one weight pair (as weight_pair), left unpacked.
+    auto exp_pair = [&](const f32x16 (&s)[QB][2], int b, int kb, int tt, int j, auto masked,
+                        int rel, float (&e)[2]) {
+        constexpr bool MASKED = decltype(masked)::value;
+        float x0 = s[b][kb][8 * tt + 2 * j], x1 = s[b][kb][8 * tt + 2 * j + 1];
+        if constexpr (MASKED) {
+            const int i0 = 8 * tt + 2 * j;
+            if (kb * 32 + 8 * (i0 >> 2) + (i0 & 3) > rel) x0 = -INFINITY;
+            if (kb * 32 + 8 * (i0 >> 2) + (i0 & 3) + 1 > rel) x1 = -INFINITY;
+        }
+        e[0] = __builtin_amdgcn_exp2f(x0);
+        e[1] = __builtin_amdgcn_exp2f(x1);
+    };
+    // One PV step: O^T block db += V^T_tile(key block kb, k-step tt) . p^T for every query
+    // block; the V operand is read once. Slot 8*half + j of k-step tt in key block kb holds
+    // key kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, in the score accumulator and in the V^T
+    // tile alike.
+    auto pv_step = [&](const char* Vs, const u32x4 (&p)[QB][2][2], int db, int kb, int tt) {
         const bf16x8 a = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const u32x4*>(Vs + db * 32 * 128 + vread[kb][tt]));
-        acc[db] = mfma32x32x16(a, __builtin_bit_cast(bf16x8, p[kb][tt]), acc[db]);
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+            acc[b][db] = mfma32x32x16(a, __builtin_bit_cast(bf16x8, p[b][kb][tt]), acc[b][db]);
     };
-    auto pv = [&](const char* Vs, const u32x4 (&p)[2][2]) {
+    auto pv = [&](const char* Vs, const u32x4 (&p)[QB][2][2]) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -248,78 +323,207 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) pv_step(Vs, p, db, kb, tt);
     };
-    auto weights = [&](const f32x16 (&s)[2], u32x4 (&p)[2][2]) {
+    auto weights = [&](const f32x16 (&s)[QB][2], u32x4 (&p)[QB][2][2]) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int b = 0; b < QB; ++b)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    p[kb][tt][j] = weight_pair(s, kb, tt, j, std::false_type{}, 0);
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        p[b][kb][tt][j] = weight_pair(s, b, kb, tt, j, std::false_type{}, 0);
     };
+    // Order of the PV steps of a tile: V^T block db outermost with one query block (each
+    // step's weights stay live to the end of the tile), key block kb outermost with two
+    // (the weights of the first key block die halfway, and the next tile's take their
+    // registers).
+    auto pv_db = [](int v) { return QB == 1 ? v / 4 : v % DB; };
+    auto pv_kb = [](int v) { return QB == 1 ? (v >> 1) & 1 : v / (2 * DB); };
+    auto pv_tt = [](int v) { return QB == 1 ? v & 1 : (v / DB) & 1; };
     // One pipelined step: scores of the next tile (K tile Kn) and PV of this one (V^T tile
     // Vs, weights p), with the next tile's weights (out pn) computed while the PV MFMAs run.
     // The schedule is fixed explicitly (scheduling fences between slots), since the LDS
     // reads and the MFMA -> exp dependency each take about three MFMA issue slots to come
     // back: all K operands and the first PF V operands are read up front; the score MFMAs
-    // follow; PV MFMA i is preceded by the read of V operand i + PF; the weights start
+    // follow; the V operand of PV step i + PF is read before PV step i; the weights start
     // WSTART PV MFMAs after the score MFMAs (their inputs are ready by then) and are spread
-    // evenly over the remaining PV MFMAs.
-    auto pipelined_step = [&](const char* Kn, const char* Vs, const u32x4 (&p)[2][2],
-                              u32x4 (&pn)[2][2], auto masked, int rel) {
-        constexpr int NPV = 4 * DB;  // PV MFMAs per tile
-        constexpr int PF = 4;        // V operand prefetch distance, in MFMAs
-        constexpr int WSTART = 3;    // first PV MFMA that weight work is placed after
-        constexpr int NW = NPV - WSTART;
-        u32x4 ka[2][KS];
+    // evenly over the remaining PV MFMAs, in the order the score MFMAs completed.
+    constexpr int NPV = 4 * DB;      // PV steps (V operands) per tile
+    constexpr int PF = QB == 1 ? 4 : 3;  // V operand prefetch distance, in PV steps
+    // The score operands of the K tile at Kn, and the first PF V operands of the V^T tile
+    // at Vs.
+    auto load_ka = [&](const char* Kn, u32x4 (&ka)[2][KS]) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 ka[kb][ks] = *reinterpret_cast<const u32x4*>(Kn + kread[kb][ks]);
-        u32x4 va[NPV];
-        auto vload = [&](int i) {
-            const int db = i / 4, kb = (i >> 1) & 1, tt = i & 1;
-            va[i] = *reinterpret_cast<const u32x4*>(Vs + db * 32 * 128 + vread[kb][tt]);
+    };
+    auto vload = [&](const char* Vs, u32x4 (&va)[NPV], int i) {
+        va[i] = *reinterpret_cast<const u32x4*>(Vs + pv_db(i) * 32 * 128 + vread[pv_kb(i)][pv_tt(i)]);
+    };
+    auto load_va_prefix = [&](const char* Vs, u32x4 (&va)[NPV]) {
+#pragma unroll
+        for (int i = 0; i < PF; ++i) vload(Vs, va, i);
+    };
+    // The step with the next tile's score operands (ka) and this tile's first PF V operands
+    // (va) already in registers.
+    auto step_core = [&](const u32x4 (&ka)[2][KS], u32x4 (&va)[NPV], const char* Vs,
+                         const u32x4 (&p)[QB][2][2], u32x4 (&pn)[QB][2][2], auto masked,
+                         const int (&rel)[QB]) {
+        constexpr int NM = NPV * QB;     // PV MFMAs per tile
+        constexpr int WSTART = 3;        // first PV MFMA that weight work is placed after
+        constexpr int NU = 16 * QB;      // weight pairs per tile
+        // Weight pair u: key block u / (8 QB), query block (u / 8) % QB, k-step (u / 4) % 2,
+        // pair u % 4 -- the order in which the score MFMAs finish. Slot i >= WSTART takes
+        // pairs [ulo(i), ulo(i + 1)). With QB = 2 the score MFMAs of key block 1 are issued
+        // halfway (SPLIT), once the exps of key block 0 have consumed theirs, so the two
+        // blocks' scores share registers; each half then spreads its own pairs.
+        constexpr bool SPLIT = QB != 1;
+        auto ulo = [&](int i) {
+            if constexpr (!SPLIT) {
+                constexpr int NW = NM - WSTART;
+                return i <= WSTART ? 0 : i >= NM ? NU : (i - WSTART) * NU / NW;
+            } else {
+                constexpr int H = NM / 2, NU2 = NU / 2, NW2 = H - WSTART;
+                if (i >= NM) return NU;
+                const int base = (i / H) * NU2, j = i % H;
+                return j <= WSTART ? base : base + (j - WSTART) * NU2 / NW2;
+            }
         };
+        float ex[NU][2];
+        f32x16 sn[QB][2];
+        auto score_mfmas = [&](int kb) {
+            if constexpr (QB == 1) {
+                sn[0][kb] = cinit[0];
 #pragma unroll
-        for (int i = 0; i < PF; ++i) vload(i);
-        f32x16 sn[2];
+                for (int ks = 0; ks < KS; ++ks)
+                    sn[0][kb] = mfma32x32x16(__builtin_bit_cast(f16x8, ka[kb][ks]), qf[0][ks],
+                                             sn[0][kb]);
+            } else {
+                // VGPR-form MFMAs: the exps read these results; the first of them comes
+                // at least WSTART PV MFMAs after the last score MFMA of its block.
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            sn[kb] = cinit;
+                for (int b = 0; b < QB; ++b)
+                    sn[b][kb] = mfma32x32x16_v(__builtin_bit_cast(f16x8, ka[kb][0]), qf[b][0],
+                                               cinit[0]);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                sn[kb] = mfma32x32x16(__builtin_bit_cast(f16x8, ka[kb][ks]), qf[ks], sn[kb]);
-        }
+                for (int ks = 1; ks < KS; ++ks)
+#pragma unroll
+                    for (int b = 0; b < QB; ++b)
+                        mfma32x32x16_v_acc(__builtin_bit_cast(f16x8, ka[kb][ks]), qf[b][ks],
+                                           sn[b][kb]);
+            }
+        };
+        score_mfmas(0);
+        if constexpr (!SPLIT) score_mfmas(1);
         __builtin_amdgcn_sched_barrier(0);  // nothing below moves above the score MFMAs
 #pragma unroll
-        for (int i = 0; i < NPV; ++i) {
-            if (i + PF < NPV) vload(i + PF);
-            const int db = i / 4, kb = (i >> 1) & 1, tt = i & 1;
-            acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, va[i]),
-                                   __builtin_bit_cast(bf16x8, p[kb][tt]), acc[db]);
-            if (i >= WSTART) {
+        for (int i = 0; i < NM; ++i) {
+            const int v = i / QB, b = i % QB;
+            if (SPLIT && i == NM / 2) score_mfmas(1);
+            if (b == 0 && v + PF < NPV) vload(Vs, va, v + PF);
+            const int db = pv_db(v), kb = pv_kb(v), tt = pv_tt(v);
+            acc[b][db] = mfma32x32x16(__builtin_bit_cast(bf16x8, va[v]),
+                                      __builtin_bit_cast(bf16x8, p[b][kb][tt]), acc[b][db]);
+            if constexpr (!kSkewWeights) {
+                if (i >= WSTART) {
 #pragma unroll
-                for (int u = (i - WSTART) * 16 / NW; u < (i - WSTART + 1) * 16 / NW; ++u)
-                    pn[u >> 3][(u >> 2) & 1][u & 3] =
-                        weight_pair(sn, u >> 3, (u >> 2) & 1, u & 3, masked, rel);
+                    for (int u = ulo(i); u < ulo(i + 1); ++u) {
+                        const int ukb = u / (8 * QB), ub = (u / 8) % QB, utt = (u >> 2) & 1,
+                                  uj = u & 3;
+                        pn[ub][ukb][utt][uj] =
+                            weight_pair(sn, ub, ukb, utt, uj, masked, rel[ub]);
+                    }
+                }
+            } else {
+                // The weight pairs of this slot are exponentiated here, packed and summed
+                // one slot later: with one wave per SIMD nothing else fills the latency of
+                // exp -> pack -> sum, so each stage's input comes from the slot before.
+                if (i > WSTART) {
+#pragma unroll
+                    for (int u = ulo(i - 1); u < ulo(i); ++u) {
+                        const int ukb = u / (8 * QB), ub = (u / 8) % QB, utt = (u >> 2) & 1,
+                                  uj = u & 3;
+                        pn[ub][ukb][utt][uj] = pack_bf16x2(ex[u][0], ex[u][1]);
+                    }
+                }
+                if (i >= WSTART) {
+#pragma unroll
+                    for (int u = ulo(i); u < ulo(i + 1); ++u) {
+                        const int ukb = u / (8 * QB), ub = (u / 8) % QB, utt = (u >> 2) & 1,
+                                  uj = u & 3;
+                        exp_pair(sn, ub, ukb, utt, uj, masked, rel[ub], ex[u]);
+                    }
+                }
+                if (i > WSTART) {
+#pragma unroll
+                    for (int u = ulo(i - 1); u < ulo(i); ++u) {
+                        const int ukb = u / (8 * QB), ub = (u / 8) % QB, utt = (u >> 2) & 1,
+                                  uj = u & 3;
+                        if constexpr (!kNormMfma) lsum[ub] = add_bf16x2(pn[ub][ukb][utt][uj], lsum[ub]);
+                    }
+                }
             }
             // Slot fence: the compiler keeps this order (it would otherwise bunch the exps).
             __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    auto init_state = [&](float mu0) {
+        if constexpr (kSkewWeights) {
+            // The last slot's pairs: pack and sum.
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] = f32x16_fill(0.0f);
-        lsum = 0.0f;
-        mu = mu0;
-        cinit = f32x16_fill(-mu);
+            for (int u = ulo(NM - 1); u < NU; ++u) {
+                const int ukb = u / (8 * QB), ub = (u / 8) % QB, utt = (u >> 2) & 1, uj = u & 3;
+                pn[ub][ukb][utt][uj] = pack_bf16x2(ex[u][0], ex[u][1]);
+                if constexpr (!kNormMfma) lsum[ub] = add_bf16x2(pn[ub][ukb][utt][uj], lsum[ub]);
+            }
+        }
+        // Keep the weights here, beside the MFMAs they overlap: the compiler may otherwise
+        // sink the VALU work past a later branch, to their first use in the next step.
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) asm volatile("" : "+v"(pn[b][kb][tt]));
+            asm volatile("" : "+v"(lsum[b]));
+        }
+        if constexpr (kNormMfma) {
+            // The normaliser of the new weights on the matrix core: one 16x16x32 MFMA per
+            // 16 keys whose A operand selects, for output row 0 (1), the lanes holding
+            // queries 0-15 (16-31) in both half-waves.
+#pragma unroll
+            for (int b = 0; b < QB; ++b)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+                        lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            lsel, __builtin_bit_cast(bf16x8, pn[b][kb][tt]), lacc[b], 0, 0, 0);
+        }
+    };
+    auto pipelined_step = [&](const char* Kn, const char* Vs, const u32x4 (&p)[QB][2][2],
+                              u32x4 (&pn)[QB][2][2], auto masked, const int (&rel)[QB]) {
+        u32x4 ka[2][KS], va[NPV];
+        load_ka(Kn, ka);
+        load_va_prefix(Vs, va);
+        step_core(ka, va, Vs, p, pn, masked, rel);
+    };
+    auto init_state = [&](const float (&mu0)[QB]) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[b][db] = f32x16_fill(0.0f);
+            lsum[b] = 0.0f;
+            lacc[b] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            mu[b] = mu0[b];
+            cinit[b] = f32x16_fill(-mu[b]);
+        }
     };
 
     // Tiles [t0, ntiles), one at a time: the next tile's copy is issued first; keys past N
     // and after the query (causal) are masked; waves whose queries all precede a tile skip
-    // it. The exact variant keeps a lazy running maximum.
+    // it. The exact variant keeps a lazy running maximum per query.
     auto tile_loop = [&](auto exact_tag, int t0) {
         constexpr bool EXACT = decltype(exact_tag)::value;
 #pragma unroll 1
@@ -332,49 +536,54 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
             const char* Ks = lds + (t & 1) * BUF;
             const char* Vs = Ks + K_BYTES;
 
-            if (!CAUSAL || k0 <= qw0 + 31) {
-                f32x16 s[2];
+            if (!CAUSAL || k0 <= qw0 + WQ - 1) {
+                f32x16 s[QB][2];
                 scores(Ks, s);
                 const bool edge = (k0 + kBC > N) || (CAUSAL && k0 + kBC - 1 > qw0);
                 if (edge) {
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                            if (key >= N || (CAUSAL && key > myq)) s[kb][i] = -INFINITY;
-                        }
-                }
-                if constexpr (EXACT) {
-                    float tmax = -INFINITY;
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
-                    tmax = halves_max(tmax);
-                    // The first tile sets mu to its maximum (key 0 is unmasked for every
-                    // query, so that maximum is finite, and nothing has been accumulated
-                    // yet); later tiles move mu only past the kTau slack, rescaling what was
-                    // accumulated by 2^-delta <= 1.
-                    if (t == 0 || __any(tmax > kTau)) {
-                        const float delta = (t == 0) ? tmax : fmaxf(tmax, 0.0f);
-                        if (t != 0) {
-                            const float alpha = __builtin_amdgcn_exp2f(-delta);
-                            lsum *= alpha;
-#pragma unroll
-                            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                                for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-                        }
-                        mu += delta;
+                    for (int b = 0; b < QB; ++b)
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                            for (int i = 0; i < 16; ++i) s[kb][i] -= delta;
-                        cinit = f32x16_fill(-mu);
+                            for (int i = 0; i < 16; ++i) {
+                                const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                                if (key >= N || (CAUSAL && key > myq[b])) s[b][kb][i] = -INFINITY;
+                            }
+                }
+                if constexpr (EXACT) {
+#pragma unroll
+                    for (int b = 0; b < QB; ++b) {
+                        float tmax = -INFINITY;
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[b][kb][i]);
+                        tmax = halves_max(tmax);
+                        // The first tile sets mu to its maximum (key 0 is unmasked for every
+                        // query, so that maximum is finite, and nothing has been accumulated
+                        // yet); later tiles move mu only past the kTau slack, rescaling what
+                        // was accumulated by 2^-delta <= 1.
+                        if (t == 0 || __any(tmax > kTau)) {
+                            const float delta = (t == 0) ? tmax : fmaxf(tmax, 0.0f);
+                            if (t != 0) {
+                                const float alpha = __builtin_amdgcn_exp2f(-delta);
+                                lsum[b] *= alpha;
+#pragma unroll
+                                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                                    for (int i = 0; i < 16; ++i) acc[b][db][i] *= alpha;
+                            }
+                            mu[b] += delta;
+#pragma unroll
+                            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                                for (int i = 0; i < 16; ++i) s[b][kb][i] -= delta;
+                            cinit[b] = f32x16_fill(-mu[b]);
+                        }
                     }
                 }
-                u32x4 p[2][2];
+                u32x4 p[QB][2][2];
                 weights(s, p);
                 pv(Vs, p);
             }
@@ -392,55 +601,70 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
     //   buffer (t+1)&1 and K[t+2] into buffer t&1.
     // Tiles [0, nfull) have no masked key for any query of the workgroup; their steps run in
     // a loop of two steps with the buffer parity as a template constant (every LDS offset an
-    // immediate) and no branch around the MFMAs. The at most three steps after it mask the
-    // keys past N and past each query (causal) as the weights are formed, and a wave skips
-    // the score or PV half of a step whose tile lies wholly after its queries. Returns the
-    // number of tiles done (all, or none for the shapes that are not pipelined). The copies
-    // of tile 0 (and of tile 1's keys) were issued at the top of the kernel.
+    // immediate) and no branch around the MFMAs. The steps after it (the causal diagonal,
+    // the ragged tail) mask the keys past N and past each query as the weights are formed,
+    // and a wave skips the score or PV half of a step whose tile lies wholly after its
+    // queries. Returns the number of tiles done (all, or none for the shapes that are not
+    // pipelined). The copies of tile 0 (and of tile 1's keys) were issued at the top of the
+    // kernel.
     auto fast_phase = [&]() -> int {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if constexpr (!PIPELINED) {
             return 0;
-        } else {
-            // The lane's last admissible key (ragged tail, causal diagonal).
-            const int klim = CAUSAL ? min(myq, N - 1) : N - 1;
-            auto rel_of = [&](int k0) { return klim - k0 - 4 * half; };
+        } else if constexpr (QB == 1) {
+            // The lane's last admissible key per query block (ragged tail, causal diagonal).
+            int klim[QB];
+#pragma unroll
+            for (int b = 0; b < QB; ++b) klim[b] = CAUSAL ? min(myq[b], N - 1) : N - 1;
+            auto rel_of = [&](int k0, int (&rel)[QB]) {
+#pragma unroll
+                for (int b = 0; b < QB; ++b) rel[b] = klim[b] - k0 - 4 * half;
+            };
+            const int rel0[QB] = {};
             // Does this wave have an admissible key in tile t?
-            auto wave_needs = [&](int t) { return !CAUSAL || t * kBC <= qw0 + 31; };
-            u32x4 pa[2][2], pb[2][2];
+            auto wave_needs = [&](int t) { return !CAUSAL || t * kBC <= qw0 + WQ - 1; };
+            u32x4 pa[QB][2][2], pb[QB][2][2];
             {
-                f32x16 s[2];
+                f32x16 s[QB][2];
                 scores(lds, s);
                 if (nfull == 0) {
-                    const int rel = rel_of(0);
+                    int rel[QB];
+                    rel_of(0, rel);
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                    for (int b = 0; b < QB; ++b)
 #pragma unroll
-                        for (int tt = 0; tt < 2; ++tt)
+                        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                pa[kb][tt][j] = weight_pair(s, kb, tt, j, std::true_type{}, rel);
+                            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    pa[b][kb][tt][j] =
+                                        weight_pair(s, b, kb, tt, j, std::true_type{}, rel[b]);
                 } else {
                     weights(s, pa);
                 }
             }
             __syncthreads();  // K[0] read by every wave before step 0 refills buffer 0
             // Step t of the unmasked loop, weights p of tile t in, pn of tile t+1 out.
-            auto step = [&](auto parity, int t, const u32x4 (&p)[2][2], u32x4 (&pn)[2][2]) {
+            auto step = [&](auto parity, int t, const u32x4 (&p)[QB][2][2],
+                            u32x4 (&pn)[QB][2][2]) {
                 constexpr int PAR = decltype(parity)::value;
                 copy_v((t + 1) * kBC, 1 - PAR);  // t + 1 < nfull <= ntiles
                 if (t + 2 < ntiles) copy_k((t + 2) * kBC, PAR);
                 pipelined_step(lds + (1 - PAR) * BUF, lds + PAR * BUF + K_BYTES, p, pn,
-                               std::false_type{}, 0);
+                               std::false_type{}, rel0);
                 // The weights are plain register arithmetic, which the compiler may sink past
                 // the barrier to their use in the next step; pin them here, beside the MFMAs
                 // they are meant to overlap.
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int b = 0; b < QB; ++b) {
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) asm volatile("" : "+v"(pn[kb][tt]));
-                asm volatile("" : "+v"(lsum));
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt) asm volatile("" : "+v"(pn[b][kb][tt]));
+                    asm volatile("" : "+v"(lsum[b]));
+                }
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
             };
@@ -452,8 +676,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 step(P0{}, t, pa, pb);
                 step(P1{}, t + 1, pb, pa);
             }
-            // The rest, t .. ntiles - 1 (at most three steps and the last PV: t + 2 >= nfull,
-            // ntiles <= nfull + 2), with the buffer parity at run time and tile t's weights
+            // The rest, t .. ntiles - 1 (t + 2 >= nfull; the causal diagonal adds at most
+            // kBR / kBC tiles), with the buffer parity at run time and tile t's weights
             // always in pa.
 #pragma unroll 1
             for (; t + 1 < ntiles; ++t) {
@@ -463,86 +687,226 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(
                 copy_v((t + 1) * kBC, 1 - par);
                 if (t + 2 < ntiles) copy_k((t + 2) * kBC, par);
                 if (wave_needs(t + 1)) {
-                    if (t + 1 < nfull)
-                        pipelined_step(Kn, Vs, pa, pb, std::false_type{}, 0);
-                    else
-                        pipelined_step(Kn, Vs, pa, pb, std::true_type{}, rel_of((t + 1) * kBC));
+                    if (t + 1 < nfull) {
+                        pipelined_step(Kn, Vs, pa, pb, std::false_type{}, rel0);
+                    } else {
+                        int rel[QB];
+                        rel_of((t + 1) * kBC, rel);
+                        pipelined_step(Kn, Vs, pa, pb, std::true_type{}, rel);
+                    }
                 } else {
                     if (wave_needs(t)) pv(Vs, pa);
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                    for (int b = 0; b < QB; ++b)
 #pragma unroll
-                        for (int tt = 0; tt < 2; ++tt) pb[kb][tt] = u32x4{0u, 0u, 0u, 0u};
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int tt = 0; tt < 2; ++tt) pb[b][kb][tt] = u32x4{0u, 0u, 0u, 0u};
                 }
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int b = 0; b < QB; ++b)
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) pa[kb][tt] = pb[kb][tt];
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt) pa[b][kb][tt] = pb[b][kb][tt];
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
             }
             if (wave_needs(t)) pv(lds + (t & 1) * BUF + K_BYTES, pa);
+            return ntiles;
+        } else {
+            // One wave per SIMD: nothing else on the SIMD runs while this wave waits, so
+            // every step starts with its operands in registers. Step t copies V[t+2] and
+            // K[t+3] (the slots of tiles t-1 and t, both consumed before the last barrier),
+            // issues tile t+1's score MFMAs from the key operands in ka and tile t's PV MFMAs
+            // from its V^T slot (the first PF operands already in va), and before its closing
+            // barrier reads the key operands of tile t+2 and the first V operands of tile
+            // t+1 -- tiles whose copies were awaited before an earlier barrier.
+            int klim[QB];
+#pragma unroll
+            for (int b = 0; b < QB; ++b) klim[b] = CAUSAL ? min(myq[b], N - 1) : N - 1;
+            auto rel_of = [&](int k0, int (&rel)[QB]) {
+#pragma unroll
+                for (int b = 0; b < QB; ++b) rel[b] = klim[b] - k0 - 4 * half;
+            };
+            const int rel0[QB] = {};
+            auto wave_needs = [&](int t) { return !CAUSAL || t * kBC <= qw0 + WQ - 1; };
+            u32x4 pa[QB][2][2], pb[QB][2][2];
+            u32x4 ka[2][KS], va[NPV];
+            {
+                f32x16 s[QB][2];
+                scores(lds + kslot(0), s);
+                if (nfull == 0) {
+                    int rel[QB];
+                    rel_of(0, rel);
+#pragma unroll
+                    for (int b = 0; b < QB; ++b)
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j)
+                                    pa[b][kb][tt][j] =
+                                        weight_pair(s, b, kb, tt, j, std::true_type{}, rel[b]);
+                } else {
+                    weights(s, pa);
+                }
+            }
+            if (ntiles > 1) load_ka(lds + kslot(1), ka);
+            load_va_prefix(lds + vslot(0), va);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();  // K[0] read by every wave before step 0 refills its slot
+            // Tiles below wfull have no masked key for any query of this wave.
+            const int wfull = CAUSAL ? min(N / kBC, qw0 / kBC) : N / kBC;
+            // Step t with ring slot S = t % 3. The generic variant (the causal diagonal, the
+            // ragged tail) picks per wave the unmasked step, the masked one, or only the PV
+            // of tile t when the wave has no admissible key in tile t+1.
+            auto ring_step = [&](int S, int t, const u32x4 (&p)[QB][2][2], u32x4 (&pn)[QB][2][2],
+                                 auto generic) {
+                constexpr bool GENERIC = decltype(generic)::value;
+                const int S1 = S == 2 ? 0 : S + 1, S2 = S == 0 ? 2 : S - 1;
+                if (t + 3 < ntiles) copy_k_to((t + 3) * kBC, kslot(S));
+                if (t + 2 < ntiles) copy_v_to((t + 2) * kBC, vslot(S2));
+                if (!GENERIC || t + 1 < wfull) {
+                    step_core(ka, va, lds + vslot(S), p, pn, std::false_type{}, rel0);
+                } else if (wave_needs(t + 1)) {
+                    int rel[QB];
+                    rel_of((t + 1) * kBC, rel);
+                    step_core(ka, va, lds + vslot(S), p, pn, std::true_type{}, rel);
+                } else {
+                    if (wave_needs(t)) pv(lds + vslot(S), p);
+#pragma unroll
+                    for (int b = 0; b < QB; ++b)
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int tt = 0; tt < 2; ++tt) pn[b][kb][tt] = u32x4{0u, 0u, 0u, 0u};
+                }
+                // (Past the last tile these read a slot no copy refills: unused values.)
+                load_ka(lds + kslot(S2), ka);
+                load_va_prefix(lds + vslot(S1), va);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            };
+            int t = 0;
+            // Steps whose next tile is unmasked for the whole workgroup, six per trip:
+            // constant ring slots, and the weights back in pa at the end of a trip.
+#pragma unroll 1
+            for (; t + 6 < nfull; t += 6) {
+                ring_step(0, t, pa, pb, std::false_type{});
+                ring_step(1, t + 1, pb, pa, std::false_type{});
+                ring_step(2, t + 2, pa, pb, std::false_type{});
+                ring_step(0, t + 3, pb, pa, std::false_type{});
+                ring_step(1, t + 4, pa, pb, std::false_type{});
+                ring_step(2, t + 5, pb, pa, std::false_type{});
+            }
+            bool in_b = false;  // the weights of tile t are in pb (else pa)
+            // The rest: up to five unmasked steps, the causal diagonal (kBR / kBC tiles)
+            // and the ragged tail.
+#pragma unroll 1
+            for (; t + 1 < ntiles; ++t) {
+                if (!in_b)
+                    ring_step(t % 3, t, pa, pb, std::true_type{});
+                else
+                    ring_step(t % 3, t, pb, pa, std::true_type{});
+                in_b = !in_b;
+            }
+            if (wave_needs(t)) {
+                if (in_b)
+                    pv(lds + vslot(t % 3), pb);
+                else
+                    pv(lds + vslot(t % 3), pa);
+            }
             return ntiles;
         }
     };
 
     init_state(bound);
     tile_loop(std::false_type{}, fast_phase());
-    float ltot = halves_sum(lsum);
-    if (__syncthreads_or(myq < N && ltot < 0x1p-64f)) {
-        init_state(0.0f);
+    float ltot[QB];
+    bool low = false;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        ltot[b] = halves_sum(lsum[b]);
+        if constexpr (kNormMfma) {
+            const int src = col & 15;
+            const float l0 = __shfl(lacc[b][0], src, 64), l1 = __shfl(lacc[b][1], src, 64);
+            ltot[b] += col < 16 ? l0 : l1;
+        }
+        low = low || (myq[b] < N && ltot[b] < 0x1p-64f);
+    }
+    if (__syncthreads_or(low)) {
+        const float zero[QB] = {};
+        init_state(zero);
         copy_k(0, 0);
         copy_v(0, 0);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         tile_loop(std::true_type{}, 0);
-        ltot = halves_sum(lsum);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) ltot[b] = halves_sum(lsum[b]);
     }
 
     // ---- epilogue: O = O_acc / l (both half-waves' key subsets summed) ------------------
-    const float inv = 1.0f / ltot;
-    if (myq < N) {
-        const size_t row = (size_t)bh * N + myq;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            if (out_f32) {
+    for (int b = 0; b < QB; ++b) {
+        const float inv = 1.0f / ltot[b];
+        if (myq[b] < N) {
+            const size_t row = (size_t)bh * N + myq[b];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int c0 = db * 32 + 8 * g + 4 * half;
-                    float* dst = static_cast<float*>(O) + row * DV + c0;
-                    *reinterpret_cast<float4*>(dst) =
-                        make_float4(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv,
-                                    acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-                }
-            } else {
-                // 16-byte stores: of each pair of 8-column groups (g0, g1) the lower half-wave
-                // writes g0 and the upper g1, each taking the partner's four columns of it
+            for (int db = 0; db < DB; ++db) {
+                if (out_f32) {
 #pragma unroll
-                for (int g0 = 0; g0 < 4; g0 += 2) {
-                    u32x2 a, b;
-                    a.x = pack_bf16x2(acc[db][4 * g0] * inv, acc[db][4 * g0 + 1] * inv);
-                    a.y = pack_bf16x2(acc[db][4 * g0 + 2] * inv, acc[db][4 * g0 + 3] * inv);
-                    b.x = pack_bf16x2(acc[db][4 * g0 + 4] * inv, acc[db][4 * g0 + 5] * inv);
-                    b.y = pack_bf16x2(acc[db][4 * g0 + 6] * inv, acc[db][4 * g0 + 7] * inv);
-                    const u32x2 send = half ? a : b;
-                    u32x2 recv;
-                    recv.x = __shfl_xor(send.x, 32, 64);
-                    recv.y = __shfl_xor(send.y, 32, 64);
-                    const u32x4 v = half ? u32x4{recv.x, recv.y, b.x, b.y} : u32x4{a.x, a.y, recv.x, recv.y};
-                    bf16_t* dst = static_cast<bf16_t*>(O) + row * DV + db * 32 + 8 * (g0 + half);
-                    *reinterpret_cast<u32x4*>(dst) = v;
+                    for (int g = 0; g < 4; ++g) {
+                        const int c0 = db * 32 + 8 * g + 4 * half;
+                        float* dst = static_cast<float*>(O) + row * DV + c0;
+                        *reinterpret_cast<float4*>(dst) = make_float4(
+                            acc[b][db][4 * g] * inv, acc[b][db][4 * g + 1] * inv,
+                            acc[b][db][4 * g + 2] * inv, acc[b][db][4 * g + 3] * inv);
+                    }
+                } else {
+                    // 16-byte stores: of each pair of 8-column groups (g0, g1) the lower
+                    // half-wave writes g0 and the upper g1, each taking the partner's four
+                    // columns of it
+#pragma unroll
+                    for (int g0 = 0; g0 < 4; g0 += 2) {
+                        u32x2 a, c;
+                        a.x = pack_bf16x2(acc[b][db][4 * g0] * inv, acc[b][db][4 * g0 + 1] * inv);
+                        a.y = pack_bf16x2(acc[b][db][4 * g0 + 2] * inv, acc[b][db][4 * g0 + 3] * inv);
+                        c.x = pack_bf16x2(acc[b][db][4 * g0 + 4] * inv, acc[b][db][4 * g0 + 5] * inv);
+                        c.y = pack_bf16x2(acc[b][db][4 * g0 + 6] * inv, acc[b][db][4 * g0 + 7] * inv);
+                        const u32x2 send = half ? a : c;
+                        u32x2 recv;
+                        recv.x = __shfl_xor(send.x, 32, 64);
+                        recv.y = __shfl_xor(send.y, 32, 64);
+                        const u32x4 v = half ? u32x4{recv.x, recv.y, c.x, c.y}
+                                             : u32x4{a.x, a.y, recv.x, recv.y};
+                        bf16_t* dst = static_cast<bf16_t*>(O) + row * DV + db * 32 + 8 * (g0 + half);
+                        *reinterpret_cast<u32x4*>(dst) = v;
+                    }
                 }
             }
+            if (lse && half == 0) lse[row] = (mu[b] + __log2f(ltot[b])) * 0.69314718055994530942f;
         }
-        if (lse && half == 0) lse[row] = (mu + __log2f(ltot)) * 0.69314718055994530942f;
     }
 }
 
-template <int MP, int DV, bool CAUSAL>
+// Query blocks per wave: two (one wave per SIMD, every LDS operand read and tile copy shared
+// by 64 queries) where the register file holds them and the grid still has several
+// workgroups per CU; one otherwise.
+inline int pick_qb(int BH, int N, int mp, bool causal) {
+    if (mp > 32 || causal) return 1;
+    const long long wgs2 = (long long)BH * ((N + 255) / 256);
+    return wgs2 >= 512 ? 2 : 1;
+}
+
+template <int MP, int DV, bool CAUSAL, int QB>
 hipError_t launch(const void* Qt, const void* Kt, const void* Vt, const float* kmax, void* O,
                   float* lse, int BH, int N, bool out_f32, hipStream_t stream) {
+    constexpr int kBR = kWaves * 32 * QB;
     const int nqb = (N + kBR - 1) / kBR;
-    attn_bf16_kernel<MP, DV, CAUSAL><<<dim3(nqb * BH), kThreads, 0, stream>>>(
+    attn_bf16_kernel<MP, DV, CAUSAL, QB><<<dim3(nqb * BH), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(Qt), static_cast<const uint16_t*>(Kt),
         static_cast<const bf16_t*>(Vt), kmax, O, lse, N, nqb, out_f32 ? 1 : 0);
     return hipGetLastError();
@@ -550,18 +914,23 @@ hipError_t launch(const void* Qt, const void* Kt, const void* Vt, const float* k
 
 template <int MP, int DV>
 hipError_t launch_c(const void* Qt, const void* Kt, const void* V, const float* kmax, void* O,
-                    float* lse, int BH, int N, bool causal, bool out_f32, hipStream_t stream) {
-    return causal ? launch<MP, DV, true>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream)
-                  : launch<MP, DV, false>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream);
+                    float* lse, int BH, int N, bool causal, bool out_f32, int qb,
+                    hipStream_t stream) {
+    if constexpr (MP <= 32) {
+        if (qb == 2 && !causal)
+            return launch<MP, DV, false, 2>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream);
+    }
+    return causal ? launch<MP, DV, true, 1>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream)
+                  : launch<MP, DV, false, 1>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream);
 }
 
 template <int MP>
 hipError_t launch_dv(const void* Qt, const void* Kt, const void* V, const float* kmax, void* O,
-                     float* lse, int BH, int N, int dv, bool causal, bool out_f32,
+                     float* lse, int BH, int N, int dv, bool causal, bool out_f32, int qb,
                      hipStream_t stream) {
     switch (dv) {
-        case 64: return launch_c<MP, 64>(Qt, Kt, V, kmax, O, lse, BH, N, causal, out_f32, stream);
-        case 128: return launch_c<MP, 128>(Qt, Kt, V, kmax, O, lse, BH, N, causal, out_f32, stream);
+        case 64: return launch_c<MP, 64>(Qt, Kt, V, kmax, O, lse, BH, N, causal, out_f32, qb, stream);
+        case 128: return launch_c<MP, 128>(Qt, Kt, V, kmax, O, lse, BH, N, causal, out_f32, qb, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -571,11 +940,12 @@ hipError_t launch_dv(const void* Qt, const void* Kt, const void* V, const float*
 hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* V, const float* kmax,
                             void* O, float* lse, int BH, int N, int mp, int dv, bool causal,
                             bool out_f32, hipStream_t stream) {
+    const int qb = pick_qb(BH, N, mp, causal);
     switch (mp) {
-        case 16: return launch_dv<16>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, stream);
-        case 32: return launch_dv<32>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, stream);
-        case 64: return launch_dv<64>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, stream);
-        case 128: return launch_dv<128>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, stream);
+        case 16: return launch_dv<16>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
+        case 32: return launch_dv<32>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
+        case 64: return launch_dv<64>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
+        case 128: return launch_dv<128>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
         default: return hipErrorInvalidValue;
     }
 }

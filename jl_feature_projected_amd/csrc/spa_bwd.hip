@@ -1,9 +1,9 @@
 // spa_bwd.hip -- backward of the projected attention for bf16 inputs on gfx950 MFMA.
 //
 // What it computes: the chain rule of the forward ("Sparse Projection Attention" page,
-// Sec. 3.1.3 and Algorithm 1; Sec. 3.2 and Algorithm 2 train the projection by
-// backpropagation, with the query term of the projection's gradient written out; the key
-// term enters the same way). With A the row softmax of the forward, O = A V, dO = dL/dO:
+// Sec. 3.1.3 and Algorithm 1; its Sec. 3.4.1 Gradient Flow writes out the query term of the
+// projection's gradient, which Algorithm 2 trains the projection with; the key term enters
+// the same way). With A the row softmax of the forward, O = A V, dO = dL/dO:
 //   D_i = <dO_i, O_i>,  dA_ij = <dO_i, V_j>,  dS_ij = A_ij (dA_ij - D_i)
 //   dV_j = sum_i A_ij dO_i,  dQt_i = scale sum_j dS_ij Kt_j,  dKt_j = scale sum_i dS_ij Qt_i
 //   dQ = dQt P^T,  dK = dKt P^T,  dP_h = sum over batches and rows of Q^T dQt + K^T dKt.

@@ -1,9 +1,9 @@
 // spa_bwd_f32.hip -- the backward of the fp32 path: every product and sum in fp32 on the VALU.
 //
 // The gradients of the projected attention: the chain rule through the forward's definition
-// ("Sparse Projection Attention" page, Sec. 3.1.3 and Algorithm 1; Sec. 3.2 and Algorithm 2
-// learn the projection by backpropagation and write the query term of its gradient, the
-// key term entering the same way). With A = softmax(scale Qt Kt^T [+ mask]) recomputed from
+// ("Sparse Projection Attention" page, Sec. 3.1.3 and Algorithm 1; its Sec. 3.4.1 Gradient
+// Flow writes the query term of the projection's gradient, which Algorithm 2 trains the
+// projection with; the key term enters the same way). With A = softmax(scale Qt Kt^T [+ mask]) recomputed from
 // the forward's natural-log lse:
 //   D_i = <dO_i, O_i>,  dS_ij = A_ij (<dO_i, V_j> - D_i),  dV_j = sum_i A_ij dO_i,
 //   dQt = scale dS Kt,  dKt = scale dS^T Qt,  dQ = dQt P^T,  dK = dKt P^T,

@@ -30,6 +30,27 @@ __device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// The same fp16 MFMA with its result and accumulator in VGPRs. In a kernel that may use
+// more than 256 registers the compiler gives every MFMA the AGPR form, and a VALU use of the
+// result then needs one v_accvgpr_read per element; this form avoids that for results the
+// VALU consumes. The compiler does not track the MFMA -> VALU latency of inline assembly, so
+// the caller keeps at least three MFMAs between this and the first VALU read of the result.
+// A chain of these on one accumulator needs no wait (exact overlap of result and srcC).
+__device__ __forceinline__ f32x16 mfma32x32x16_v(f16x8 a, f16x8 b, f32x16 c) {
+    f32x16 d;
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+#else
+    d = c;
+#endif
+    return d;
+}
+__device__ __forceinline__ void mfma32x32x16_v_acc(f16x8 a, f16x8 b, f32x16& c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+#endif
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
 __device__ __forceinline__ uint4 as_uint4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }

@@ -294,9 +294,9 @@ int spa_oracle_weights(const double* Q, const double* K, const double* P, double
 
 /*
  * Backward of spa_oracle_attn_fwd for a loss L with dL/dO = dO: the chain rule of the
- * definition above. The "Sparse Projection Attention" page, Sec. 3.2 and Algorithm 2, learns
- * the projection by backpropagation and writes the query term of dL/dP; P multiplies the
- * keys too, so the key term enters the same way. Per (b, h), with A the row softmax and
+ * definition above. The "Sparse Projection Attention" page, Sec. 3.4.1 (Gradient Flow),
+ * writes the query term of dL/dP, and its Algorithm 2 trains the projection with it; P
+ * multiplies the keys too, so the key term enters the same way. Per (b, h), with A the row softmax and
  * O = A V as in the forward:
  *
  *   D_i    = sum_c dO_ic O_ic

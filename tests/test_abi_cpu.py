@@ -281,3 +281,10 @@ def test_binding_rejects_tensors_on_other_devices():
     spa._same_device(T(device="cuda:0"), T(device="cuda:0"), None)
     with pytest.raises(ValueError):
         spa._same_device(T(device="cuda:0"), T(device="cuda:0"), T(device="cuda:1"))
+
+
+def test_probe_rates_rejects_null_outputs(L):
+    x = ctypes.c_double()
+    st = L.spa_probe_rates(None, ctypes.byref(x), ctypes.byref(x), ctypes.byref(x), None)
+    assert st == spa.SPA_ERR_INVALID_ARGUMENT
+    assert b"null" in L.spa_last_error()

@@ -68,6 +68,9 @@ CASES = [  # B, H, Nq, Nk, rows, d, m, dv, causal
     (1, 2, 16, 777, 800, 64, 48, 128, False),
     (1, 1, 20, 500, 500, 64, 24, 64, True),
     (1, 1, 7, 600, 640, 128, 5, 128, False),
+    # m in 72..96 with more than four queries: the matrix-core kernel's three-k-step instance
+    (1, 2, 16, 1000, 1000, 128, 80, 128, True),
+    (1, 1, 9, 700, 720, 64, 72, 64, False),
 ]
 
 

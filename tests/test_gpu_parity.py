@@ -130,6 +130,53 @@ def test_small_shapes_full(dev, oracle_mod, N, d, m, dv, causal):
     assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
 
 
+# Grids of at least 512 workgroups of 256 queries take the kernel variant with one wave per
+# SIMD and 64 queries per wave (non-causal, m <= 32): every output of ragged shapes.
+WIDE = [
+    # (B, H, N, d, m, dv)
+    (4, 32, 1000, 128, 32, 128), (4, 32, 1000, 128, 16, 64), (2, 64, 777, 64, 5, 128),
+    (8, 16, 1025, 128, 24, 128), (1, 128, 1024, 128, 32, 64),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,m,dv", WIDE)
+def test_wide_variant_full(dev, oracle_mod, B, H, N, d, m, dv):
+    w = inputs.Workload(f"wide-b{B}h{H}-n{N}-d{d}-m{m}-dv{dv}", B, H, N, d, m, dv, False,
+                        seed=3000 + N + m)
+    x = inputs.draw(w)
+    note(w.name)
+    O, lse = run(x, dev, return_lse=True)
+    Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, False, with_lse=True)
+    assert_bf16_close(np64(O), Or, what=w.name)
+    assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
+    Ob = run(x, dev, out_dtype=torch.bfloat16)
+    assert_bf16_close(np64(Ob), Or, out_bf16=True, what=w.name + "/bf16")
+
+
+@pytest.mark.parametrize("factor", [2.0, 5.0])
+def test_wide_variant_unequal_query_norms(dev, oracle_mod, factor):
+    """The 64-query waves give a lane's two queries (32 apart) one shared score offset, the
+    larger of their two bounds. Queries 32..63 of every 64 made longer push the shorter
+    queries' weights down: by about 2^-16 at twice the length (the fast path still holds
+    them), below 2^-64 at five times (the workgroup must take the exact path). Both are
+    checked against the oracle. V is halved: the five-times-longer queries' sharper softmax
+    amplifies the fp16 rounding of their scores (the operand precision every variant of the
+    kernel shares) to about 1e-2 at unit V, which is not what this test is about."""
+    w = inputs.Workload(f"wide-unequal-norms-x{factor:g}", 4, 32, 769, 128, 32, 128, False,
+                        seed=91)
+    x = inputs.draw(w)
+    Q = x.f64("Q")
+    idx = np.arange(w.N)
+    Q[:, :, (idx % 64) >= 32] *= factor
+    x = inputs.Inputs(w, inputs.to_storage(Q, "bf16"), x.K,
+                      inputs.to_storage(0.5 * x.f64("V"), "bf16"), x.P)
+    note(w.name)
+    O, lse = run(x, dev, return_lse=True)
+    Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, False, with_lse=True)
+    assert_bf16_close(np64(O), Or, what=w.name)
+    assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
+
+
 # Fixed sparse and structured projections (Sparse Projection Attention page, Sec. 2.2
 # Definition 1; the block and banded patterns of Sec. 3.2 / Table 6 as the input generators
 # read them): the kernel takes any dense P, zeros included.
@@ -169,24 +216,29 @@ def test_fp32_path_other_shapes(dev, oracle_mod, N, m, dv, causal):
 
 FULL = {  # workload -> (random rows per head, heads compared in full)
     "c3": (96, (0, 31)),
-    "c4": (24, ()),
+    "c4": (24, (31,)),
     "c5_m8": (48, (15,)),
-    "c5_m16": (48, ()),
-    "c5_m32": (48, ()),
-    "c5_m64": (48, ()),
-    "c5_m128": (48, ()),
+    "c5_m16": (48, (3,)),
+    "c5_m32": (48, (7,)),
+    "c5_m64": (48, (11,)),
+    "c5_m128": (48, (0,)),
     "c5_identity": (48, (15,)),
 }
 
 
 def sample_rows(w, per_head, full_heads, seed=0):
+    """Per head: the first and last row of every 128-query block (the kernels' workgroup
+    tiles are 128 or 256 queries), the rows around the 32- and 64-row boundaries of the
+    first and last blocks, random rows, and every row of the heads in full_heads."""
     rng = np.random.default_rng(seed)
     N, BH = w.N, w.B * w.H
     edges = [0, 1, 31, 32, 63, 64, 65, 127, 128, 129, N // 2, N - 129, N - 128, N - 65,
              N - 64, N - 1]
+    blocks = set(range(0, N, 128)) | set(min(N - 1, j + 127) for j in range(0, N, 128))
     bh, ri = [], []
     for h in range(BH):
-        rows = set(e for e in edges if 0 <= e < N) | set(rng.integers(0, N, per_head).tolist())
+        rows = (set(e for e in edges if 0 <= e < N) | blocks
+                | set(rng.integers(0, N, per_head).tolist()))
         if h in full_heads:
             rows = set(range(N))
         rows = sorted(rows)
@@ -214,6 +266,71 @@ def test_full_size_sampled(dev, oracle_mod, key):
         # fp32 rounding of weight * value / weight
         v0 = x.V[:, :, 0].float().to(dev)
         assert torch.all(torch.abs(O[:, :, 0] - v0) <= 2.0 ** -22 * torch.abs(v0))
+
+
+def test_headline_bf16_output_launch(dev, oracle_mod):
+    """The benchmark's exact launch (the N = 8192 workload, bf16 output, dv = 128): sampled
+    rows against the oracle, and the bf16 output equal bit for bit to the round-to-nearest-
+    even of the same call's fp32 output (PDA, Algorithm 2.1 step 5: the epilogue's only
+    difference is the output rounding)."""
+    w = inputs.WORKLOADS["c3"]
+    x = inputs.draw(w)
+    Ob = run(x, dev, out_dtype=torch.bfloat16)
+    Of = run(x, dev, out_dtype=torch.float32)
+    assert torch.equal(Ob.view(torch.int16), Of.to(torch.bfloat16).view(torch.int16))
+    bh, ri = sample_rows(w, 48, ())
+    Or = oracle_mod.attn_rows(x.Q, x.K, x.V, x.P, w.scale, w.causal, bh, ri)
+    Og = Ob.reshape(w.B * w.H, w.N, w.dv)[torch.from_numpy(bh).to(dev), torch.from_numpy(ri).to(dev)]
+    assert_bf16_close(np64(Og), Or, out_bf16=True, what="c3/bf16-out")
+
+
+@pytest.mark.parametrize("N,causal", [(7, True), (1000, True), (1000, False), (333, False)])
+def test_bf16_output_dv128_small(dev, oracle_mod, N, causal):
+    w = inputs.Workload(f"bf16out-n{N}-c{int(causal)}", 2, 3, N, 128, 32, 128, causal,
+                        seed=1500 + N)
+    x = inputs.draw(w)
+    Ob = run(x, dev, out_dtype=torch.bfloat16)
+    Of = run(x, dev, out_dtype=torch.float32)
+    assert torch.equal(Ob.view(torch.int16), Of.to(torch.bfloat16).view(torch.int16))
+    Or = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, causal)
+    assert_bf16_close(np64(Ob), Or, out_bf16=True, what=w.name)
+
+
+@pytest.mark.parametrize("N,causal", [(64, True), (128, False), (128, True)])
+def test_identity_values_expose_the_weights(dev, oracle_mod, N, causal):
+    """V = I_N (dv = N): O is the attention matrix itself, compared entry by entry with the
+    oracle's row softmax of the projected scores (SPA Sec. 3.1.3; PDA Algorithm 2.1 step 3),
+    and every row sums to one."""
+    w = inputs.Workload(f"v-identity-n{N}-c{int(causal)}", 1, 2, N, 128, 32, N, causal,
+                        seed=2500 + N)
+    x = inputs.draw(w)
+    V = torch.eye(N, dtype=torch.bfloat16).expand(w.B, w.H, N, N).contiguous()
+    x = inputs.Inputs(w, x.Q, x.K, V, x.P)
+    O = run(x, dev, out_dtype=torch.float32)
+    A = oracle_mod.weights(x.Q, x.K, x.P, w.scale, causal)
+    err = np.abs(np64(O) - A)
+    note(f"V = I, N={N}: max-abs {err.max():.3e}")
+    assert err.max() <= TOL_BF16
+    assert np.max(np.abs(np64(O).sum(-1) - 1.0)) <= 1e-3
+    if causal:
+        assert float(O.triu(1).abs().max()) == 0.0  # masked weights are exactly zero
+
+
+def test_large_magnitude_inputs(dev, oracle_mod):
+    """Keys 1000x longer and queries 1000x shorter: the projected keys reach the
+    thousands (inside fp16, whose largest finite value is 65504, the limit the library
+    documents for the projected operands) while the scores keep their scale. The output
+    must be finite and agree with the oracle."""
+    w = inputs.Workload("large-magnitude", 1, 4, 900, 128, 32, 128, True, seed=2600)
+    x = inputs.draw(w)
+    Q = inputs.to_storage(x.f64("Q") / 1000.0, "bf16")
+    K = inputs.to_storage(x.f64("K") * 1000.0, "bf16")
+    x = inputs.Inputs(w, Q, K, x.V, x.P)
+    O, lse = run(x, dev, return_lse=True)
+    assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(lse).all())
+    Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, True, with_lse=True)
+    assert_bf16_close(np64(O), Or, what=w.name)
+    assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
 
 
 def test_identity_projection_matches_exact_attention(dev):

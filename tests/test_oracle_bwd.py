@@ -1,8 +1,8 @@
 """Pins of the oracle's backward (``oracle.attn_bwd``) to things other than itself.
 
 The backward is the chain rule of the forward definition ("Sparse Projection Attention"
-page, Sec. 3.1.3 and Algorithm 1 for the forward; Sec. 3.2 and Algorithm 2 train the
-projection by backpropagation). Pins:
+page, Sec. 3.1.3 and Algorithm 1 for the forward; Sec. 3.4.1 Gradient Flow gives the
+projection's gradient, Algorithm 2 trains the projection with it). Pins:
 
 * central finite differences of the forward oracle, in double, for every input element of
   tiny problems (queries, keys, values and the projection, both masks, several batches so
