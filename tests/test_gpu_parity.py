@@ -174,7 +174,9 @@ def test_wide_variant_unequal_query_norms(dev, oracle_mod, factor):
     O, lse = run(x, dev, return_lse=True)
     Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, False, with_lse=True)
     assert_bf16_close(np64(O), Or, what=w.name)
-    assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
+    # lse reaches about 50 here: besides the absolute 2e-2, allow the two fp16 roundings of
+    # the score operands (2^-11 relative each) on the score scale that lse carries
+    assert np.all(np.abs(np64(lse) - lr) <= TOL_BF16 + 2.0 ** -10 * np.abs(lr))
 
 
 # Fixed sparse and structured projections (Sparse Projection Attention page, Sec. 2.2
