@@ -132,6 +132,25 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * spa_attn_fwd_noalloc -- spa_attn_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments and results as spa_attn_fwd without the workspace pair: the workspace is a
+ * static device array inside the library, spa_attn_fwd_noalloc_max_workspace_bytes() bytes
+ * (128 MiB) per GPU, which every GPU the library runs on holds until the process ends. The
+ * call allocates nothing (no hipMalloc, no stream-ordered allocation). Sizes whose
+ * spa_attn_fwd_workspace_bytes(...) exceeds that limit are rejected with
+ * SPA_ERR_UNSUPPORTED before any HIP work; other errors as spa_attn_fwd. Every call on a GPU
+ * shares that GPU's array, so calls that overlap on one GPU (on different streams, or from
+ * several threads) race: serialize them. The array keeps the last call's contents; the
+ * forward overwrites all of the workspace it reads, so nothing needs clearing.
+ */
+size_t spa_attn_fwd_noalloc_max_workspace_bytes(void);
+spa_status_t spa_attn_fwd_noalloc(const void* Q, const void* K, const void* V, const void* P,
+                                  float scale, int causal, int B, int H, int N, int d, int m,
+                                  int dv, spa_dtype_t dtype, void* O, spa_dtype_t o_dtype,
+                                  float* lse, void* stream);
+
+/*
  * Workspace bytes spa_attn_bwd needs for these sizes (0 for arguments it would reject).
  * Contents (each region 256-byte aligned), bf16 path: the projected queries (scaled by
  * scale*log2(e)) and keys, fp16, row-major and transposed; dO transposed (bf16); the row

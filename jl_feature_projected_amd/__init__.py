@@ -28,7 +28,8 @@ SPA_BF16 = 1
 EXPORTS = ("spa_version", "spa_status_string", "spa_last_error", "spa_project",
            "spa_attn_fwd_workspace_bytes", "spa_attn_fwd", "spa_attn_bwd_workspace_bytes",
            "spa_attn_bwd", "spa_sfa_fwd_workspace_bytes", "spa_sfa_fwd", "spa_kcache_append", "spa_attn_decode_workspace_bytes",
-           "spa_attn_decode", "spa_profile_begin", "spa_profile_end", "spa_probe_rates")
+           "spa_attn_decode", "spa_profile_begin", "spa_profile_end", "spa_probe_rates",
+           "spa_attn_fwd_noalloc", "spa_attn_fwd_noalloc_max_workspace_bytes")
 
 
 class SpaError(RuntimeError):
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
     L.spa_attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.spa_attn_fwd.restype = st
     L.spa_attn_fwd.argtypes = [vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, vp, i, vp, vp, z, vp]
+    L.spa_attn_fwd_noalloc.restype = st
+    L.spa_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, vp, i, vp, vp]
+    L.spa_attn_fwd_noalloc_max_workspace_bytes.restype = z
+    L.spa_attn_fwd_noalloc_max_workspace_bytes.argtypes = []
     L.spa_attn_bwd_workspace_bytes.restype = z
     L.spa_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.spa_attn_bwd.restype = st
@@ -199,6 +204,50 @@ def spa_attn_fwd(Q, K, V, P, scale: float | None = None, causal: bool = False,
                              lse.data_ptr() if lse is not None else None, ws_ptr, ws_bytes,
                              _stream_ptr(Q.device)))
     return (out, lse) if return_lse else out
+
+
+def spa_attn_fwd_noalloc(Q, K, V, P, scale: float | None = None, causal: bool = False,
+                         out=None, out_dtype=None, lse=None):
+    """spa_attn_fwd through the allocation-free entry point (the library's static workspace;
+    the caller passes the outputs). Q, K, V, P as for spa_attn_fwd; out [B,H,N,dv] and the
+    optional lse [B,H,N] fp32 are preallocated device tensors (created here if None, which is
+    the binding's allocation, not the library's). Returns out."""
+    torch = _torch()
+    for name, x in (("Q", Q), ("K", K), ("V", V), ("P", P)):
+        _device_tensor(x, name)
+    if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3]:
+        raise ValueError("Q, K must be [B,H,N,d] and V [B,H,N,dv]")
+    B, H, N, d = Q.shape
+    dv = V.shape[3]
+    if P.dim() != 3 or P.shape[0] != H or P.shape[1] != d:
+        raise ValueError("P must be [H,d,m]")
+    m = P.shape[2]
+    dt = Q.dtype
+    if any(x.dtype != dt for x in (K, V, P)) or any(x.device != Q.device for x in (K, V, P)):
+        raise ValueError("Q, K, V and P must share dtype and device")
+    odt = out.dtype if out is not None else (dt if out_dtype is None else out_dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=odt, device=Q.device)
+    _device_tensor(out, "out")
+    if out.shape != (B, H, N, dv):
+        raise ValueError("out has the wrong shape")
+    if lse is not None:
+        _device_tensor(lse, "lse")
+        if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+            raise ValueError("lse must be fp32 [B,H,N]")
+    _same_device(Q, out, lse)
+    check(lib().spa_attn_fwd_noalloc(Q.data_ptr(), K.data_ptr(), V.data_ptr(), P.data_ptr(),
+                                     float(scale), int(bool(causal)), B, H, N, d, m, dv,
+                                     _dtype_code(dt), out.data_ptr(), _dtype_code(odt),
+                                     lse.data_ptr() if lse is not None else None,
+                                     _stream_ptr(Q.device)))
+    return out
+
+
+def spa_attn_fwd_noalloc_max_workspace_bytes() -> int:
+    return int(lib().spa_attn_fwd_noalloc_max_workspace_bytes())
 
 
 def spa_attn_bwd_workspace_bytes(B, H, N, d, m, dv, dtype) -> int:

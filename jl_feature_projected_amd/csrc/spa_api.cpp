@@ -237,12 +237,18 @@ size_t spa_attn_fwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
     return out;
 }
 
-spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const void* P,
-                          float scale, int causal, int B, int H, int N, int d, int m, int dv,
-                          spa_dtype_t dtype, void* O, spa_dtype_t o_dtype, float* lse,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-    g_err[0] = '\0';
-    const char* fn = "spa_attn_fwd";
+}  // extern "C"
+
+namespace {
+
+// The forward behind spa_attn_fwd and spa_attn_fwd_noalloc. A null workspace is allocated
+// stream-ordered (spa_attn_fwd only: the allocation-free entry point always passes one);
+// `timed` lets the launch timing of spa_profile_begin record events.
+spa_status_t attn_fwd_impl(const char* fn, const void* Q, const void* K, const void* V,
+                           const void* P, float scale, int causal, int B, int H, int N, int d,
+                           int m, int dv, spa_dtype_t dtype, void* O, spa_dtype_t o_dtype,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                           bool timed) {
     if (!Q || !K || !V || !P || !O)
         return fail(SPA_ERR_INVALID_ARGUMENT, "%s: null tensor pointer", fn);
     spa_status_t st = check_dims(fn, B, H, N, d, m, dv);
@@ -306,7 +312,7 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
     void* Vt = wsb + wl.vt_offset;
 
     hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
-    {
+    if (timed) {
         std::lock_guard<std::mutex> lock(g_prof.mu);
         if (g_prof.on && g_prof.calls < g_prof.max_calls) {
             for (int i = 0; i < 3; ++i) ev[i] = g_prof.ev[3 * g_prof.calls + i];
@@ -353,6 +359,77 @@ spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const voi
     }
     if (e != hipSuccess) return hip_fail(fn, e);
     return SPA_OK;
+}
+
+// Workspace of the allocation-free forward: one array per GPU the library runs on, held
+// until the process ends. kScratchBytes covers the forward's workspace up to, e.g.,
+// B*H = 32 heads of N = 8192 at d = m = dv = 128 on the bf16 path (96 MiB).
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch` (looked up once per device, with that device current;
+// the host-side name of the array is not a device address).
+spa_status_t scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("spa_attn_fwd_noalloc: hipGetDevice", e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SPA_ERR_UNSUPPORTED, "spa_attn_fwd_noalloc: device %d beyond %d", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail("spa_attn_fwd_noalloc: hipGetSymbolAddress", e);
+        if (!ptr) return fail(SPA_ERR_HIP, "spa_attn_fwd_noalloc: null scratch address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+spa_status_t spa_attn_fwd(const void* Q, const void* K, const void* V, const void* P,
+                          float scale, int causal, int B, int H, int N, int d, int m, int dv,
+                          spa_dtype_t dtype, void* O, spa_dtype_t o_dtype, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    return attn_fwd_impl("spa_attn_fwd", Q, K, V, P, scale, causal, B, H, N, d, m, dv, dtype,
+                         O, o_dtype, lse, workspace, workspace_bytes, stream, true);
+}
+
+size_t spa_attn_fwd_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
+
+spa_status_t spa_attn_fwd_noalloc(const void* Q, const void* K, const void* V, const void* P,
+                                  float scale, int causal, int B, int H, int N, int d, int m,
+                                  int dv, spa_dtype_t dtype, void* O, spa_dtype_t o_dtype,
+                                  float* lse, void* stream) {
+    g_err[0] = '\0';
+    const char* fn = "spa_attn_fwd_noalloc";
+    // The size check needs only the dimensions; everything else is validated by the
+    // forward before any HIP work.
+    spa_status_t st = check_dims(fn, B, H, N, d, m, dv);
+    if (st != SPA_OK) return st;
+    st = check_shape_support(fn, dtype, d, m, dv);
+    if (st != SPA_OK) return st;
+    const size_t need = workspace_layout(B * H, N, m, dv, dtype).total;
+    if (need > kScratchBytes)
+        return fail(SPA_ERR_UNSUPPORTED,
+                    "%s: these sizes need %zu bytes of workspace, more than the %zu of the "
+                    "library's static scratch; use spa_attn_fwd with a workspace",
+                    fn, need, kScratchBytes);
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != SPA_OK) return st;
+    return attn_fwd_impl(fn, Q, K, V, P, scale, causal, B, H, N, d, m, dv, dtype, O, o_dtype,
+                         lse, ws, kScratchBytes, stream, false);
 }
 
 spa_status_t spa_kcache_append(const void* K, const void* P, void* cache, int B, int H, int N,
