@@ -44,12 +44,20 @@ typedef enum spa_status {
                                      misaligned or overlapping buffers */
     SPA_ERR_UNSUPPORTED = 2,      /* a valid shape or dtype with no compiled kernel */
     SPA_ERR_WORKSPACE = 3,        /* workspace given but smaller than required */
-    SPA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+    SPA_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed */
+    /* Not statuses: these give the type the range of int, so that any int a caller passes
+       (e.g. to spa_status_string) is a value C++ may load and compare. */
+    SPA_STATUS_INT_MIN_ = -2147483647 - 1,
+    SPA_STATUS_INT_MAX_ = 2147483647
 } spa_status_t;
 
 typedef enum spa_dtype {
     SPA_F32 = 0, /* IEEE binary32 */
-    SPA_BF16 = 1 /* bfloat16 (8-bit exponent, 7-bit stored mantissa) */
+    SPA_BF16 = 1, /* bfloat16 (8-bit exponent, 7-bit stored mantissa) */
+    /* Not dtypes: these give the type the range of int, so that any int a caller passes is a
+       value the library may load, compare and reject (SPA_ERR_INVALID_ARGUMENT). */
+    SPA_DTYPE_INT_MIN_ = -2147483647 - 1,
+    SPA_DTYPE_INT_MAX_ = 2147483647
 } spa_dtype_t;
 
 /* Library version, major*10000 + minor*100 + patch. */

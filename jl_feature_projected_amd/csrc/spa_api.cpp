@@ -185,6 +185,7 @@ const char* spa_status_string(spa_status_t s) {
         case SPA_ERR_UNSUPPORTED: return "SPA_ERR_UNSUPPORTED";
         case SPA_ERR_WORKSPACE: return "SPA_ERR_WORKSPACE";
         case SPA_ERR_HIP: return "SPA_ERR_HIP";
+        default: break;
     }
     return "SPA_ERR_UNKNOWN";
 }

@@ -40,6 +40,8 @@ def test_version_and_status_strings(L):
     for code, name in ((0, "SPA_OK"), (1, "SPA_ERR_INVALID_ARGUMENT"), (2, "SPA_ERR_UNSUPPORTED"),
                        (3, "SPA_ERR_WORKSPACE"), (4, "SPA_ERR_HIP")):
         assert L.spa_status_string(code).decode() == name
+    for code in (-1, 5, 99, 2 ** 31 - 1):
+        assert L.spa_status_string(code).decode() == "SPA_ERR_UNKNOWN"
 
 
 def _attn(L, **kw):
