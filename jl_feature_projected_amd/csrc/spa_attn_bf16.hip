@@ -77,11 +77,15 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     // core (16x16x32 MFMAs over the packed weights), off the VALU.
     constexpr bool kNormMfma = QB != 1;
 
-    // QB = 1: two buffers, each one K tile and one V^T tile. QB = 2: rings of three K tiles
-    // (at offset 0) and three V^T tiles (at RING_V), so that a step can read the operands of
-    // the next one before its closing barrier. The exact fallback uses the two-buffer layout.
-    constexpr int NBUF = QB == 1 ? 2 : 3;
+    // Two buffers, each one K tile and one V^T tile, at TWO_BUF (the per-tile loop; for
+    // QB = 1 also the pipelined steps). QB = 2 adds rings of three K tiles (at offset 0) and
+    // three V^T tiles (at RING_V) ahead of them, so that a pipelined step can read the
+    // operands of the next one before its closing barrier, and has four buffers at TWO_BUF
+    // (the first two are the per-tile loop's): the tiles with masked keys (at most
+    // kBR / kBC), all copied at the start.
+    constexpr int NBUF = QB == 1 ? 2 : 7;
     constexpr int RING_V = 3 * K_BYTES;
+    constexpr int TWO_BUF = QB == 1 ? 0 : 3 * BUF;
     __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF];
 
     // Workgroup -> (head, query block). Workgroups are handed to the 8 XCDs round-robin;
@@ -150,8 +154,8 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < VPW; ++i) copy16_to_lds(vr, lds_wave + at + 1024 * kWaves * i, voff[i]);
     };
-    auto copy_k = [&](int k0, int buf) { copy_k_to(k0, buf * BUF); };
-    auto copy_v = [&](int k0, int buf) { copy_v_to(k0, buf * BUF + K_BYTES); };
+    auto copy_k = [&](int k0, int buf) { copy_k_to(k0, TWO_BUF + buf * BUF); };
+    auto copy_v = [&](int k0, int buf) { copy_v_to(k0, TWO_BUF + buf * BUF + K_BYTES); };
     // Ring slots (QB = 2): tile t's keys at kslot(t % 3), its V^T at vslot(t % 3).
     auto kslot = [](int r) { return r * K_BYTES; };
     auto vslot = [](int r) { return RING_V + r * V_BYTES; };
@@ -169,13 +173,20 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
         copy_v(0, 0);
         if (PIPELINED && ntiles > 1) copy_k(kBC, 1);
     } else {
-        copy_k_to(0, kslot(0));
-        copy_v_to(0, vslot(0));
-        if (ntiles > 1) {
+        // Every tile with a masked key (buffer d holds tile nfull + d), then the ring's.
+        for (int d = 0; d < ntiles - nfull; ++d) {
+            copy_k((nfull + d) * kBC, d);
+            copy_v((nfull + d) * kBC, d);
+        }
+        if (nfull > 0) {
+            copy_k_to(0, kslot(0));
+            copy_v_to(0, vslot(0));
+        }
+        if (nfull > 1) {
             copy_k_to(kBC, kslot(1));
             copy_v_to(kBC, vslot(1));
         }
-        if (ntiles > 2) copy_k_to(2 * kBC, kslot(2));
+        if (nfull > 2) copy_k_to(2 * kBC, kslot(2));
     }
 
     // This lane's queries as the B operand of the score MFMA (zero past N).
@@ -533,7 +544,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
                 copy_k(k0 + kBC, (t + 1) & 1);
                 copy_v(k0 + kBC, (t + 1) & 1);
             }
-            const char* Ks = lds + (t & 1) * BUF;
+            const char* Ks = lds + TWO_BUF + (t & 1) * BUF;
             const char* Vs = Ks + K_BYTES;
 
             if (!CAUSAL || k0 <= qw0 + WQ - 1) {
@@ -722,67 +733,29 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
             // from its V^T slot (the first PF operands already in va), and before its closing
             // barrier reads the key operands of tile t+2 and the first V operands of tile
             // t+1 -- tiles whose copies were awaited before an earlier barrier.
-            int klim[QB];
-#pragma unroll
-            for (int b = 0; b < QB; ++b) klim[b] = CAUSAL ? min(myq[b], N - 1) : N - 1;
-            auto rel_of = [&](int k0, int (&rel)[QB]) {
-#pragma unroll
-                for (int b = 0; b < QB; ++b) rel[b] = klim[b] - k0 - 4 * half;
-            };
-            const int rel0[QB] = {};
-            auto wave_needs = [&](int t) { return !CAUSAL || t * kBC <= qw0 + WQ - 1; };
+            // Only the tiles [0, nfull) with no masked key for the whole workgroup run here (the
+            // per-tile loop has done the rest); their first copies were issued at the top.
+            const int nf = nfull;
+            if (nf == 0) return 0;
             u32x4 pa[QB][2][2], pb[QB][2][2];
             u32x4 ka[2][KS], va[NPV];
             {
                 f32x16 s[QB][2];
                 scores(lds + kslot(0), s);
-                if (nfull == 0) {
-                    int rel[QB];
-                    rel_of(0, rel);
-#pragma unroll
-                    for (int b = 0; b < QB; ++b)
-#pragma unroll
-                        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                                for (int j = 0; j < 4; ++j)
-                                    pa[b][kb][tt][j] =
-                                        weight_pair(s, b, kb, tt, j, std::true_type{}, rel[b]);
-                } else {
-                    weights(s, pa);
-                }
+                weights(s, pa);
             }
-            if (ntiles > 1) load_ka(lds + kslot(1), ka);
+            if (nf > 1) load_ka(lds + kslot(1), ka);
             load_va_prefix(lds + vslot(0), va);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();  // K[0] read by every wave before step 0 refills its slot
-            // Tiles below wfull have no masked key for any query of this wave.
-            const int wfull = CAUSAL ? min(N / kBC, qw0 / kBC) : N / kBC;
-            // Step t with ring slot S = t % 3. The generic variant (the causal diagonal, the
-            // ragged tail) picks per wave the unmasked step, the masked one, or only the PV
-            // of tile t when the wave has no admissible key in tile t+1.
-            auto ring_step = [&](int S, int t, const u32x4 (&p)[QB][2][2], u32x4 (&pn)[QB][2][2],
-                                 auto generic) {
-                constexpr bool GENERIC = decltype(generic)::value;
+            const int rel0[QB] = {};
+            // Step t with ring slot S = t % 3 (a constant in the unrolled loop).
+            auto ring_step = [&](int S, int t, const u32x4 (&p)[QB][2][2],
+                                 u32x4 (&pn)[QB][2][2]) {
                 const int S1 = S == 2 ? 0 : S + 1, S2 = S == 0 ? 2 : S - 1;
-                if (t + 3 < ntiles) copy_k_to((t + 3) * kBC, kslot(S));
-                if (t + 2 < ntiles) copy_v_to((t + 2) * kBC, vslot(S2));
-                if (!GENERIC || t + 1 < wfull) {
-                    step_core(ka, va, lds + vslot(S), p, pn, std::false_type{}, rel0);
-                } else if (wave_needs(t + 1)) {
-                    int rel[QB];
-                    rel_of((t + 1) * kBC, rel);
-                    step_core(ka, va, lds + vslot(S), p, pn, std::true_type{}, rel);
-                } else {
-                    if (wave_needs(t)) pv(lds + vslot(S), p);
-#pragma unroll
-                    for (int b = 0; b < QB; ++b)
-#pragma unroll
-                        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                            for (int tt = 0; tt < 2; ++tt) pn[b][kb][tt] = u32x4{0u, 0u, 0u, 0u};
-                }
+                if (t + 3 < nf) copy_k_to((t + 3) * kBC, kslot(S));
+                if (t + 2 < nf) copy_v_to((t + 2) * kBC, vslot(S2));
+                step_core(ka, va, lds + vslot(S), p, pn, std::false_type{}, rel0);
                 // (Past the last tile these read a slot no copy refills: unused values.)
                 load_ka(lds + kslot(S2), ka);
                 load_va_prefix(lds + vslot(S1), va);
@@ -790,40 +763,73 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
                 __syncthreads();
             };
             int t = 0;
-            // Steps whose next tile is unmasked for the whole workgroup, six per trip:
-            // constant ring slots, and the weights back in pa at the end of a trip.
+            // Six steps per trip: constant ring slots, and the weights back in pa at the end.
 #pragma unroll 1
-            for (; t + 6 < nfull; t += 6) {
-                ring_step(0, t, pa, pb, std::false_type{});
-                ring_step(1, t + 1, pb, pa, std::false_type{});
-                ring_step(2, t + 2, pa, pb, std::false_type{});
-                ring_step(0, t + 3, pb, pa, std::false_type{});
-                ring_step(1, t + 4, pa, pb, std::false_type{});
-                ring_step(2, t + 5, pb, pa, std::false_type{});
+            for (; t + 6 < nf; t += 6) {
+                ring_step(0, t, pa, pb);
+                ring_step(1, t + 1, pb, pa);
+                ring_step(2, t + 2, pa, pb);
+                ring_step(0, t + 3, pb, pa);
+                ring_step(1, t + 4, pa, pb);
+                ring_step(2, t + 5, pb, pa);
             }
-            bool in_b = false;  // the weights of tile t are in pb (else pa)
-            // The rest: up to five unmasked steps, the causal diagonal (kBR / kBC tiles)
-            // and the ragged tail.
-#pragma unroll 1
-            for (; t + 1 < ntiles; ++t) {
-                if (!in_b)
-                    ring_step(t % 3, t, pa, pb, std::true_type{});
-                else
-                    ring_step(t % 3, t, pb, pa, std::true_type{});
-                in_b = !in_b;
+            // The r < 6 steps left start, like every trip, at ring slot 0 with the weights in
+            // pa: each keeps its constant slot and weight array; the last tile's PV follows.
+            const int r = nf - 1 - t;
+            if (r >= 1) ring_step(0, t, pa, pb);
+            if (r >= 2) ring_step(1, t + 1, pb, pa);
+            if (r >= 3) ring_step(2, t + 2, pa, pb);
+            if (r >= 4) ring_step(0, t + 3, pb, pa);
+            if (r >= 5) ring_step(1, t + 4, pa, pb);
+            switch (r) {
+                case 0: pv(lds + vslot(0), pa); break;
+                case 1: pv(lds + vslot(1), pb); break;
+                case 2: pv(lds + vslot(2), pa); break;
+                case 3: pv(lds + vslot(0), pb); break;
+                case 4: pv(lds + vslot(1), pa); break;
+                default: pv(lds + vslot(2), pb); break;
             }
-            if (wave_needs(t)) {
-                if (in_b)
-                    pv(lds + vslot(t % 3), pb);
-                else
-                    pv(lds + vslot(t % 3), pa);
-            }
-            return ntiles;
+            return nf;
         }
     };
 
     init_state(bound);
-    tile_loop(std::false_type{}, fast_phase());
+    if constexpr (QB == 1) {
+        tile_loop(std::false_type{}, fast_phase());
+    } else {
+        // The tiles with masked keys first (the causal diagonal, the ragged tail), one at a
+        // time, while the ring's first copies land; then the pipelined ring over the rest.
+        // The static offset makes the softmax independent of the tile order.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // Tiles are read only here, so no barrier between them: a wave with no admissible
+        // key in a tile skips it.
+        int klim[QB];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) klim[b] = CAUSAL ? min(myq[b], N - 1) : N - 1;
+#pragma unroll 1
+        for (int d = 0; d < ntiles - nfull; ++d) {
+            const int t = nfull + d;
+            if (CAUSAL && t * kBC > qw0 + WQ - 1) continue;
+            const char* Ks = lds + TWO_BUF + d * BUF;
+            f32x16 s[QB][2];
+            scores(Ks, s);
+            u32x4 p[QB][2][2];
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                const int rel = klim[b] - t * kBC - 4 * half;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            p[b][kb][tt][j] = weight_pair(s, b, kb, tt, j, std::true_type{}, rel);
+            }
+            pv(Ks + K_BYTES, p);
+        }
+        fast_phase();
+    }
     float ltot[QB];
     bool low = false;
 #pragma unroll
@@ -896,7 +902,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
 // by 64 queries) where the register file holds them and the grid still has several
 // workgroups per CU; one otherwise.
 inline int pick_qb(int BH, int N, int mp, bool causal) {
-    if (mp > 32 || causal) return 1;
+    if (mp > 32) return 1;
     const long long wgs2 = (long long)BH * ((N + 255) / 256);
     return wgs2 >= 512 ? 2 : 1;
 }
@@ -917,8 +923,9 @@ hipError_t launch_c(const void* Qt, const void* Kt, const void* V, const float* 
                     float* lse, int BH, int N, bool causal, bool out_f32, int qb,
                     hipStream_t stream) {
     if constexpr (MP <= 32) {
-        if (qb == 2 && !causal)
-            return launch<MP, DV, false, 2>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream);
+        if (qb == 2)
+            return causal ? launch<MP, DV, true, 2>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream)
+                          : launch<MP, DV, false, 2>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream);
     }
     return causal ? launch<MP, DV, true, 1>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream)
                   : launch<MP, DV, false, 1>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream);
