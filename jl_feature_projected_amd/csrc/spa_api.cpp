@@ -330,12 +330,16 @@ spa_status_t attn_fwd_impl(const char* fn, const void* Q, const void* K, const v
             // significand holds the score error well inside the bf16 path's tolerance where
             // bf16 operands (8 bits) do not, at the same MFMA rate.
             const float qscale = scale * 1.44269504088896340736f;
+            // V^T is written only for the attention variant that reads it.
+            const bool vrows = spa::attn_bf16_reads_v_rows(B * H, N, mp, dv, causal == 1);
             e = spa::launch_project_bf16(Q, K, P, Qt, Kt, 2, B * H, H, N, d, m, mp, mp, qscale,
-                                         1.0f, /*out_f16=*/true, kmax, V, Vt, dv, s);
+                                         1.0f, /*out_f16=*/true, kmax, vrows ? nullptr : V,
+                                         vrows ? nullptr : Vt, dv, s);
             if (e == hipSuccess && ev[1]) e = hipEventRecord(ev[1], s);
             if (e == hipSuccess)
-                e = spa::launch_attn_bf16(Qt, Kt, Vt, kmax, O, lse, B * H, N, mp, dv,
-                                          causal == 1, o_dtype == SPA_F32, s);
+                e = spa::launch_attn_bf16(Qt, Kt, vrows ? nullptr : Vt, vrows ? V : nullptr,
+                                          kmax, O, lse, B * H, N, mp, dv, causal == 1,
+                                          o_dtype == SPA_F32, s);
         } else {
             e = spa::launch_project_f32(static_cast<const float*>(Q),
                                         static_cast<const float*>(P), static_cast<float*>(Qt),
@@ -648,7 +652,7 @@ spa_status_t spa_sfa_fwd(const void* Q, const void* K, const void* V, int topk, 
         e = spa::launch_project_bf16(nullptr, nullptr, nullptr, nullptr, nullptr, 0, B * H, H,
                                      N, d, 1, 1, 1, 1.0f, 1.0f, true, nullptr, V, Vt, dv, s);
     if (e == hipSuccess)
-        e = spa::launch_attn_bf16(Qt, Kt, Vt, kmax, O, lse, B * H, N, d, dv, causal == 1,
+        e = spa::launch_attn_bf16(Qt, Kt, Vt, nullptr, kmax, O, lse, B * H, N, d, dv, causal == 1,
                                   o_dtype == SPA_F32, s);
     if (!workspace) {
         hipError_t e2 = hipFreeAsync(ws, s);

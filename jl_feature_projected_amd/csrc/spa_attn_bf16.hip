@@ -56,19 +56,27 @@ constexpr float kTau = 8.0f;
 template <int MP, int DV, bool CAUSAL, int QB>
 __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Kt, const bf16_t* __restrict__ Vt,
-    const float* __restrict__ kmax, void* __restrict__ O, float* __restrict__ lse, int N, int nqb,
-    int out_f32) {
+    const bf16_t* __restrict__ Vrow, const float* __restrict__ kmax, void* __restrict__ O,
+    float* __restrict__ lse, int N, int nqb, int out_f32) {
     constexpr int kBR = kWaves * 32 * QB;    // queries per workgroup
     constexpr int WQ = 32 * QB;              // queries per wave
     constexpr int KS = MP / 16;              // score MFMA k-steps
     constexpr int KCH = MP / 8;              // 16-byte chunks per projected-key row
     constexpr int K_BYTES = kBC * MP * 2;    // one K tile
-    constexpr int V_BYTES = kBC * DV * 2;    // one V^T tile (DV rows of 64 keys)
+    // VDIRECT (QB = 2, DV = 128): V tiles are row-major V as stored, one key per row, and
+    // each PV operand is two transposing LDS reads (ds_read_b64_tr_b16). Within a row the
+    // 16-byte slots are permuted by an XOR with vxswz(row % 4), so that the four rows one
+    // transposing read touches fall on disjoint banks. Otherwise V^T tiles as the
+    // preparation launch writes them, each operand one 16-byte read.
+    constexpr bool VDIRECT = QB == 2 && DV == 128;
+    constexpr int VP = DV * 2;               // VDIRECT: LDS bytes per key row
+    constexpr int V_BYTES = VDIRECT ? kBC * VP : kBC * DV * 2;  // one V (or V^T) tile
     constexpr int BUF = K_BYTES + V_BYTES;   // one LDS buffer
     constexpr int KINS = K_BYTES / 1024;     // 64-lane x 16-byte copies per K tile (2 .. 16)
     constexpr int VINS = V_BYTES / 1024;     // ... per V tile (8 or 16)
     constexpr int DB = DV / 32;              // 32-row blocks of V^T / O^T
     static_assert(KINS >= 2 && VINS % kWaves == 0, "tile copy split");
+    static_assert(V_BYTES % 1024 == 0, "whole copies per V tile");
     static_assert(QB == 1 || QB == 2, "query blocks per wave");
     // With one wave per SIMD the weight stages (exp, pack, sum) of a pair are spread over
     // consecutive MFMA slots; with two, the other wave fills their latency.
@@ -110,7 +118,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* Qh = Qt + (size_t)bh * N * MP;
     const uint16_t* Kh = Kt + (size_t)bh * N * MP;
     const int Np = vt_padded_keys(N);  // row length of V^T
-    const bf16_t* Vh = Vt + (size_t)bh * DV * Np;
+    const bf16_t* Vh = VDIRECT ? Vrow + (size_t)bh * N * DV : Vt + (size_t)bh * DV * Np;
 
     const int kend = CAUSAL ? min(N, q0 + kBR) : N;
     const int ntiles = (kend + kBC - 1) / kBC;
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     // Copies are dealt round-robin to the waves (wave w issues j = w, w + 4, ...); the
     // global byte offsets are fixed per lane, a tile only moves the descriptor's base.
     constexpr int KPW = (KINS + kWaves - 1) / kWaves;  // K copies per wave (the last may idle)
-    constexpr int VPW = VINS / kWaves;                 // V copies per wave
+    constexpr int VPW = (VINS + kWaves - 1) / kWaves;  // V copies per wave (the last may idle)
     uint32_t koff[KPW], voff[VPW];
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
@@ -133,8 +141,15 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < VPW; ++i) {
         const int c = 64 * (wave + kWaves * i) + lane;
-        const int row = c >> 3;  // V column
-        voff[i] = row * Np * 2 + 16 * ((c & 7) ^ vtswz(row));
+        if constexpr (VDIRECT) {
+            // LDS slot c of the tile: key row c / 16, bytes 16 * (c % 16) of that row, which
+            // hold the row's bytes at that offset XOR vxswz(row % 4)
+            const int row = c >> 4;
+            voff[i] = row * VP + ((16 * (c & 15)) ^ vxswz(row & 3));
+        } else {
+            const int row = c >> 3;  // V column
+            voff[i] = row * Np * 2 + 16 * ((c & 7) ^ vtswz(row));
+        }
     }
     // LDS byte address of this wave's first copy slot in buffer 0 (wave-uniform; the M0
     // values below are this plus constants).
@@ -150,9 +165,13 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
         }
     };
     auto copy_v_to = [&](int k0, int at) {
-        const u32x4 vr = make_rsrc(Vh + k0, (uint32_t)(DV * Np - k0) * 2);
+        const u32x4 vr = VDIRECT ? make_rsrc(Vh + (size_t)k0 * DV, (uint32_t)(N - k0) * DV * 2)
+                                 : make_rsrc(Vh + k0, (uint32_t)(DV * Np - k0) * 2);
 #pragma unroll
-        for (int i = 0; i < VPW; ++i) copy16_to_lds(vr, lds_wave + at + 1024 * kWaves * i, voff[i]);
+        for (int i = 0; i < VPW; ++i) {
+            const int j = wave + kWaves * i;
+            if (j < VINS) copy16_to_lds(vr, lds_wave + at + 1024 * kWaves * i, voff[i]);
+        }
     };
     auto copy_k = [&](int k0, int buf) { copy_k_to(k0, TWO_BUF + buf * BUF); };
     auto copy_v = [&](int k0, int buf) { copy_v_to(k0, TWO_BUF + buf * BUF + K_BYTES); };
@@ -220,6 +239,17 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
             vread[kb][tt] = col * 128 + 16 * ((4 * kb + 2 * tt + half) ^ vtswz(col));
+    // VDIRECT operand reads: lane l of 16-lane group (half, gc) addresses key row
+    // r = 4*half + (l & 15) / 4 and columns 16*gc + 4*(l & 3) .. +3 of V block db, i.e. row
+    // bytes (64*db + 32*gc + 8*(l & 3)) ^ vxswz(r % 4) = vdir[db]; the step's rows (multiples
+    // of 8, so r % 4 is the lane's) are added as immediates.
+    int vdir[DB];
+    {
+        const int r = 4 * half + ((lane & 15) >> 2);
+        const int cb = 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vdir[db] = r * VP + ((64 * db + cb) ^ vxswz(r & 3));
+    }
 
     // ---- score bound: M = |q| * max |k| over the key blocks this workgroup reads -------
     float kmx = 0.0f;
@@ -319,9 +349,26 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     // block; the V operand is read once. Slot 8*half + j of k-step tt in key block kb holds
     // key kb*32 + 16*tt + 8*(j/4) + 4*half + j%4, in the score accumulator and in the V^T
     // tile alike.
+    // The A operand of PV step (db, kb, tt): 8 keys (in the score accumulator's slot order)
+    // of V column db*32 + col. VDIRECT: two transposing reads; in each, a 16-lane group
+    // reads 4 key rows x 16 columns and lane i receives column i of the 4 rows.
+    auto vop = [&](const char* Vs, int db, int kb, int tt) -> u32x4 {
+        if constexpr (VDIRECT) {
+            typedef short v4i16 __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+            const char* base = Vs + vdir[db] + (kb * 32 + 16 * tt) * VP;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(__attribute__((address_space(3))) char*)(base));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(__attribute__((address_space(3))) char*)(base + 8 * VP));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            return u32x4{l2.x, l2.y, h2.x, h2.y};
+        } else {
+            return *reinterpret_cast<const u32x4*>(Vs + db * 32 * 128 + vread[kb][tt]);
+        }
+    };
     auto pv_step = [&](const char* Vs, const u32x4 (&p)[QB][2][2], int db, int kb, int tt) {
-        const bf16x8 a = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(Vs + db * 32 * 128 + vread[kb][tt]));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, vop(Vs, db, kb, tt));
 #pragma unroll
         for (int b = 0; b < QB; ++b)
             acc[b][db] = mfma32x32x16(a, __builtin_bit_cast(bf16x8, p[b][kb][tt]), acc[b][db]);
@@ -372,7 +419,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
                 ka[kb][ks] = *reinterpret_cast<const u32x4*>(Kn + kread[kb][ks]);
     };
     auto vload = [&](const char* Vs, u32x4 (&va)[NPV], int i) {
-        va[i] = *reinterpret_cast<const u32x4*>(Vs + pv_db(i) * 32 * 128 + vread[pv_kb(i)][pv_tt(i)]);
+        va[i] = vop(Vs, pv_db(i), pv_kb(i), pv_tt(i));
     };
     auto load_va_prefix = [&](const char* Vs, u32x4 (&va)[NPV]) {
 #pragma unroll
@@ -908,51 +955,57 @@ inline int pick_qb(int BH, int N, int mp, bool causal) {
 }
 
 template <int MP, int DV, bool CAUSAL, int QB>
-hipError_t launch(const void* Qt, const void* Kt, const void* Vt, const float* kmax, void* O,
-                  float* lse, int BH, int N, bool out_f32, hipStream_t stream) {
+hipError_t launch(const void* Qt, const void* Kt, const void* Vt, const void* Vrow,
+                  const float* kmax, void* O, float* lse, int BH, int N, bool out_f32,
+                  hipStream_t stream) {
     constexpr int kBR = kWaves * 32 * QB;
     const int nqb = (N + kBR - 1) / kBR;
     attn_bf16_kernel<MP, DV, CAUSAL, QB><<<dim3(nqb * BH), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(Qt), static_cast<const uint16_t*>(Kt),
-        static_cast<const bf16_t*>(Vt), kmax, O, lse, N, nqb, out_f32 ? 1 : 0);
+        static_cast<const bf16_t*>(Vt), static_cast<const bf16_t*>(Vrow), kmax, O, lse, N, nqb,
+        out_f32 ? 1 : 0);
     return hipGetLastError();
 }
 
 template <int MP, int DV>
-hipError_t launch_c(const void* Qt, const void* Kt, const void* V, const float* kmax, void* O,
-                    float* lse, int BH, int N, bool causal, bool out_f32, int qb,
-                    hipStream_t stream) {
+hipError_t launch_c(const void* Qt, const void* Kt, const void* Vt, const void* Vrow,
+                    const float* kmax, void* O, float* lse, int BH, int N, bool causal,
+                    bool out_f32, int qb, hipStream_t stream) {
     if constexpr (MP <= 32) {
         if (qb == 2)
-            return causal ? launch<MP, DV, true, 2>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream)
-                          : launch<MP, DV, false, 2>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream);
+            return causal ? launch<MP, DV, true, 2>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, stream)
+                          : launch<MP, DV, false, 2>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, stream);
     }
-    return causal ? launch<MP, DV, true, 1>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream)
-                  : launch<MP, DV, false, 1>(Qt, Kt, V, kmax, O, lse, BH, N, out_f32, stream);
+    return causal ? launch<MP, DV, true, 1>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, stream)
+                  : launch<MP, DV, false, 1>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, stream);
 }
 
 template <int MP>
-hipError_t launch_dv(const void* Qt, const void* Kt, const void* V, const float* kmax, void* O,
-                     float* lse, int BH, int N, int dv, bool causal, bool out_f32, int qb,
-                     hipStream_t stream) {
+hipError_t launch_dv(const void* Qt, const void* Kt, const void* Vt, const void* Vrow,
+                     const float* kmax, void* O, float* lse, int BH, int N, int dv, bool causal,
+                     bool out_f32, int qb, hipStream_t stream) {
     switch (dv) {
-        case 64: return launch_c<MP, 64>(Qt, Kt, V, kmax, O, lse, BH, N, causal, out_f32, qb, stream);
-        case 128: return launch_c<MP, 128>(Qt, Kt, V, kmax, O, lse, BH, N, causal, out_f32, qb, stream);
+        case 64: return launch_c<MP, 64>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, causal, out_f32, qb, stream);
+        case 128: return launch_c<MP, 128>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, causal, out_f32, qb, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* V, const float* kmax,
-                            void* O, float* lse, int BH, int N, int mp, int dv, bool causal,
-                            bool out_f32, hipStream_t stream) {
+bool attn_bf16_reads_v_rows(int BH, int N, int mp, int dv, bool causal) {
+    return pick_qb(BH, N, mp, causal) == 2 && dv == 128;
+}
+
+hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* Vt, const void* Vrow,
+                            const float* kmax, void* O, float* lse, int BH, int N, int mp,
+                            int dv, bool causal, bool out_f32, hipStream_t stream) {
     const int qb = pick_qb(BH, N, mp, causal);
     switch (mp) {
-        case 16: return launch_dv<16>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
-        case 32: return launch_dv<32>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
-        case 64: return launch_dv<64>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
-        case 128: return launch_dv<128>(Qt, Kt, V, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
+        case 16: return launch_dv<16>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
+        case 32: return launch_dv<32>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
+        case 64: return launch_dv<64>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
+        case 128: return launch_dv<128>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -150,6 +150,11 @@ __device__ __forceinline__ int kswz(int row) {
     return (row & 1 ? b0 : 0) ^ (row & 2 ? b1 : 0) ^ (row & 4 ? b2 : 0) ^ (row & 8 ? b3 : 0);
 }
 __device__ __forceinline__ int vtswz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// Row-major V tile (rows of 256 bytes), transposing PV operand read: a 16-lane group takes 32
+// bytes of each of 4 consecutive rows, two groups 64 bytes of the same rows. Byte offsets in
+// row r are XORed with vxswz(r % 4) (it moves whole 32-byte blocks), which sends the 4 rows to
+// 4 distinct quarters of 128 bytes and of 256 bytes alike.
+__device__ __forceinline__ int vxswz(int r3) { return 64 * r3 + 32 * (r3 >> 1); }
 
 // As copy16_to_lds, 4 bytes per lane, to m0 + 4 * lane.
 __device__ __forceinline__ void copy4_to_lds(u32x4 rsrc, uint32_t m0, uint32_t voff) {

@@ -38,12 +38,15 @@ hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, vo
 
 // Attention over projected inputs. Qt and Kt are fp16 [BH, N, mp] with zero columns past m
 // (score MFMA in fp16); Qt is pre-scaled by scale*log2(e) so the scores come out in base-2
-// exponent units. Vt is V^T as written by launch_project_bf16 (weights x V MFMA in bf16). O is
-// [BH, N, dv] in fp32 (out_f32) or bf16; lse [BH, N] optional. kmax holds the per-block key
-// norm maxima written by the projection launch.
-hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* Vt, const float* kmax,
-                            void* O, float* lse, int BH, int N, int mp, int dv, bool causal,
-                            bool out_f32, hipStream_t stream);
+// exponent units. The weights x V MFMA (bf16) reads V^T as written by launch_project_bf16
+// (Vt) or, when attn_bf16_reads_v_rows(...) is true for these sizes, V itself ([BH, N, dv]
+// bf16, Vrow); the other pointer may be null. O is [BH, N, dv] in fp32 (out_f32) or bf16;
+// lse [BH, N] optional. kmax holds the per-block key norm maxima written by the projection
+// launch.
+bool attn_bf16_reads_v_rows(int BH, int N, int mp, int dv, bool causal);
+hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* Vt, const void* Vrow,
+                            const float* kmax, void* O, float* lse, int BH, int N, int mp,
+                            int dv, bool causal, bool out_f32, hipStream_t stream);
 
 // Backward of the bf16 path. The preparation launch (launch_project_bf16 with the queries
 // scaled by scale*log2(e), fp16 outputs, the transposed copies Qst and Ktt, and dO
