@@ -187,16 +187,8 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     constexpr bool PIPELINED = !(QB == 1 && MP == 128 && DV == 128);
     // Tiles with no masked key for any query of the workgroup.
     const int nfull = CAUSAL ? min(ntiles, q0 / kBC) : N / kBC;
-    if constexpr (QB == 1) {
-        copy_k(0, 0);
-        copy_v(0, 0);
-        if (PIPELINED && ntiles > 1) copy_k(kBC, 1);
-    } else {
-        // Every tile with a masked key (buffer d holds tile nfull + d), then the ring's.
-        for (int d = 0; d < ntiles - nfull; ++d) {
-            copy_k((nfull + d) * kBC, d);
-            copy_v((nfull + d) * kBC, d);
-        }
+    // The copies of the ring's first tiles: K and V of tiles 0 and 1, K of tile 2.
+    auto copy_ring_start = [&]() {
         if (nfull > 0) {
             copy_k_to(0, kslot(0));
             copy_v_to(0, vslot(0));
@@ -206,6 +198,19 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
             copy_v_to(kBC, vslot(1));
         }
         if (nfull > 2) copy_k_to(2 * kBC, kslot(2));
+    };
+    if constexpr (QB == 1) {
+        copy_k(0, 0);
+        copy_v(0, 0);
+        if (PIPELINED && ntiles > 1) copy_k(kBC, 1);
+    } else {
+        // Every tile with a masked key (buffer d holds tile nfull + d); the ring's first
+        // tiles here too when there is none, else once those have landed (below).
+        for (int d = 0; d < ntiles - nfull; ++d) {
+            copy_k((nfull + d) * kBC, d);
+            copy_v((nfull + d) * kBC, d);
+        }
+        if (ntiles == nfull) copy_ring_start();
     }
 
     // This lane's queries as the B operand of the score MFMA (zero past N).
@@ -431,7 +436,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
                          const u32x4 (&p)[QB][2][2], u32x4 (&pn)[QB][2][2], auto masked,
                          const int (&rel)[QB]) {
         constexpr int NM = NPV * QB;     // PV MFMAs per tile
-        constexpr int WSTART = 3;        // first PV MFMA that weight work is placed after
+        constexpr int WSTART = QB == 1 ? 3 : 2;  // first PV MFMA that weight work follows
         constexpr int NU = 16 * QB;      // weight pairs per tile
         // Weight pair u: key block u / (8 QB), query block (u / 8) % QB, k-step (u / 4) % 2,
         // pair u % 4 -- the order in which the score MFMAs finish. Slot i >= WSTART takes
@@ -846,9 +851,12 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     } else {
         // The tiles with masked keys first (the causal diagonal, the ragged tail), one at a
         // time, while the ring's first copies land; then the pipelined ring over the rest.
-        // The static offset makes the softmax independent of the tile order.
+        // The static offset makes the softmax independent of the tile order. (The queries
+        // and key-norm bounds are loaded after the copies of the masked tiles, so waiting
+        // for them waits for those copies too; the ring's are issued only now.)
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if (ntiles != nfull) copy_ring_start();
         // Tiles are read only here, so no barrier between them: a wave with no admissible
         // key in a tile skips it.
         int klim[QB];
