@@ -330,16 +330,19 @@ spa_status_t attn_fwd_impl(const char* fn, const void* Q, const void* K, const v
             // significand holds the score error well inside the bf16 path's tolerance where
             // bf16 operands (8 bits) do not, at the same MFMA rate.
             const float qscale = scale * 1.44269504088896340736f;
-            // V^T is written only for the attention variant that reads it.
+            // V^T is written only for the attention variant that reads it, and the queries
+            // are projected here only for the variant that does not project them itself.
             const bool vrows = spa::attn_bf16_reads_v_rows(B * H, N, mp, dv, causal == 1);
-            e = spa::launch_project_bf16(Q, K, P, Qt, Kt, 2, B * H, H, N, d, m, mp, mp, qscale,
-                                         1.0f, /*out_f16=*/true, kmax, vrows ? nullptr : V,
-                                         vrows ? nullptr : Vt, dv, s);
+            const bool qfold = spa::attn_bf16_projects_queries(B * H, N, mp, d, causal == 1);
+            e = spa::launch_project_bf16(qfold ? nullptr : Q, K, P, Qt, Kt, 2, B * H, H, N, d, m,
+                                         mp, mp, qscale, 1.0f, /*out_f16=*/true, kmax,
+                                         vrows ? nullptr : V, vrows ? nullptr : Vt, dv, s);
             if (e == hipSuccess && ev[1]) e = hipEventRecord(ev[1], s);
             if (e == hipSuccess)
                 e = spa::launch_attn_bf16(Qt, Kt, vrows ? nullptr : Vt, vrows ? V : nullptr,
                                           kmax, O, lse, B * H, N, mp, dv, causal == 1,
-                                          o_dtype == SPA_F32, s);
+                                          o_dtype == SPA_F32, s, qfold ? Q : nullptr, P,
+                                          qscale, d, H, m);
         } else {
             e = spa::launch_project_f32(static_cast<const float*>(Q),
                                         static_cast<const float*>(P), static_cast<float*>(Qt),

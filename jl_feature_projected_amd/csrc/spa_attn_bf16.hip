@@ -53,11 +53,22 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBC = 64;   // keys per tile
 constexpr float kTau = 8.0f;
 
+// The query projection folded into the attention launch (one-wave variant): raw queries
+// [BH, N, d] (bf16, d in {64, 128}), the projection P [H, d, m] (bf16, m <= MP) and the
+// factor the projected queries carry (scale * log2 e). Q == null: the projected queries
+// come from Qt instead.
+struct QueryFold {
+    const uint16_t* Q;
+    const uint16_t* P;
+    float scale;
+    int d, H, m;
+};
+
 template <int MP, int DV, bool CAUSAL, int QB>
 __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ Qt, const uint16_t* __restrict__ Kt, const bf16_t* __restrict__ Vt,
     const bf16_t* __restrict__ Vrow, const float* __restrict__ kmax, void* __restrict__ O,
-    float* __restrict__ lse, int N, int nqb, int out_f32) {
+    float* __restrict__ lse, int N, int nqb, int out_f32, QueryFold fq) {
     constexpr int kBR = kWaves * 32 * QB;    // queries per workgroup
     constexpr int WQ = 32 * QB;              // queries per wave
     constexpr int KS = MP / 16;              // score MFMA k-steps
@@ -94,7 +105,11 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     constexpr int NBUF = QB == 1 ? 2 : 7;
     constexpr int RING_V = 3 * K_BYTES;
     constexpr int TWO_BUF = QB == 1 ? 0 : 3 * BUF;
-    __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF];
+    // QB = 2 with the query projection folded in: P^T (32 rows, d <= 128 columns, rows
+    // padded by 16 bytes) after the buffers.
+    constexpr int PTP = 136;
+    constexpr int PT_BYTES = QB == 2 ? 32 * PTP * 2 : 0;
+    __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF + PT_BYTES];
 
     // Workgroup -> (head, query block). Workgroups are handed to the 8 XCDs round-robin;
     // when the grid divides evenly, XCD x gets a contiguous range of (head, block) pairs so
@@ -179,6 +194,60 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     auto kslot = [](int r) { return r * K_BYTES; };
     auto vslot = [](int r) { return RING_V + r * V_BYTES; };
 
+    // Query projection (QB = 2, raw queries given): this lane's query rows and the
+    // workgroup's share of P are requested before the tile copies, which they then overlap.
+    // P^T is staged in LDS with its 32 rows permuted by fold_row (an involution), so that
+    // the MFMA result lands in the layout of the score MFMA's B operand: lane half h holds
+    // rows 4h..4h+3 + 8j, i.e. features 8h..8h+7 (+16 for the second k-step).
+    const bool fold = QB == 2 && fq.Q != nullptr;
+    auto fold_row = [](int r) {
+        const int b4 = r >> 2;
+        return 4 * ((b4 & 4) | ((b4 & 1) << 1) | ((b4 >> 1) & 1)) + (r & 3);
+    };
+    constexpr int XK = QB == 2 ? 8 : 1;  // 16-k-steps over d <= 128
+    u32x4 xq[QB][XK];
+    u32x4 pvec[2];      // 16-byte vectors of P rows (m a multiple of 8): d*m/8 <= 2 per thread
+    uint16_t pel[16];   // otherwise single elements of P^T: 32*d <= 16 per thread
+    const int fks = fq.d >> 4;
+    const int pvr = fq.m >> 3;  // 16-byte vectors per row of P
+    const bool pvecs = (fq.m & 7) == 0;
+    const uint16_t* Pf = fq.P + (size_t)(fold ? bh % fq.H : 0) * fq.d * fq.m;
+    if constexpr (QB == 2) {
+        if (fold) {
+            if (pvecs) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int v = tid + kThreads * i;
+                    pvec[i] = u32x4{0u, 0u, 0u, 0u};
+                    if (v < fq.d * pvr) {
+                        const int k = v / pvr, c8 = (v - k * pvr) * 8;
+                        pvec[i] = *reinterpret_cast<const u32x4*>(Pf + (size_t)k * fq.m + c8);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int idx = tid + kThreads * i;
+                    pel[i] = 0;
+                    if (idx < 32 * fq.d) {
+                        const int r = idx / fq.d, k = idx - r * fq.d, c = fold_row(r);
+                        if (c < fq.m) pel[i] = Pf[(size_t)k * fq.m + c];
+                    }
+                }
+            }
+            const uint16_t* Qb = fq.Q + (size_t)bh * N * fq.d;
+#pragma unroll
+            for (int b = 0; b < QB; ++b)
+#pragma unroll
+                for (int ks = 0; ks < XK; ++ks) {
+                    xq[b][ks] = u32x4{0u, 0u, 0u, 0u};
+                    if (ks < fks && myq[b] < N)
+                        xq[b][ks] = *reinterpret_cast<const u32x4*>(
+                            Qb + (size_t)myq[b] * fq.d + ks * 16 + half * 8);
+                }
+        }
+    }
+
     // The first tiles' copies go out before anything else is loaded, so their latency
     // overlaps that of the query and key-norm loads below (the fast path starts from tile 0
     // in buffer 0 and, when pipelined, the keys of tile 1 in buffer 1).
@@ -215,15 +284,70 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
 
     // This lane's queries as the B operand of the score MFMA (zero past N).
     f16x8 qf[QB][KS];
+    if (fold) {
+        if constexpr (QB == 2) {
+            // P^T[r][k] = P[k][fold_row(r)] (zero past m) in LDS; then per query block the
+            // projection X~^T = P^T X^T on bf16 MFMA (k-steps in order, one RNE rounding of
+            // the scaled result to fp16), as the preparation launch computes it.
+            uint16_t* Pt = reinterpret_cast<uint16_t*>(lds + NBUF * BUF);
+            if (pvecs) {
 #pragma unroll
-    for (int b = 0; b < QB; ++b)
+                for (int i = 0; i < 2; ++i) {
+                    const int v = tid + kThreads * i;
+                    if (v >= fq.d * pvr) continue;
+                    const int k = v / pvr, c8 = (v - k * pvr) * 8;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (myq[b] < N)
-                v = *reinterpret_cast<const u32x4*>(Qh + (size_t)myq[b] * MP + ks * 16 + half * 8);
-            qf[b][ks] = __builtin_bit_cast(f16x8, v);
+                    for (int j = 0; j < 4; ++j) {
+                        Pt[fold_row(c8 + 2 * j) * PTP + k] = (uint16_t)(pvec[i][j] & 0xffffu);
+                        Pt[fold_row(c8 + 2 * j + 1) * PTP + k] = (uint16_t)(pvec[i][j] >> 16);
+                    }
+                }
+                for (int idx = tid; idx < (32 - fq.m) * fq.d; idx += kThreads) {
+                    const int c = fq.m + idx / fq.d, k = idx % fq.d;
+                    Pt[fold_row(c) * PTP + k] = 0;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int idx = tid + kThreads * i;
+                    if (idx < 32 * fq.d) {
+                        const int r = idx / fq.d, k = idx - r * fq.d;
+                        Pt[r * PTP + k] = pel[i];
+                    }
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                f32x16 a = f32x16_fill(0.0f);
+#pragma unroll
+                for (int ks = 0; ks < XK; ++ks) {
+                    if (ks >= fks) break;
+                    const u32x4 pa = *reinterpret_cast<const u32x4*>(Pt + col * PTP + ks * 16 + half * 8);
+                    a = mfma32x32x16(__builtin_bit_cast(bf16x8, pa),
+                                     __builtin_bit_cast(bf16x8, xq[b][ks]), a);
+                }
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    u32x4 v;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        v[j] = pack_f16x2(a[8 * ks + 2 * j] * fq.scale, a[8 * ks + 2 * j + 1] * fq.scale);
+                    qf[b][ks] = __builtin_bit_cast(f16x8, v);
+                }
+            }
         }
+    } else {
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (myq[b] < N)
+                    v = *reinterpret_cast<const u32x4*>(Qh + (size_t)myq[b] * MP + ks * 16 + half * 8);
+                qf[b][ks] = __builtin_bit_cast(f16x8, v);
+            }
+    }
 
     // Per-lane LDS read offsets, fixed across tiles.
     // Score operand: key row kb*32 + col, global chunk 2*ks + half.
@@ -965,36 +1089,36 @@ inline int pick_qb(int BH, int N, int mp, bool causal) {
 template <int MP, int DV, bool CAUSAL, int QB>
 hipError_t launch(const void* Qt, const void* Kt, const void* Vt, const void* Vrow,
                   const float* kmax, void* O, float* lse, int BH, int N, bool out_f32,
-                  hipStream_t stream) {
+                  const QueryFold& fq, hipStream_t stream) {
     constexpr int kBR = kWaves * 32 * QB;
     const int nqb = (N + kBR - 1) / kBR;
     attn_bf16_kernel<MP, DV, CAUSAL, QB><<<dim3(nqb * BH), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(Qt), static_cast<const uint16_t*>(Kt),
         static_cast<const bf16_t*>(Vt), static_cast<const bf16_t*>(Vrow), kmax, O, lse, N, nqb,
-        out_f32 ? 1 : 0);
+        out_f32 ? 1 : 0, fq);
     return hipGetLastError();
 }
 
 template <int MP, int DV>
 hipError_t launch_c(const void* Qt, const void* Kt, const void* Vt, const void* Vrow,
                     const float* kmax, void* O, float* lse, int BH, int N, bool causal,
-                    bool out_f32, int qb, hipStream_t stream) {
+                    bool out_f32, int qb, const QueryFold& fq, hipStream_t stream) {
     if constexpr (MP <= 32) {
         if (qb == 2)
-            return causal ? launch<MP, DV, true, 2>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, stream)
-                          : launch<MP, DV, false, 2>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, stream);
+            return causal ? launch<MP, DV, true, 2>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, fq, stream)
+                          : launch<MP, DV, false, 2>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, fq, stream);
     }
-    return causal ? launch<MP, DV, true, 1>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, stream)
-                  : launch<MP, DV, false, 1>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, stream);
+    return causal ? launch<MP, DV, true, 1>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, fq, stream)
+                  : launch<MP, DV, false, 1>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, out_f32, fq, stream);
 }
 
 template <int MP>
 hipError_t launch_dv(const void* Qt, const void* Kt, const void* Vt, const void* Vrow,
                      const float* kmax, void* O, float* lse, int BH, int N, int dv, bool causal,
-                     bool out_f32, int qb, hipStream_t stream) {
+                     bool out_f32, int qb, const QueryFold& fq, hipStream_t stream) {
     switch (dv) {
-        case 64: return launch_c<MP, 64>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, causal, out_f32, qb, stream);
-        case 128: return launch_c<MP, 128>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, causal, out_f32, qb, stream);
+        case 64: return launch_c<MP, 64>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, causal, out_f32, qb, fq, stream);
+        case 128: return launch_c<MP, 128>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, causal, out_f32, qb, fq, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1005,15 +1129,22 @@ bool attn_bf16_reads_v_rows(int BH, int N, int mp, int dv, bool causal) {
     return pick_qb(BH, N, mp, causal) == 2 && dv == 128;
 }
 
+bool attn_bf16_projects_queries(int BH, int N, int mp, int d, bool causal) {
+    return pick_qb(BH, N, mp, causal) == 2 && (d == 64 || d == 128);
+}
+
 hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* Vt, const void* Vrow,
                             const float* kmax, void* O, float* lse, int BH, int N, int mp,
-                            int dv, bool causal, bool out_f32, hipStream_t stream) {
+                            int dv, bool causal, bool out_f32, hipStream_t stream, const void* Q,
+                            const void* P, float qscale, int d, int H, int m) {
     const int qb = pick_qb(BH, N, mp, causal);
+    const QueryFold fq{static_cast<const uint16_t*>(qb == 2 ? Q : nullptr),
+                       static_cast<const uint16_t*>(P), qscale, d, H, m};
     switch (mp) {
-        case 16: return launch_dv<16>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
-        case 32: return launch_dv<32>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
-        case 64: return launch_dv<64>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
-        case 128: return launch_dv<128>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, stream);
+        case 16: return launch_dv<16>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, fq, stream);
+        case 32: return launch_dv<32>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, fq, stream);
+        case 64: return launch_dv<64>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, fq, stream);
+        case 128: return launch_dv<128>(Qt, Kt, Vt, Vrow, kmax, O, lse, BH, N, dv, causal, out_f32, qb, fq, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -29,6 +29,7 @@ __host__ __device__ inline int vt_padded_keys(int N) { return (N + kVtTileKeys -
 // not null, the same launch writes V^T of V ([BH, N, dv] bf16) in the layout above. If Yt0
 // (Yt1) is not null, Y0 (Y1) is also written transposed, [BH, out_cols, vt_padded_keys(N)],
 // tokens in the same permuted order as V^T and zero past N.
+// With X0 null and nz = 2 only the second tensor (X1 -> Y1, and kmax) is projected.
 hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, void* Y0,
                                void* Y1, int nz, int BH, int H, int N, int d, int m,
                                int out_stride, int out_cols, float out_scale0,
@@ -43,10 +44,16 @@ hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, vo
 // bf16, Vrow); the other pointer may be null. O is [BH, N, dv] in fp32 (out_f32) or bf16;
 // lse [BH, N] optional. kmax holds the per-block key norm maxima written by the projection
 // launch.
+// When attn_bf16_projects_queries(...) is true, the launch projects the queries itself from
+// Q ([BH, N, d] bf16) and P ([H, d, m] bf16), scaled by qscale, and Qt is not read; otherwise
+// (or with Q null) it reads the projected queries from Qt.
 bool attn_bf16_reads_v_rows(int BH, int N, int mp, int dv, bool causal);
+bool attn_bf16_projects_queries(int BH, int N, int mp, int d, bool causal);
 hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* Vt, const void* Vrow,
                             const float* kmax, void* O, float* lse, int BH, int N, int mp,
-                            int dv, bool causal, bool out_f32, hipStream_t stream);
+                            int dv, bool causal, bool out_f32, hipStream_t stream,
+                            const void* Q = nullptr, const void* P = nullptr,
+                            float qscale = 0.0f, int d = 0, int H = 1, int m = 0);
 
 // Backward of the bf16 path. The preparation launch (launch_project_bf16 with the queries
 // scaled by scale*log2(e), fp16 outputs, the transposed copies Qst and Ktt, and dO

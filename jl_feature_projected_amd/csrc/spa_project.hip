@@ -54,6 +54,7 @@ struct PrepArgs {
     uint16_t* Yt1;      // permuted within 16-groups as in Vt
     float* kmax;
     int N, BH, H, m, out_stride, out_cols, nz, nroles, Np;
+    int z0;  // first projection role (1: the first tensor is skipped)
     long long out_head_stride;  // elements between heads of Y0 / Y1
     float scale0, scale1;
 };
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kProjThreads) void prep_bf16_kernel(PrepArgs a) {
     __shared__ float wave_max[kProjThreads / 64];
 
     const int nblk = (a.N + kProjTokensPerBlock - 1) / kProjTokensPerBlock;
-    const int role = blockIdx.x % a.nroles;
+    const int role = a.z0 + blockIdx.x % a.nroles;
     const int rest = blockIdx.x / a.nroles;
     const int blk = rest % nblk;
     const int bh = rest / nblk;
@@ -327,7 +328,8 @@ hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, vo
     a.out_cols = out_cols;
     a.out_head_stride = out_head_stride < 0 ? (long long)N * out_stride : out_head_stride;
     a.nz = nz;
-    a.nroles = nz + (Vt ? 1 : 0);
+    a.z0 = (X0 == nullptr && nz == 2) ? 1 : 0;
+    a.nroles = nz - a.z0 + (Vt ? 1 : 0);
     a.Np = vt_padded_keys(N);
     a.scale0 = out_scale0;
     a.scale1 = out_scale1;

@@ -135,8 +135,23 @@ def test_small_shapes_full(dev, oracle_mod, N, d, m, dv, causal):
 WIDE = [
     # (B, H, N, d, m, dv)
     (4, 32, 1000, 128, 32, 128), (4, 32, 1000, 128, 16, 64), (2, 64, 777, 64, 5, 128),
-    (8, 16, 1025, 128, 24, 128), (1, 128, 1024, 128, 32, 64),
+    (8, 16, 1025, 128, 24, 128), (1, 128, 1024, 128, 32, 64), (4, 32, 1000, 128, 20, 128),
 ]
+# The same variant with the causal mask (its masked tiles run before the ring), including
+# the query projection's element-wise staging of P (m not a multiple of 8) at d = 64 and 128.
+WIDE_CAUSAL = [(4, 32, 1000, 64, 12, 64), (2, 32, 2000, 128, 20, 128), (2, 16, 4100, 128, 32, 128)]
+
+
+@pytest.mark.parametrize("B,H,N,d,m,dv", WIDE_CAUSAL)
+def test_wide_variant_causal(dev, oracle_mod, B, H, N, d, m, dv):
+    w = inputs.Workload(f"wide-causal-b{B}h{H}-n{N}-d{d}-m{m}-dv{dv}", B, H, N, d, m, dv, True,
+                        seed=4000 + N + m)
+    x = inputs.draw(w)
+    note(w.name)
+    O, lse = run(x, dev, return_lse=True)
+    Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, True, with_lse=True)
+    assert_bf16_close(np64(O), Or, what=w.name)
+    assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
 
 
 @pytest.mark.parametrize("B,H,N,d,m,dv", WIDE)
