@@ -310,10 +310,17 @@ def main() -> int:
     value = work.total_flops / (ms_per_step * 1e-3) / 1e12
     peak = accounting.PEAK_BF16_DENSE_TFLOPS if w.dtype == "bf16" else accounting.PEAK_FP32_VECTOR_TFLOPS
     attn_avg_ms = attn_ms / calls
-    achieved = work.attn_flops / (attn_avg_ms * 1e-3) / 1e12
+    plan = spa.spa_attn_fwd_plan(w.B, w.H, w.N, w.d, w.m, w.dv, spa.SPA_BF16 if w.dtype == "bf16"
+                                 else spa.SPA_F32, w.causal)
+    q_in_attn = plan > 0 and bool(plan & spa.SPA_PLAN_QUERIES_IN_ATTENTION)
+    # the attention launch's work: scores and weights x V, plus the query projection when it
+    # runs there
+    attn_work = work.attn_flops + (work.project_flops / 2 if q_in_attn else 0.0)
+    achieved = attn_work / (attn_avg_ms * 1e-3) / 1e12
     bytes_ = accounting.path_bytes(w.B, w.H, w.N, w.d, w.m, w.dv,
                                    elem=2 if w.dtype == "bf16" else 4,
-                                   out_elem=2 if w.dtype == "bf16" else 4)
+                                   out_elem=2 if w.dtype == "bf16" else 4,
+                                   queries_in_attention=q_in_attn)
     res = {
         "metric": METRIC,
         "value": round(value, 3),

@@ -90,9 +90,24 @@ spa_status_t spa_project(const void* X, const void* P, void* Xt, int B, int H, i
  * (bf16 path: fp16 at m rounded up to 16, 32, 64 or 128 columns; fp32 path: fp32 at m
  * columns) and, on the bf16 path only, one fp32 per (head, 256-key block) with that block's
  * largest projected key norm, and V transposed per head ([dv, N rounded up to 64] bf16).
+ * The projected-query and V^T regions go unused where spa_attn_fwd_plan reports the
+ * corresponding flag; the size does not depend on it.
  */
 size_t spa_attn_fwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
                                     spa_dtype_t dtype);
+
+/*
+ * How spa_attn_fwd runs these sizes on the bf16 path (a host-side query; no GPU work, no
+ * error recorded). Returns a set of flags, or -1 for arguments spa_attn_fwd would reject:
+ *   SPA_PLAN_QUERIES_IN_ATTENTION: the attention launch projects the queries itself (the
+ *     projection launch handles the keys only), so the projected queries never reach HBM;
+ *   SPA_PLAN_V_ROW_MAJOR: the attention launch reads V as given (no transposed copy).
+ * Neither changes the result beyond fp32 summation order; the fp32 path returns 0.
+ */
+#define SPA_PLAN_QUERIES_IN_ATTENTION 1
+#define SPA_PLAN_V_ROW_MAJOR 2
+int spa_attn_fwd_plan(int B, int H, int N, int d, int m, int dv, spa_dtype_t dtype,
+                      int causal);
 
 /*
  * spa_attn_fwd -- the projected attention forward:

@@ -29,7 +29,10 @@ EXPORTS = ("spa_version", "spa_status_string", "spa_last_error", "spa_project",
            "spa_attn_fwd_workspace_bytes", "spa_attn_fwd", "spa_attn_bwd_workspace_bytes",
            "spa_attn_bwd", "spa_sfa_fwd_workspace_bytes", "spa_sfa_fwd", "spa_kcache_append", "spa_attn_decode_workspace_bytes",
            "spa_attn_decode", "spa_profile_begin", "spa_profile_end", "spa_probe_rates",
-           "spa_attn_fwd_noalloc", "spa_attn_fwd_noalloc_max_workspace_bytes")
+           "spa_attn_fwd_noalloc", "spa_attn_fwd_noalloc_max_workspace_bytes",
+           "spa_attn_fwd_plan")
+SPA_PLAN_QUERIES_IN_ATTENTION = 1
+SPA_PLAN_V_ROW_MAJOR = 2
 
 
 class SpaError(RuntimeError):
@@ -65,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.spa_project.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
     L.spa_attn_fwd_workspace_bytes.restype = z
     L.spa_attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.spa_attn_fwd_plan.restype = i
+    L.spa_attn_fwd_plan.argtypes = [i, i, i, i, i, i, i, i]
     L.spa_attn_fwd.restype = st
     L.spa_attn_fwd.argtypes = [vp, vp, vp, vp, f, i, i, i, i, i, i, i, i, vp, i, vp, vp, z, vp]
     L.spa_attn_fwd_noalloc.restype = st
@@ -157,6 +162,12 @@ def spa_project(X, P):
 def spa_attn_fwd_workspace_bytes(B, H, N, d, m, dv, dtype) -> int:
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return int(lib().spa_attn_fwd_workspace_bytes(B, H, N, d, m, dv, code))
+
+
+def spa_attn_fwd_plan(B, H, N, d, m, dv, dtype, causal) -> int:
+    """SPA_PLAN_* flags of how spa_attn_fwd runs these sizes (-1: unsupported)."""
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return int(lib().spa_attn_fwd_plan(B, H, N, d, m, dv, code, 1 if causal else 0))
 
 
 def spa_attn_fwd(Q, K, V, P, scale: float | None = None, causal: bool = False,

@@ -14,7 +14,9 @@ with c = 1/2 under a causal mask (the N^2 terms are halved; the projection term 
 
 Bytes per head of the whole path: read Q, K, V and P once, write O once, and one round trip
 (write plus read) of the projected keys and queries that the projection launch hands to the
-attention launch. The exact-score work the method avoids is never counted.
+attention launch. Where the attention launch projects the queries itself, only the keys make
+that round trip, and the queries (and P) are read by the attention launch. The exact-score
+work the method avoids is never counted.
 """
 from __future__ import annotations
 
@@ -72,16 +74,20 @@ def bwd_work(B: int, H: int, N: int, d: int, m: int, dv: int, causal: bool) -> B
 
 
 def path_bytes(B: int, H: int, N: int, d: int, m: int, dv: int, elem: int = 2,
-               out_elem: int = 2) -> dict[str, float]:
+               out_elem: int = 2, queries_in_attention: bool = False) -> dict[str, float]:
     """Algorithmic HBM bytes of each launch and of the whole path (see module docstring)."""
     heads = B * H
-    qk = 2.0 * heads * N * d * elem
+    x = 1.0 * heads * N * d * elem  # Q or K
     v = 1.0 * heads * N * dv * elem
     o = 1.0 * heads * N * dv * out_elem
     p = 1.0 * H * d * m * elem
-    tilde = 2.0 * heads * N * m * elem  # projected queries and keys
-    project = qk + p + tilde  # read Q, K, P; write Qt, Kt
-    attn = tilde + v + o  # read Qt, Kt, V; write O
+    tilde = 1.0 * heads * N * m * elem  # projected queries or keys
+    if queries_in_attention:
+        project = x + p + tilde  # read K, P; write Kt
+        attn = x + p + tilde + v + o  # read Q, P, Kt, V; write O
+    else:
+        project = 2 * x + p + 2 * tilde  # read Q, K, P; write Qt, Kt
+        attn = 2 * tilde + v + o  # read Qt, Kt, V; write O
     return {"project": project, "attn": attn, "total": project + attn}
 
 

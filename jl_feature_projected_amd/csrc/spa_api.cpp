@@ -238,6 +238,27 @@ size_t spa_attn_fwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
     return out;
 }
 
+int spa_attn_fwd_plan(int B, int H, int N, int d, int m, int dv, spa_dtype_t dtype,
+                      int causal) {
+    char saved[sizeof(g_err)];
+    memcpy(saved, g_err, sizeof(g_err));
+    int out = -1;
+    if (check_dims("spa_attn_fwd_plan", B, H, N, d, m, dv) == SPA_OK &&
+        check_shape_support("spa_attn_fwd_plan", dtype, d, m, dv) == SPA_OK &&
+        (causal == 0 || causal == 1)) {
+        out = 0;
+        if (dtype == SPA_BF16) {
+            const int mp = spa::padded_m(m);
+            if (spa::attn_bf16_projects_queries(B * H, N, mp, d, causal == 1))
+                out |= SPA_PLAN_QUERIES_IN_ATTENTION;
+            if (spa::attn_bf16_reads_v_rows(B * H, N, mp, dv, causal == 1))
+                out |= SPA_PLAN_V_ROW_MAJOR;
+        }
+    }
+    memcpy(g_err, saved, sizeof(g_err));
+    return out;
+}
+
 }  // extern "C"
 
 namespace {

@@ -137,6 +137,11 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
 
     const int kend = CAUSAL ? min(N, q0 + kBR) : N;
     const int ntiles = (kend + kBC - 1) / kBC;
+    // The key-norm maxima of the key blocks this workgroup reads (the first 64 requested
+    // before anything else, so their latency overlaps the tile copies').
+    const int nkb = proj_blocks(N);
+    const int kblocks = (kend + kProjBlockTokens - 1) / kProjBlockTokens;
+    float kmx = lane < kblocks ? kmax[(size_t)bh * nkb + lane] : 0.0f;
 
     // ---- HBM -> LDS tile copy ---------------------------------------------------------
     // Copy j (64 lanes x 16 bytes) fills LDS chunks 64j .. 64j+63 of the tile; lane l writes
@@ -381,11 +386,8 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     }
 
     // ---- score bound: M = |q| * max |k| over the key blocks this workgroup reads -------
-    float kmx = 0.0f;
     {
-        const int nkb = proj_blocks(N);
-        const int kblocks = (kend + kProjBlockTokens - 1) / kProjBlockTokens;
-        for (int b = lane; b < kblocks; b += 64) kmx = fmaxf(kmx, kmax[(size_t)bh * nkb + b]);
+        for (int b = lane + 64; b < kblocks; b += 64) kmx = fmaxf(kmx, kmax[(size_t)bh * nkb + b]);
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) kmx = fmaxf(kmx, __shfl_xor(kmx, o, 64));
     }

@@ -111,6 +111,24 @@ def test_workspace_bytes(L):
     assert L.spa_attn_fwd_workspace_bytes(0, 1, 512, 64, 16, 64, spa.SPA_BF16) == 0
 
 
+def test_attn_fwd_plan(L):
+    B = spa.SPA_BF16
+    both = spa.SPA_PLAN_QUERIES_IN_ATTENTION | spa.SPA_PLAN_V_ROW_MAJOR
+    # one-wave variant (m <= 32, >= 512 workgroups of 256 queries): projects the queries
+    # itself; reads V as given when dv = 128
+    assert L.spa_attn_fwd_plan(2, 16, 8192, 128, 32, 128, B, 1) == both
+    assert L.spa_attn_fwd_plan(1, 128, 1024, 128, 32, 64, B, 0) == spa.SPA_PLAN_QUERIES_IN_ATTENTION
+    assert L.spa_attn_fwd_plan(2, 64, 777, 64, 5, 128, B, 0) == both
+    # two-wave variant: too few workgroups, or m > 32
+    assert L.spa_attn_fwd_plan(4, 12, 2048, 64, 16, 64, B, 1) == 0
+    assert L.spa_attn_fwd_plan(2, 16, 8192, 128, 64, 128, B, 1) == 0
+    assert L.spa_attn_fwd_plan(2, 16, 8192, 128, 32, 128, spa.SPA_F32, 1) == 0
+    # rejected arguments
+    assert L.spa_attn_fwd_plan(2, 16, 8192, 96, 32, 128, B, 1) == -1
+    assert L.spa_attn_fwd_plan(2, 16, 8192, 128, 32, 128, B, 2) == -1
+    assert L.spa_attn_fwd_plan(0, 16, 8192, 128, 32, 128, B, 1) == -1
+
+
 def test_profile_api_state(L):
     assert L.spa_profile_begin(0) == spa.SPA_ERR_INVALID_ARGUMENT
     d, e, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()

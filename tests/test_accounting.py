@@ -60,3 +60,9 @@ def test_path_bytes():
     assert b["project"] == 2 * heads * 8192 * 128 * 2 + 16 * 128 * 32 * 2 + 2 * heads * 8192 * 32 * 2
     assert b["attn"] == 2 * heads * 8192 * 32 * 2 + 2 * heads * 8192 * 128 * 2
     assert math.isclose(b["total"], b["project"] + b["attn"])
+    # queries projected inside the attention launch: only the keys make the round trip
+    f = accounting.path_bytes(2, 16, 8192, 128, 32, 128, queries_in_attention=True)
+    x, p, t = heads * 8192 * 128 * 2, 16 * 128 * 32 * 2, heads * 8192 * 32 * 2
+    assert f["project"] == x + p + t
+    assert f["attn"] == x + p + t + 2 * heads * 8192 * 128 * 2
+    assert math.isclose(b["total"] - f["total"], 2 * t - p)
