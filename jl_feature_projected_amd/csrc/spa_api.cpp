@@ -367,12 +367,8 @@ spa_status_t attn_fwd_impl(const char* fn, const void* Q, const void* K, const v
         } else {
             e = spa::launch_project_f32(static_cast<const float*>(Q),
                                         static_cast<const float*>(P), static_cast<float*>(Qt),
-                                        B * H, H, N, d, m, 1.0f, s);
-            if (e == hipSuccess)
-                e = spa::launch_project_f32(static_cast<const float*>(K),
-                                            static_cast<const float*>(P),
-                                            static_cast<float*>(Kt), B * H, H, N, d, m, 1.0f,
-                                            s);
+                                        B * H, H, N, d, m, 1.0f, s,
+                                        static_cast<const float*>(K), static_cast<float*>(Kt));
             if (e == hipSuccess && ev[1]) e = hipEventRecord(ev[1], s);
             if (e == hipSuccess)
                 e = spa::launch_attn_f32(static_cast<const float*>(Qt),

@@ -259,8 +259,7 @@ hipError_t launch_core(const BwdF32Args& a, hipStream_t s) {
 hipError_t launch_attn_bwd_f32(const BwdF32Args& a, hipStream_t s) {
     if (a.m < 1 || a.m > 128 || a.dv < 1 || a.dv > kMaxDv || a.d < 1) return hipErrorInvalidValue;
     const int BH = a.B * a.H;
-    hipError_t e = launch_project_f32(a.Q, a.P, a.Qt, BH, a.H, a.N, a.d, a.m, 1.0f, s);
-    if (e == hipSuccess) e = launch_project_f32(a.K, a.P, a.Kt, BH, a.H, a.N, a.d, a.m, 1.0f, s);
+    hipError_t e = launch_project_f32(a.Q, a.P, a.Qt, BH, a.H, a.N, a.d, a.m, 1.0f, s, a.K, a.Kt);
     if (e != hipSuccess) return e;
     if (a.m <= 16) e = launch_core<16>(a, s);
     else if (a.m <= 32) e = launch_core<32>(a, s);

@@ -88,9 +88,11 @@ struct BwdArgs {
 };
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
-// fp32 projection: Y[bh, n, c] = out_scale * sum_k X[bh, n, k] P[h, k, c], fp32 FMAs.
+// fp32 projection: Y[bh, n, c] = out_scale * sum_k X[bh, n, k] P[h, k, c], fp32 FMAs; with
+// X1 non-null the same launch also writes Y1 from X1.
 hipError_t launch_project_f32(const float* X, const float* P, float* Y, int BH, int H, int N,
-                              int d, int m, float out_scale, hipStream_t stream);
+                              int d, int m, float out_scale, hipStream_t stream,
+                              const float* X1 = nullptr, float* Y1 = nullptr);
 
 // fp32 attention over projected inputs (natural-exponent online softmax, fp32 FMAs).
 hipError_t launch_attn_f32(const float* Qt, const float* Kt, const float* V, float* O,

@@ -219,14 +219,18 @@ def test_structured_projections_full(dev, oracle_mod, kw, causal):
     assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
 
 
-@pytest.mark.parametrize("N,m,dv,causal", [(200, 16, 64, True), (333, 40, 128, False)])
+@pytest.mark.parametrize("N,m,dv,causal", [(200, 16, 64, True), (333, 40, 128, False),
+                                           (130, 128, 40, True), (70, 64, 128, True),
+                                           (1, 7, 3, False), (17, 33, 17, True)])
 def test_fp32_path_other_shapes(dev, oracle_mod, N, m, dv, causal):
-    w = inputs.Workload(f"f32-n{N}-m{m}", 1, 2, N, 96, m, dv, causal, dtype="f32", seed=7)
+    w = inputs.Workload(f"f32-n{N}-m{m}-dv{dv}", 1, 2, N, 96, m, dv, causal, dtype="f32",
+                        seed=7)
     x = inputs.draw(w)
     note(w.name)
-    O = run(x, dev)
-    Or = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, causal)
+    O, lse = run(x, dev, return_lse=True)
+    Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, causal, with_lse=True)
     assert np.max(np.abs(np64(O) - Or)) / np.max(np.abs(Or)) <= TOL_F32_REL
+    assert np.max(np.abs(np64(lse) - lr)) <= TOL_F32_REL * max(1.0, np.max(np.abs(lr)))
 
 
 # ---- full-size workloads: stratified row samples ----------------------------------------
