@@ -86,6 +86,27 @@ def test_backward_small_shapes(dev, oracle_mod, shape):
         compare(f"{shape} {name}", a, b)
 
 
+# Wider grids (128 heads, 512 or more blocks of 256 keys, as the longer workloads launch) at
+# ragged N, both masks, m not a multiple of 16, d = 64 and 128, dv = 64 and 128, every head
+# against the oracle.
+WIDE = [  # B, H, N, d, m, dv, causal
+    (4, 32, 1000, 64, 24, 64, True),
+    (2, 64, 777, 128, 5, 128, False),
+    (1, 128, 1025, 128, 32, 128, True),
+    (4, 32, 1024, 128, 16, 64, False),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE, ids=lambda s: "-".join(map(str, s)))
+def test_backward_wide_grids(dev, oracle_mod, shape):
+    B, H, N, d, m, dv, causal = shape
+    w = inputs.Workload(f"bwd-wide-{N}", B, H, N, d, m, dv, causal, seed=1900 + N + m)
+    x, V, dO, got = run_bwd(w, dev, seed=41 + N)
+    ref = oracle.attn_bwd(x.Q, x.K, V, x.P, dO, w.scale, causal)
+    for name, a, b in zip(("dQ", "dK", "dV", "dP"), got, ref):
+        compare(f"{shape} {name}", a, b)
+
+
 def test_backward_headline_recipe_reduced_length(dev, oracle_mod):
     """The N = 8192 workload's recipe (low-rank-plus-noise Q and K, d = dv = 128, m = 32,
     causal) on two heads at N = 2048, where the double-precision oracle takes seconds."""
