@@ -558,9 +558,15 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     };
     // The step with the next tile's score operands (ka) and this tile's first PF V operands
     // (va) already in registers.
-    auto step_core = [&](const u32x4 (&ka)[2][KS], u32x4 (&va)[NPV], const char* Vs,
+    // With next_tag true (the ring), the step also reads the next step's operands (key tile
+    // Kn, V tile Vn) into ka and va -- the key operands once its own second score block has
+    // consumed them, the first V operands in its last PV slots -- so that their LDS latency
+    // is hidden behind its MFMAs.
+    auto step_core = [&](u32x4 (&ka)[2][KS], u32x4 (&va)[NPV], const char* Vs,
                          const u32x4 (&p)[QB][2][2], u32x4 (&pn)[QB][2][2], auto masked,
-                         const int (&rel)[QB]) {
+                         const int (&rel)[QB], auto next_tag, const char* Kn,
+                         const char* Vn) {
+        constexpr bool NEXT = decltype(next_tag)::value;
         constexpr int NM = NPV * QB;     // PV MFMAs per tile
         constexpr int WSTART = QB == 1 ? 3 : 2;  // first PV MFMA that weight work follows
         constexpr int NU = 16 * QB;      // weight pairs per tile
@@ -613,6 +619,10 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
             const int v = i / QB, b = i % QB;
             if (SPLIT && i == NM / 2) score_mfmas(1);
             if (b == 0 && v + PF < NPV) vload(Vs, va, v + PF);
+            if constexpr (SPLIT && NEXT) {
+                if (i == NM / 2 + 1) load_ka(Kn, ka);
+                if (b == 0 && v >= NPV - PF) vload(Vn, va, v - (NPV - PF));
+            }
             const int db = pv_db(v), kb = pv_kb(v), tt = pv_tt(v);
             acc[b][db] = mfma32x32x16(__builtin_bit_cast(bf16x8, va[v]),
                                       __builtin_bit_cast(bf16x8, p[b][kb][tt]), acc[b][db]);
@@ -696,7 +706,7 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
         u32x4 ka[2][KS], va[NPV];
         load_ka(Kn, ka);
         load_va_prefix(Vs, va);
-        step_core(ka, va, Vs, p, pn, masked, rel);
+        step_core(ka, va, Vs, p, pn, masked, rel, std::false_type{}, nullptr, nullptr);
     };
     auto init_state = [&](const float (&mu0)[QB]) {
 #pragma unroll
@@ -933,10 +943,10 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
                 const int S1 = S == 2 ? 0 : S + 1, S2 = S == 0 ? 2 : S - 1;
                 if (t + 3 < nf) copy_k_to((t + 3) * kBC, kslot(S));
                 if (t + 2 < nf) copy_v_to((t + 2) * kBC, vslot(S2));
-                step_core(ka, va, lds + vslot(S), p, pn, std::false_type{}, rel0);
-                // (Past the last tile these read a slot no copy refills: unused values.)
-                load_ka(lds + kslot(S2), ka);
-                load_va_prefix(lds + vslot(S1), va);
+                // (Past the last tile the next operands come from a slot no copy refills:
+                // unused values.)
+                step_core(ka, va, lds + vslot(S), p, pn, std::false_type{}, rel0,
+                          std::true_type{}, lds + kslot(S2), lds + vslot(S1));
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
             };
