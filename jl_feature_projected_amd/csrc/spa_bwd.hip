@@ -553,10 +553,16 @@ __global__ __launch_bounds__(kThreads, MP >= 128 ? 1 : 2) void proj_grad_kernel(
     constexpr int XT_B = MB * 32 * TP;         // one bf16 plane of dQt^T or dKt^T
     constexpr int ZW = KB == 4 ? 1 : 2;        // waves per feature block (D = 64: one per term)
     static_assert(KB * ZW == kWaves, "one feature block (and term) per wave");
-    __shared__ __attribute__((aligned(16))) char lds[2 * QT_B + 4 * XT_B];
+    // MP <= 32: dQt and dKt rows also kept row-major in LDS (fp32, rows padded by 16 bytes),
+    // the B operands of dQ and dK; wider rows read them from global memory instead.
+    constexpr bool XROW = MP <= 32;
+    constexpr int XRP = MP + 4;                // row pitch (floats)
+    constexpr int XR_B = XROW ? kPgSub * XRP * 4 : 0;
+    __shared__ __attribute__((aligned(16))) char lds[2 * QT_B + 4 * XT_B + 2 * XR_B];
     // Q^T (z = 0) and K^T (z = 1); then the hi (p = 0) and lo planes of dQt^T and dKt^T
     auto QTs = [&](int z) { return lds + z * QT_B; };
     auto XTs = [&](int z, int p) { return lds + 2 * QT_B + (2 * z + p) * XT_B; };
+    auto XRs = [&](int z) { return reinterpret_cast<float*>(lds + 2 * QT_B + 4 * XT_B + z * XR_B); };
 
     const int bh = blockIdx.x / nch;
     const int ch = blockIdx.x - bh * nch;
@@ -591,11 +597,13 @@ __global__ __launch_bounds__(kThreads, MP >= 128 ? 1 : 2) void proj_grad_kernel(
 #pragma unroll
     for (int b = 0; b < MB; ++b) accp[b] = f32x16_fill(0.0f);
 
-#pragma unroll 1
-    for (int rs = r0; rs < r0 + kPgRows && rs < N; rs += kPgSub) {
-        __syncthreads();  // the previous pass's tiles are read
-        // Q^T and K^T: thread = (row, 16-byte chunk column), 8 two-byte transposed writes.
-        const int row = tid % kPgSub;
+    // This thread's share of a pass's rows, loaded a pass ahead: Q and K rows (thread =
+    // (row, 16-byte chunk column)) and dQt and dKt rows (thread = (row, 4-column chunk)).
+    constexpr int XC = (MP / 4 + kWaves - 1) / kWaves;  // 4-column chunks per thread and term
+    const int row = tid % kPgSub;
+    u32x4 qv[2][D / 32];
+    float4 xv[2][XC];
+    auto load_pass = [&](int rs) {
         const bool rok = rs + row < N;
 #pragma unroll
         for (int z = 0; z < 2; ++z) {
@@ -603,24 +611,45 @@ __global__ __launch_bounds__(kThreads, MP >= 128 ? 1 : 2) void proj_grad_kernel(
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) {
                 const int cc = tid / kPgSub + kWaves * i;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (rok) v = *reinterpret_cast<const u32x4*>(X + cc * 8);
+                qv[z][i] = u32x4{0u, 0u, 0u, 0u};
+                if (rok) qv[z][i] = *reinterpret_cast<const u32x4*>(X + cc * 8);
+            }
+            const float* Xt = (z ? dKt : dQt) + ((size_t)bh * N + rs + row) * MP;
+#pragma unroll
+            for (int i = 0; i < XC; ++i) {
+                const int cc = tid / kPgSub + kWaves * i;
+                xv[z][i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (rok && cc < MP / 4) xv[z][i] = *reinterpret_cast<const float4*>(Xt + cc * 4);
+            }
+        }
+    };
+    load_pass(r0);
+
+#pragma unroll 1
+    for (int rs = r0; rs < r0 + kPgRows && rs < N; rs += kPgSub) {
+        __syncthreads();  // the previous pass's tiles are read
+        // Q^T and K^T: 8 two-byte transposed writes per 16-byte chunk.
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) {
+                const int cc = tid / kPgSub + kWaves * i;
+                const u32x4 v = qv[z][i];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
                     *reinterpret_cast<uint16_t*>(QTs(z) + (cc * 8 + e) * TP + row * 2) =
                         (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
             }
         }
-        // dQt^T and dKt^T, hi and lo planes: thread = (row, 4-column chunk).
+        // dQt^T and dKt^T, hi and lo planes (and the row-major copy).
 #pragma unroll
         for (int z = 0; z < 2; ++z) {
-            const float* X = (z ? dKt : dQt) + ((size_t)bh * N + rs + row) * MP;
 #pragma unroll
-            for (int i = 0; i < (MP / 4 + kWaves - 1) / kWaves; ++i) {
+            for (int i = 0; i < XC; ++i) {
                 const int cc = tid / kPgSub + kWaves * i;
                 if (cc < MP / 4) {
-                    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-                    if (rok) v = *reinterpret_cast<const float4*>(X + cc * 4);
+                    const float4 v = xv[z][i];
+                    if constexpr (XROW) *reinterpret_cast<float4*>(XRs(z) + row * XRP + cc * 4) = v;
                     const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -633,6 +662,9 @@ __global__ __launch_bounds__(kThreads, MP >= 128 ? 1 : 2) void proj_grad_kernel(
             }
         }
         __syncthreads();
+        // The next pass's rows are requested now, to arrive during this pass's products.
+        const bool more = rs + kPgSub < r0 + kPgRows && rs + kPgSub < N;
+        if (XROW && more) load_pass(rs + kPgSub);
 
         // dQ, dK: output block (term z, 32-row block rb, feature block kb):
         // D[k][row] = sum_c P[k][c] Xt[row][c], B operand = lane row's 8 columns, hi and lo.
@@ -647,7 +679,12 @@ __global__ __launch_bounds__(kThreads, MP >= 128 ? 1 : 2) void proj_grad_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f), b = a;
-                if (ook) {
+                if constexpr (XROW) {
+                    // rows past N were staged as zeros
+                    const float* xr = XRs(z) + (rb * 32 + col) * XRP + ks * 16 + half * 8;
+                    a = *reinterpret_cast<const float4*>(xr);
+                    b = *reinterpret_cast<const float4*>(xr + 4);
+                } else if (ook) {
                     a = *reinterpret_cast<const float4*>(X + ks * 16 + half * 8);
                     b = *reinterpret_cast<const float4*>(X + ks * 16 + half * 8 + 4);
                 }
@@ -680,6 +717,10 @@ __global__ __launch_bounds__(kThreads, MP >= 128 ? 1 : 2) void proj_grad_kernel(
                 }
             }
         }
+
+        // (Wider rows: their B operands above came from global memory, so the next pass's
+        // loads go out only now, behind them.)
+        if (!XROW && more) load_pass(rs + kPgSub);
 
         // Partial: D[k][c] += sum_rows X^T[k][row] Xt[row][c] over this wave's term(s).
 #pragma unroll
