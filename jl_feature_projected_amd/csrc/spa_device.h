@@ -33,13 +33,17 @@ __device__ __forceinline__ f32x16 mfma32x32x16(f16x8 a, f16x8 b, f32x16 c) {
 // The same fp16 MFMA with its result and accumulator in VGPRs. In a kernel that may use
 // more than 256 registers the compiler gives every MFMA the AGPR form, and a VALU use of the
 // result then needs one v_accvgpr_read per element; this form avoids that for results the
-// VALU consumes. The compiler does not track the MFMA -> VALU latency of inline assembly, so
-// the caller keeps at least three MFMAs between this and the first VALU read of the result.
-// A chain of these on one accumulator needs no wait (exact overlap of result and srcC).
+// VALU consumes. The compiler inserts no wait states around inline assembly, so each
+// statement carries those it inserts around its own 8-pass MFMAs: two between a VALU write of
+// a source and the MFMA (s_nop 1 in front) and, where the accumulator input is a register of
+// its own, eight between the issue and a later write of that input (s_nop 7 behind). Next to
+// another MFMA these nops overlap the matrix pipe's issue wait. The caller keeps at least three
+// MFMAs between this and the first VALU read of the result; a chain on one accumulator needs
+// no wait (exact overlap of result and srcC).
 __device__ __forceinline__ f32x16 mfma32x32x16_v(f16x8 a, f16x8 b, f32x16 c) {
     f32x16 d;
 #if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %3\n\ts_nop 7" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
 #else
     d = c;
 #endif
@@ -47,7 +51,7 @@ __device__ __forceinline__ f32x16 mfma32x32x16_v(f16x8 a, f16x8 b, f32x16 c) {
 }
 __device__ __forceinline__ void mfma32x32x16_v_acc(f16x8 a, f16x8 b, f32x16& c) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 #endif
 }
 
