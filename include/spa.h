@@ -208,10 +208,12 @@ size_t spa_attn_bwd_workspace_bytes(int B, int H, int N, int d, int m, int dv,
  * SPA_F32 with d <= 256, dv <= 128, m <= 128 (SPA_ERR_UNSUPPORTED otherwise). bf16: the
  * projected queries and keys are prepared exactly as in the forward (fp16), so the
  * recomputed scores match the forward's bit for bit; the weights meet dO in bf16 and dS
- * meets the projected operands in fp16, all on MFMA with fp32 accumulation; five launches.
- * fp32: every product and sum in fp32 on the VALU (the projections, a query-major and a
- * key-major pass, the gradients mapped back through P, and dP); seven launches. Both run
- * on `stream` and are deterministic (no atomics).
+ * meets the projected operands in fp16, all on MFMA with fp32 accumulation; four launches
+ * (five at m > 64). At m <= 64 the projected-query gradient is accumulated with fp32 atomic
+ * adds, in an order that varies between runs: dQ and dP then agree run to run to rounding,
+ * dK and dV bit for bit. fp32: every product and sum in fp32 on the VALU (the projections,
+ * a query-major and a key-major pass, the gradients mapped back through P, and dP); seven
+ * launches, deterministic. Both run on `stream`.
  */
 spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const void* P,
                           const void* O, const void* dO, const float* lse, float scale,

@@ -806,10 +806,22 @@ spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const voi
         return SPA_OK;
     }
     const int mp = spa::padded_m(m);
-    const float qscale = scale * 1.44269504088896340736f;
+    const float log2e = 1.44269504088896340736f;
+    const float qscale = scale * log2e;
+    const bool fused = spa::bwd_fuses_dq(mp, dv);
+    spa::PrepRowTerms rt;
+    if (fused) {
+        rt.O = O;
+        rt.lse = lse;
+        rt.LD = reinterpret_cast<float*>(w + wl.ld);
+        rt.dQt = reinterpret_cast<float*>(w + wl.dqt);
+        rt.dqt_cols = mp;
+        rt.lse_scale = log2e;
+    }
     hipError_t e = spa::launch_project_bf16(Q, K, P, w + wl.qs, w + wl.kt, 2, B * H, H, N, d, m,
                                             mp, mp, qscale, 1.0f, /*out_f16=*/true, nullptr, dO,
-                                            w + wl.dot, dv, s, w + wl.qst, w + wl.ktt);
+                                            w + wl.dot, dv, s, w + wl.qst, w + wl.ktt, -1,
+                                            fused ? &rt : nullptr);
     if (e == hipSuccess) {
         spa::BwdArgs a;
         a.Q = static_cast<const uint16_t*>(Q);
@@ -833,6 +845,7 @@ spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const voi
         a.dK = dK;
         a.dV = dV;
         a.g_f32 = g_dtype == SPA_F32 ? 1 : 0;
+        a.fused_dq = fused ? 1 : 0;
         a.BH = B * H;
         a.H = H;
         a.N = N;

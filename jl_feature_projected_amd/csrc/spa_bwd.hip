@@ -11,15 +11,17 @@
 // are prepared exactly as in the forward (fp16, queries pre-scaled by scale*log2(e)), so the
 // recomputed base-2 scores are the forward's, bit for bit.
 //
-// Kernels (all on 32x32x16 MFMA; see the forward for the operand layouts):
-//   bwd_q_kernel   query-major: per 32-query wave, a loop over 32-key tiles computes
-//                  dQt^T = Kt^T . dS^T, after D_i from the wave's own dO and O rows.
+// Kernels (on 32x32x16 MFMA unless noted; see the forward for the operand layouts):
 //   bwd_kv_kernel  key-major: per 32-key wave, a loop over 32-query tiles computes
-//                  dV^T = dO^T . A and dKt^T = Qt^T . dS. Needs D from bwd_q_kernel.
+//                  dV^T = dO^T . A and dKt^T = Qt^T . dS; with DQ (mp <= 64) also
+//                  dQt += dS Kt over the workgroup's 128 keys (dS through LDS, 16x16x32
+//                  MFMAs, fp32 atomic adds), with D_i and lse from the preparation launch.
+//   bwd_q_kernel   query-major (mp = 128 only): per 32-query wave, a loop over 32-key tiles
+//                  computes dQt^T = Kt^T . dS^T, after D_i from the wave's own dO and O
+//                  rows, which the key-major kernel then reads.
 //   proj_grad_kernel   dQ = dQt P^T, dK = dKt P^T and the projection gradient's partial
 //                  per 256-row chunk (bf16 MFMAs, fp32 factors split hi + lo).
-//   dp_reduce_kernel   the partials summed over chunks and batches in a fixed order
-//                  (deterministic).
+//   dp_reduce_kernel   the partials summed over chunks and batches in a fixed order.
 // In the transposed (A-operand) tiles the rows are V^T-ordered: within every 16 tokens the
 // order 0-3, 8-11, 4-7, 12-15, which is the order in which a score accumulator lane holds
 // its 8 tokens of a 16-token k-step. So every MFMA operand is one 16-byte LDS read or a
@@ -51,6 +53,17 @@ struct Flag {
 
 // Byte offset that is out of range for every tile resource below (loads read zero).
 constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Key-major kernel with the projected-query gradient: one dS tile in LDS, 128 key rows of 32
+// f16 queries (64 bytes). Within every 16 queries the row holds them in the order 0-3, 8-11,
+// 4-7, 12-15, the order in which a score accumulator lane holds them, so a lane's 8 values of
+// a k-step are one 16-byte chunk; chunk c of row r sits at c ^ ds_swz(r). A half-wave's 16-byte
+// store then covers every bank twice (the minimum for 512 bytes), and the 4 rows of a 16-lane
+// transposing read lie in 4 distinct quarters of the banks.
+constexpr int kDsBytes = 128 * 64;
+__device__ __forceinline__ int ds_swz(int row) { return (row >> 2) & 3; }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 // fp32 score-layout values (slots 8*half + j of k-step tt) -> packed pairs
 template <bool F16>
@@ -292,13 +305,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_q_kernel(
 // [BH,N,MP] fp16, V [BH,N,DV] bf16, dO [BH,N,DV] bf16, dOt [BH,DV,Np] bf16 (transposed,
 // permuted), LD (from the query-major kernel).
 // Outputs: dV [BH,N,DV] (fp32 or bf16), dKt [BH,N,MP] fp32 (scale applied).
-template <int MP, int DV, bool CAUSAL>
+template <int MP, int DV, bool CAUSAL, bool DQ>
 __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd_kv_kernel(
     const uint16_t* __restrict__ Qs, const uint16_t* __restrict__ Qst,
     const uint16_t* __restrict__ Kt, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const uint16_t* __restrict__ dOt,
     const float* __restrict__ LD, void* __restrict__ dV, int dv_f32, float* __restrict__ dKt,
-    int N, int Np, int nkb) {
+    float* __restrict__ dQt, float scale, int N, int Np, int nkb) {
     constexpr int KS = MP / 16;
     constexpr int MB = (MP + 31) / 32;
     constexpr int CS = DV / 16;
@@ -316,7 +329,9 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
     constexpr int CPW = (NCP + kWaves - 1) / kWaves;
     static_assert(Q_B % 1024 == 0 && QT_B % 1024 == 0 && DO_B % 1024 == 0 && DOT_B % 1024 == 0,
                   "copy regions");
-    __shared__ __attribute__((aligned(16))) char lds[kBufs * BUF];
+    // DQ: two dS tiles (one being written, the previous one being read), kDsBytes each
+    __shared__ __attribute__((aligned(16))) char lds[kBufs * BUF + (DQ ? 2 * kDsBytes : 0)];
+    char* dsl = lds + kBufs * BUF;
 
     // Workgroup -> (head, key block), XCD-contiguous as in the query-major kernel; causal
     // key blocks are heaviest first already (block 0 meets every query).
@@ -398,6 +413,30 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
         if (kvalid) v = *reinterpret_cast<const u32x4*>(V + ((size_t)bh * N + myk) * DV + cs * 16 + half * 8);
         vf[cs] = __builtin_bit_cast(bf16x8, v);
     }
+    // DQ: this wave's share of dQt (32 queries x MP) per tile: 16x16 output
+    // blocks u (query half u & 1, features 16 (u >> 1) ..), each a sum over the workgroup's
+    // 128 keys in four 32-key k-steps; the wave takes the (block, k-step) pairs
+    // dq_block(p), dq_kstep(p). Their B operands (Kt of 8 keys for one feature) stay in
+    // registers.
+    constexpr int NT = DQ ? 2 * (MP / 16) : 0;           // 16x16 output blocks per tile
+    constexpr int NPAIR = DQ ? NT : 1;                    // (block, k-step) pairs per wave
+    const int g16 = lane >> 4, j16 = lane & 15;
+    auto dq_block = [&](int p) { return NT >= 4 ? wave + 4 * (p >> 2) : (wave & 1); };
+    auto dq_kstep = [&](int p) { return NT >= 4 ? (p & 3) : 2 * (wave >> 1) + p; };
+    f16x8 kq[NPAIR];
+    if constexpr (DQ) {
+#pragma unroll
+        for (int p = 0; p < NPAIR; ++p) {
+            const int f = 16 * (dq_block(p) >> 1) + j16;
+            const int key0 = k0 + 32 * dq_kstep(p) + 8 * g16;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int key = key0 + e;
+                kq[p][e] = key < N ? __builtin_bit_cast(_Float16, Kt[((size_t)bh * N + key) * MP + f])
+                                   : (_Float16)0.0f;
+            }
+        }
+    }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     copy_tile(qstart + kTile, 1);
 
@@ -417,10 +456,69 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 #pragma unroll
     for (int b = 0; b < MB; ++b) dka[b] = f32x16_fill(0.0f);
 
-    // Three buffers, one barrier per step, as in the query-major kernel.
+    // DQ: the tile's dS (f16) in the layout above. The lane's packed dS of k-step tt (queries
+    // 16tt + 4half .. +3 and 16tt + 8 + 4half .. +3 of its key) is chunk 2tt + half of its
+    // key's row. A wave with nothing to do in a tile stores zeros, as do keys past N.
+    const int dsrow = wave * 32 + col;
+    auto ds_store = [&](int buf, int tt, u32x4 w) {
+        *reinterpret_cast<u32x4*>(dsl + buf * kDsBytes + dsrow * 64 +
+                                  16 * ((2 * tt + half) ^ ds_swz(dsrow))) = w;
+    };
+    // dQt += scale * dS Kt for the tile in dS buffer buf (queries from qd0): the A operand of
+    // block u, k-step ks is two transposing reads; lane (g, 4e + a) of the 16x16x32 layout
+    // addresses key row 32ks + 8g + 4s + e, queries 16 (u & 1) + 4a .. +3 (s = 0, 1 for the
+    // operand's first and last four keys), which the row holds at chunk 2 (u & 1) + (a & 1),
+    // bytes 8 (a >> 1) .. +7. The results go to dQt by fp32 atomic adds through a buffer
+    // resource of the head's N rows, which drops the adds of queries past N.
+    const __amdgpu_buffer_rsrc_t dqr =
+        __builtin_amdgcn_make_buffer_rsrc(dQt + (size_t)bh * N * MP, (short)0, N * MP * 4, 0x00020000);
+    auto dq_phase = [&](int buf, int qd0) {
+        const char* base = dsl + buf * kDsBytes;
+        f32x4 acc[NT >= 4 ? NT / 4 : 1];
+#pragma unroll
+        for (int b = 0; b < (NT >= 4 ? NT / 4 : 1); ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int p = 0; p < NPAIR; ++p) {
+            const int u = dq_block(p), ks = dq_kstep(p);
+            const int e = j16 >> 2, a = j16 & 3;
+            u32x2 h[2];
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh) {
+                const int row = 32 * ks + 8 * g16 + 4 * sh + e;
+                const int c = 2 * (u & 1) + (a & 1);
+                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(base + row * 64 + 16 * (c ^ ds_swz(row)) + 8 * (a >> 1)));
+                h[sh] = __builtin_bit_cast(u32x2, r);
+            }
+            const f16x8 af = __builtin_bit_cast(f16x8, u32x4{h[0].x, h[0].y, h[1].x, h[1].y});
+            f32x4& c = acc[NT >= 4 ? p >> 2 : 0];
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, kq[p], c, 0, 0, 0);
+        }
+#pragma unroll
+        for (int b = 0; b < (NT >= 4 ? NT / 4 : 1); ++b) {
+            const int u = dq_block(NT >= 4 ? 4 * b : 0);
+            const int f = 16 * (u >> 1) + j16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = qd0 + 16 * (u & 1) + 4 * g16 + i;
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[b][i] * scale, dqr,
+                                                                 (q * MP + f) * 4, 0, 0);
+            }
+        }
+    };
+
+    // Three buffers, one barrier per step, as in the query-major kernel. DQ: step t first
+    // takes tile t-1's dS (stored before the last barrier) into dQt, before the step's tile
+    // copies: the atomic adds count in the same in-order vector-memory counter, so issued
+    // after the copies they would make the step's closing wait also wait for those copies.
     auto step = [&](int t, int cur, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int q0 = qstart + t * kTile;
+        if constexpr (DQ) {
+            if (t > 0) dq_phase((t - 1) & 1, q0 - kTile);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         copy_tile(q0 + 2 * kTile, cur == 0 ? kBufs - 1 : cur - 1);
         const char* Qts = lds + cur * BUF;      // Qs tile (rows = queries)
         const char* QTs = Qts + Q_B;            // Qs^T tile (rows = features)
@@ -428,7 +526,13 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
         const char* dOTs = dOs + DO_B;          // dO^T tile (rows = V columns)
         const float* Ls = reinterpret_cast<const float*>(Qts + B16);  // -lse2 [32], -D [32]
         // causal: nothing to do if every query of the tile precedes every key of the wave
-        if (!MASK || q0 + kTile - 1 >= k0w) {
+        const bool active = !MASK || q0 + kTile - 1 >= k0w;
+        if constexpr (DQ) {
+            if (!active)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) ds_store(t & 1, tt, u32x4{0u, 0u, 0u, 0u});
+        }
+        if (active) {
             // accumulators start at -lse2 and -D of the slot's query (8*(i/4) + 4*half + i%4)
             f32x16 s, da;
 #pragma unroll
@@ -461,7 +565,9 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const bf16x8 bw = __builtin_bit_cast(bf16x8, pack_kstep<false>(w, tt));
-                const f16x8 bs = __builtin_bit_cast(f16x8, pack_kstep<true>(ds, tt));
+                const u32x4 bsu = pack_kstep<true>(ds, tt);
+                const f16x8 bs = __builtin_bit_cast(f16x8, bsu);
+                if constexpr (DQ) ds_store(t & 1, tt, kvalid ? bsu : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const bf16x8 a = __builtin_bit_cast(
@@ -486,6 +592,9 @@ __global__ __launch_bounds__(kThreads, (MP >= 64 && DV >= 128) ? 1 : 2) void bwd
     for (; t < nmask; ++t, cur = cur == kBufs - 1 ? 0 : cur + 1) step(t, cur, Flag<true>{});
 #pragma unroll 1
     for (; t < ntiles; ++t, cur = cur == kBufs - 1 ? 0 : cur + 1) step(t, cur, Flag<false>{});
+    if constexpr (DQ) {
+        if (ntiles > 0) dq_phase((ntiles - 1) & 1, qstart + (ntiles - 1) * kTile);
+    }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy may land after the workgroup ends
 
     if (kvalid) {
@@ -805,12 +914,24 @@ __global__ __launch_bounds__(kThreads) void dp_reduce_kernel(const float* __rest
 template <int MP, int DV, bool CAUSAL>
 hipError_t launch_main(const BwdArgs& a, hipStream_t s) {
     const int nqb = (a.N + 127) / 128;
+    if (a.fused_dq) {
+        // LD and the zeroed dQt come from the preparation launch
+        if constexpr (MP <= 64) {
+            bwd_kv_kernel<MP, DV, CAUSAL, true><<<dim3(a.BH * nqb), kThreads, 0, s>>>(
+                a.Qs, a.Qst, a.Kt, a.V, a.dO, a.dOt, a.LD, a.dV, a.g_f32, a.dKt, a.dQt, a.scale,
+                a.N, a.Np, nqb);
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     bwd_q_kernel<MP, DV, CAUSAL><<<dim3(a.BH * nqb), kThreads, 0, s>>>(
         a.Qs, a.Kt, a.Ktt, a.V, a.O, a.dO, a.lse, a.dQt, a.LD, a.N, a.Np, nqb, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    bwd_kv_kernel<MP, DV, CAUSAL><<<dim3(a.BH * nqb), kThreads, 0, s>>>(
-        a.Qs, a.Qst, a.Kt, a.V, a.dO, a.dOt, a.LD, a.dV, a.g_f32, a.dKt, a.N, a.Np, nqb);
+    bwd_kv_kernel<MP, DV, CAUSAL, false><<<dim3(a.BH * nqb), kThreads, 0, s>>>(
+        a.Qs, a.Qst, a.Kt, a.V, a.dO, a.dOt, a.LD, a.dV, a.g_f32, a.dKt, nullptr, a.scale, a.N,
+        a.Np, nqb);
     return hipGetLastError();
 }
 
@@ -829,6 +950,8 @@ hipError_t launch_dv(const BwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+bool bwd_fuses_dq(int mp, int dv) { return mp <= 64 && (dv == 64 || dv == 128); }
 
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
     if ((long long)a.BH * ((a.N + 127) / 128) > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -30,12 +30,24 @@ __host__ __device__ inline int vt_padded_keys(int N) { return (N + kVtTileKeys -
 // (Yt1) is not null, Y0 (Y1) is also written transposed, [BH, out_cols, vt_padded_keys(N)],
 // tokens in the same permuted order as V^T and zero past N.
 // With X0 null and nz = 2 only the second tensor (X1 -> Y1, and kmax) is projected.
+// Backward row terms written by the dO-transpose role (V = dO): per query -lse*lse_scale and
+// -D, D = <dO, O> (O bf16 [BH, N, dv]), into LD [BH, Np/32, 2, 32] (-inf and 0 for the
+// padding queries), and zeros over dQt [BH, N, dqt_cols] (dqt_cols a multiple of 4).
+struct PrepRowTerms {
+    const void* O = nullptr;
+    const float* lse = nullptr;
+    float* LD = nullptr;
+    float* dQt = nullptr;
+    int dqt_cols = 0;
+    float lse_scale = 0.0f;
+};
 hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, void* Y0,
                                void* Y1, int nz, int BH, int H, int N, int d, int m,
                                int out_stride, int out_cols, float out_scale0,
                                float out_scale1, bool out_f16, float* kmax, const void* V,
                                void* Vt, int dv, hipStream_t stream, void* Yt0 = nullptr,
-                               void* Yt1 = nullptr, long long out_head_stride = -1);
+                               void* Yt1 = nullptr, long long out_head_stride = -1,
+                               const PrepRowTerms* row_terms = nullptr);
 
 // Attention over projected inputs. Qt and Kt are fp16 [BH, N, mp] with zero columns past m
 // (score MFMA in fp16); Qt is pre-scaled by scale*log2(e) so the scores come out in base-2
@@ -57,10 +69,11 @@ hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* Vt, cons
 
 // Backward of the bf16 path. The preparation launch (launch_project_bf16 with the queries
 // scaled by scale*log2(e), fp16 outputs, the transposed copies Qst and Ktt, and dO
-// transposed into dOt) runs first; this runs the rest: the query-major kernel (dQt and
-// D = rowsum(dO * O)), the key-major kernel (dV and dKt), dQ = dQt P^T and dK = dKt P^T, and
-// the projection gradient dP (fp32 partials per 256-row chunk in dPpart, then a fixed-order
-// sum). mp is 16, 32 or 64.
+// transposed into dOt; with fused_dq also the row terms LD and the cleared dQt) runs first;
+// this runs the rest: the query-major kernel (dQt and D = rowsum(dO * O); not with
+// fused_dq), the key-major kernel (dV and dKt, with fused_dq also dQt), dQ = dQt P^T and
+// dK = dKt P^T, and the projection gradient dP (fp32 partials per 256-row chunk in dPpart,
+// then a fixed-order sum). mp is 16, 32, 64 or 128.
 struct BwdArgs {
     const uint16_t* Q;    // bf16 [BH, N, d]
     const uint16_t* K;    // bf16 [BH, N, d]
@@ -83,10 +96,15 @@ struct BwdArgs {
     void* dK;
     void* dV;             // [BH, N, dv]
     int g_f32;
+    int fused_dq;  // 1: the key-major kernel also accumulates dQt (bwd_fuses_dq)
     int BH, H, N, Np, d, m, mp, dv, causal;
     float scale;
 };
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+// True when the key-major kernel accumulates dQt itself (fp32 atomic adds into dQt, which
+// the preparation launch clears, with LD from that launch too) and the query-major kernel is
+// not run.
+bool bwd_fuses_dq(int mp, int dv);
 
 // fp32 projection: Y[bh, n, c] = out_scale * sum_k X[bh, n, k] P[h, k, c], fp32 FMAs; with
 // X1 non-null the same launch also writes Y1 from X1.

@@ -30,6 +30,9 @@
 //
 // For the backward pass the same launch can also write the projections transposed, with
 // the tokens of every 16-group in the V^T order (Yt0, Yt1), and transpose dO in place of V.
+// The dO role can then also write, per query, -lse*log2(e) and -D with D = <dO, O> (the row
+// term of the softmax gradient), reading O's rows beside dO's, and clear the rows of the
+// projected-query gradient that the key-major backward kernel accumulates into.
 #include "spa_device.h"
 #include "spa_internal.h"
 
@@ -53,6 +56,7 @@ struct PrepArgs {
     uint16_t* Yt0;      // optional transposed projections [BH, out_cols, Np], tokens
     uint16_t* Yt1;      // permuted within 16-groups as in Vt
     float* kmax;
+    PrepRowTerms rt;    // backward row terms (rt.LD null: none)
     int N, BH, H, m, out_stride, out_cols, nz, nroles, Np;
     int z0;  // first projection role (1: the first tensor is skipped)
     long long out_head_stride;  // elements between heads of Y0 / Y1
@@ -82,19 +86,55 @@ __device__ void transpose_v(const PrepArgs& a, int bh, int t0, uint16_t* s) {
     const uint16_t* Vh = a.V + (size_t)bh * a.N * DV;
     uint16_t* Vth = a.Vt + (size_t)bh * DV * a.Np;
     const int kend = min(t0 + kProjTokensPerBlock, a.Np);
-    u32x4 v[LPT];
+    const PrepRowTerms& rt = a.rt;
+    const bool terms = rt.LD != nullptr;
+    const uint16_t* Oh = terms ? static_cast<const uint16_t*>(rt.O) + (size_t)bh * a.N * DV : nullptr;
+    u32x4 v[LPT], o[LPT];
     auto load = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
             const int c = threadIdx.x + i * kProjThreads;
             const int r = c / CH, ch = c - r * CH;
             v[i] = u32x4{0u, 0u, 0u, 0u};
-            if (k0 + r < a.N) v[i] = *reinterpret_cast<const u32x4*>(Vh + (size_t)(k0 + r) * DV + ch * 8);
+            o[i] = u32x4{0u, 0u, 0u, 0u};
+            if (k0 + r < a.N) {
+                v[i] = *reinterpret_cast<const u32x4*>(Vh + (size_t)(k0 + r) * DV + ch * 8);
+                if (terms) o[i] = *reinterpret_cast<const u32x4*>(Oh + (size_t)(k0 + r) * DV + ch * 8);
+            }
         }
     };
     load(t0);
 #pragma unroll 1
     for (int k0 = t0; k0 < kend; k0 += kVtTileKeys) {
+        if (terms) {
+            // D of each row: its CH chunks are held by CH adjacent lanes of one wave
+#pragma unroll
+            for (int i = 0; i < LPT; ++i) {
+                const int c = threadIdx.x + i * kProjThreads;
+                const int r = c / CH, ch = c - r * CH;
+                const bf16x8 x = __builtin_bit_cast(bf16x8, v[i]);
+                const bf16x8 y = __builtin_bit_cast(bf16x8, o[i]);
+                float dot = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot += (float)x[e] * (float)y[e];
+#pragma unroll
+                for (int off = 1; off < CH; off <<= 1) dot += __shfl_xor(dot, off, 64);
+                const int row = k0 + r;
+                if (ch == 0 && row < a.Np) {
+                    float* dst = rt.LD + ((size_t)bh * a.Np + (row & ~31)) * 2 + (row & 31);
+                    dst[0] = row < a.N ? -rt.lse[(size_t)bh * a.N + row] * rt.lse_scale : -INFINITY;
+                    dst[32] = -dot;
+                }
+            }
+            // the projected-query gradient rows of this tile start at zero
+            const int cq = rt.dqt_cols / 4;
+            for (int c = threadIdx.x; c < kVtTileKeys * cq; c += kProjThreads) {
+                const int row = k0 + c / cq;
+                if (row < a.N)
+                    *reinterpret_cast<float4*>(rt.dQt + ((size_t)bh * a.N + row) * rt.dqt_cols + 4 * (c % cq)) =
+                        make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
             const int c = threadIdx.x + i * kProjThreads;
@@ -308,8 +348,9 @@ hipError_t launch_project_bf16(const void* X0, const void* X1, const void* P, vo
                                int out_stride, int out_cols, float out_scale0,
                                float out_scale1, bool out_f16, float* kmax, const void* V,
                                void* Vt, int dv, hipStream_t stream, void* Yt0, void* Yt1,
-                               long long out_head_stride) {
+                               long long out_head_stride, const PrepRowTerms* row_terms) {
     PrepArgs a;
+    a.rt = row_terms ? *row_terms : PrepRowTerms{};
     a.Yt0 = static_cast<uint16_t*>(Yt0);
     a.Yt1 = static_cast<uint16_t*>(Yt1);
     a.X0 = static_cast<const bf16_t*>(X0);
