@@ -274,7 +274,9 @@ def spa_attn_bwd(Q, K, V, P, O, dO, lse, scale: float | None = None, causal: boo
     forward's output and lse its log-sum-exp (fp32 [B,H,N], spa_attn_fwd(...,
     return_lse=True)); O and dO in the inputs' dtype. grad_dtype: torch.float32 or
     torch.bfloat16 for dQ, dK, dV (default float32; float32 only on the fp32 path); dP is
-    fp32 [H,d,m]. Runs on the current stream.
+    fp32 [H,d,m]. Runs on the current stream. On the bf16 path at m <= 64 the projected-query
+    gradient is summed with fp32 atomic adds, so dQ and dP agree between runs to rounding and
+    dK, dV bit for bit; the fp32 path is bit-for-bit deterministic.
     """
     torch = _torch()
     for name, x in (("Q", Q), ("K", K), ("V", V), ("P", P), ("O", O), ("dO", dO), ("lse", lse)):
