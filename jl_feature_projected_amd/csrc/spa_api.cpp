@@ -818,9 +818,11 @@ spa_status_t spa_attn_bwd(const void* Q, const void* K, const void* V, const voi
         rt.dqt_cols = mp;
         rt.lse_scale = log2e;
     }
+    // K~^T is read only by the query-major kernel, which the fused form does not run.
     hipError_t e = spa::launch_project_bf16(Q, K, P, w + wl.qs, w + wl.kt, 2, B * H, H, N, d, m,
                                             mp, mp, qscale, 1.0f, /*out_f16=*/true, nullptr, dO,
-                                            w + wl.dot, dv, s, w + wl.qst, w + wl.ktt, -1,
+                                            w + wl.dot, dv, s, w + wl.qst,
+                                            fused ? nullptr : w + wl.ktt, -1,
                                             fused ? &rt : nullptr);
     if (e == hipSuccess) {
         spa::BwdArgs a;

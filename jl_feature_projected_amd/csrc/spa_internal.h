@@ -68,12 +68,12 @@ hipError_t launch_attn_bf16(const void* Qt, const void* Kt, const void* Vt, cons
                             float qscale = 0.0f, int d = 0, int H = 1, int m = 0);
 
 // Backward of the bf16 path. The preparation launch (launch_project_bf16 with the queries
-// scaled by scale*log2(e), fp16 outputs, the transposed copies Qst and Ktt, and dO
-// transposed into dOt; with fused_dq also the row terms LD and the cleared dQt) runs first;
-// this runs the rest: the query-major kernel (dQt and D = rowsum(dO * O); not with
-// fused_dq), the key-major kernel (dV and dKt, with fused_dq also dQt), dQ = dQt P^T and
-// dK = dKt P^T, and the projection gradient dP (fp32 partials per 256-row chunk in dPpart,
-// then a fixed-order sum). mp is 16, 32, 64 or 128.
+// scaled by scale*log2(e), fp16 outputs, the transposed copies Qst and (not with fused_dq)
+// Ktt, and dO transposed into dOt; with fused_dq also the row terms LD and the cleared dQt)
+// runs first; this runs the rest: the query-major kernel (dQt and D = rowsum(dO * O); not
+// with fused_dq), the key-major kernel (dV and dKt, with fused_dq also dQt), dQ = dQt P^T
+// and dK = dKt P^T, and the projection gradient dP (fp32 partials per 256-row chunk in
+// dPpart, then a fixed-order sum). mp is 16, 32, 64 or 128.
 struct BwdArgs {
     const uint16_t* Q;    // bf16 [BH, N, d]
     const uint16_t* K;    // bf16 [BH, N, d]
@@ -81,7 +81,7 @@ struct BwdArgs {
     const uint16_t* Qs;   // fp16 [BH, N, mp], queries projected and scaled by scale*log2(e)
     const uint16_t* Kt;   // fp16 [BH, N, mp]
     const uint16_t* Qst;  // fp16 [BH, mp, Np], Qs transposed, tokens permuted as in V^T
-    const uint16_t* Ktt;  // fp16 [BH, mp, Np]
+    const uint16_t* Ktt;  // fp16 [BH, mp, Np] (read only by the query-major kernel)
     const uint16_t* V;    // bf16 [BH, N, dv]
     const uint16_t* O;    // bf16 [BH, N, dv] (the forward's output)
     const uint16_t* dO;   // bf16 [BH, N, dv]

@@ -20,6 +20,10 @@ are:
 
 A label or branch inside one of these windows counts as a violation: the check does not
 follow control flow.
+
+The same assembly (plus the backward's) also carries the kernels' resource metadata: the
+kernels whose speed rests on their register and LDS budgets must compile with no VGPR spills
+and within the LDS that their residency assumes.
 """
 import glob
 import os
@@ -230,17 +234,57 @@ v_exp_f32_e32 v40, v16
     assert check(chain) == []
 
 
-def test_inline_asm_mfmas_keep_their_wait_states(tmp_path):
+@pytest.fixture(scope="module")
+def device_asm(tmp_path_factory):
+    """gfx950 assembly of the sources with inline MFMAs and of the backward, by file name."""
     if not os.path.exists(B.hipcc()):
         pytest.skip("hipcc is not installed")
+    out_dir = tmp_path_factory.mktemp("asm")
+    srcs = sorted(set(_sources_with_asm_mfmas()) | {os.path.join(B.CSRC, "spa_bwd.hip")})
+    texts = {}
+    for src in srcs:
+        out = str(out_dir / (os.path.basename(src) + ".s"))
+        subprocess.run([B.hipcc(), *B.compile_flags(), "--cuda-device-only", "-S", src, "-o", out],
+                       check=True, capture_output=True, text=True)
+        texts[os.path.basename(src)] = open(out).read()
+    return texts
+
+
+def test_inline_asm_mfmas_keep_their_wait_states(device_asm):
     srcs = _sources_with_asm_mfmas()
     assert srcs, "no device source issues an inline-assembly MFMA"
     problems = []
     for src in srcs:
-        out = str(tmp_path / (os.path.basename(src) + ".s"))
-        subprocess.run([B.hipcc(), *B.compile_flags(), "--cuda-device-only", "-S", src, "-o", out],
-                       check=True, capture_output=True, text=True)
-        text = open(out).read()
+        text = device_asm[os.path.basename(src)]
         assert re.search(r";;#ASMSTART\s*\n\s*(s_nop \d+\s*\n\s*)?v_mfma", text), src
         problems += [f"{os.path.basename(src)}: {p}" for p in check(text)]
     assert not problems, "\n".join(problems[:40])
+
+
+def _kernel_resources(text: str) -> dict:
+    """Per kernel symbol: vgpr_count, vgpr_spill_count, group_segment_fixed_size (LDS)."""
+    out = {}
+    for blk in text.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", blk).group(1)
+        field = lambda f: int(re.search(rf"\.{f}:\s+(\d+)", blk).group(1))
+        out[name] = {"vgpr": field("vgpr_count"), "vgpr_spill": field("vgpr_spill_count"),
+                     "lds": field("group_segment_fixed_size")}
+    return out
+
+
+# The kernels whose speed rests on their register and LDS budgets: the one-wave attention
+# variant (every register of the SIMD, no spill code in or around its ring) and the fused
+# key-major backward kernel (two workgroups per CU: at most 256 registers, half the LDS).
+HOT = [
+    ("spa_attn_bf16.hip", r"attn_bf16_kernelILi(16|32)ELi128ELb[01]ELi2E", 163840),
+    ("spa_bwd.hip", r"bwd_kv_kernelILi(16|32)ELi128ELb[01]ELb1E", 81920),
+]
+
+
+@pytest.mark.parametrize("src,pattern,lds_max", HOT, ids=["attention-one-wave", "bwd-key-major-fused"])
+def test_hot_kernels_keep_their_budgets(device_asm, src, pattern, lds_max):
+    res = {k: v for k, v in _kernel_resources(device_asm[src]).items() if re.search(pattern, k)}
+    assert len(res) == 4, sorted(res)
+    for name, r in res.items():
+        assert r["vgpr_spill"] == 0, (name, r)
+        assert r["lds"] <= lds_max, (name, r)
