@@ -321,11 +321,12 @@ spa_status_t spa_profile_end(double* project_ms, double* attn_ms, int* calls);
 
 /*
  * Rate probes for the benchmark's roofline context (not part of the attention path): the
- * sustained rate of the bf16 matrix core (32x32x16 MFMAs, one wave per SIMD, every CU) and
- * of fp32 VALU FMAs (four waves per SIMD), in TFLOP/s, each with the mean engine clock in
- * GHz while it ran (shader-clock counter against the 100 MHz counter). Runs synchronously
- * on `stream` (about 10 ms) and allocates a few KB of device memory for the duration of
- * the call. Every output pointer must be non-NULL (else SPA_ERR_INVALID_ARGUMENT);
+ * sustained rate of the bf16 matrix core (32x32x16 MFMAs on random operands, one wave per
+ * SIMD, every CU) and of fp32 VALU FMAs (four waves per SIMD), in TFLOP/s, each over 100
+ * back-to-back launches (the rate of the second half), with the mean engine clock in GHz
+ * during the last launch (shader-clock counter against the 100 MHz counter). Runs
+ * synchronously on `stream` (about 80 ms) and allocates a few KB of device memory for the
+ * duration of the call. Every output pointer must be non-NULL (else SPA_ERR_INVALID_ARGUMENT);
  * SPA_ERR_HIP if a HIP call fails.
  */
 spa_status_t spa_probe_rates(double* mfma_tflops, double* mfma_ghz, double* fma_tflops,

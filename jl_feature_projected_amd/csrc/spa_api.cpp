@@ -874,8 +874,8 @@ spa_status_t spa_probe_rates(double* mfma_tflops, double* mfma_ghz, double* fma_
     if (!mfma_tflops || !mfma_ghz || !fma_tflops || !fma_ghz)
         return fail(SPA_ERR_INVALID_ARGUMENT, "spa_probe_rates: null output pointer");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = spa::run_probe(0, 3, s, mfma_tflops, mfma_ghz);
-    if (e == hipSuccess) e = spa::run_probe(1, 3, s, fma_tflops, fma_ghz);
+    hipError_t e = spa::run_probe(0, 100, s, mfma_tflops, mfma_ghz);
+    if (e == hipSuccess) e = spa::run_probe(1, 100, s, fma_tflops, fma_ghz);
     if (e != hipSuccess) return hip_fail("spa_probe_rates", e);
     return SPA_OK;
 }

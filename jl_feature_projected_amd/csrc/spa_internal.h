@@ -155,8 +155,9 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_sfa_topk(const void* Q, const void* K, void* Qt, void* Kt, float* kmax,
                            int BH, int N, int d, int k, float qscale, hipStream_t stream);
 
-// Rate probes (spa_probe.hip): kind 0 the bf16 32x32x16 MFMA rate, kind 1 the fp32 VALU
-// FMA rate, in TFLOP/s, with the mean engine clock in GHz while it ran.
-hipError_t run_probe(int kind, int reps, hipStream_t stream, double* tflops, double* ghz);
+// Rate probes (spa_probe.hip): kind 0 the bf16 32x32x16 MFMA rate on random operands, kind 1
+// the fp32 VALU FMA rate, in TFLOP/s, sustained over `launches` back-to-back launches, with
+// the mean engine clock in GHz during the last one.
+hipError_t run_probe(int kind, int launches, hipStream_t stream, double* tflops, double* ghz);
 
 }  // namespace spa
