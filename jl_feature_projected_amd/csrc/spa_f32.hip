@@ -35,128 +35,166 @@ __global__ __launch_bounds__(256) void project_f32_kernel(const float* __restric
     Y[((size_t)bh * N + n) * m + c] = acc * out_scale;
 }
 
-constexpr int kQ = 16;      // queries per workgroup
-constexpr int kKeys = 64;   // keys per LDS tile
-constexpr int kParts = 16;  // threads per query
-constexpr int kKP = kKeys / kParts;  // keys of a tile scored by each thread
+constexpr int kQW = 4;      // queries per workgroup (one per wave)
+constexpr int kKeys = 64;   // keys per tile (one per lane)
 constexpr int kMaxDv = 128;
-constexpr int kOC = kMaxDv / kParts;  // output columns owned by each thread
 
-// One workgroup: 16 queries of one head, 16 threads per query. Per 64-key tile, thread
-// (q, part) scores keys part*4 .. part*4+3 of the tile for its query (MM-float projected row
-// in registers, zero past m); the tile maximum of each query is combined through LDS; the
-// thread exponentiates its 4 scores against the new running maximum and publishes the
-// weights in LDS; then it accumulates output columns part*8 .. part*8+7 over all 64 keys
-// (LDS reads of the key and value rows are 16-byte vectors, the same address across the
-// lanes of a query group). The normaliser is kept per thread over its own keys and summed
-// at the end.
-template <int MM>
+// Maximum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// One workgroup: 4 queries of one head, one wave per query. Per 64-key tile (staged in LDS,
+// the next tile's loads in flight in registers while this one is computed), lane k scores
+// key k0 + k for the wave's query (MM-float projected row in registers, zero past m); the
+// tile maximum is a wave reduction; the lane exponentiates its score against the new running
+// maximum (exact online softmax) and the wave accumulates output columns lane and lane + 64
+// (DVC of them) over the tile's 64 keys, each weight broadcast from its lane, the V columns
+// read four keys at a time from a transposed LDS copy. The normaliser is kept per lane over
+// its own keys and summed at the end.
+template <int MM, int DVC>
 __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__ Qt,
                                                        const float* __restrict__ Kt,
                                                        const float* __restrict__ V,
                                                        float* __restrict__ O,
                                                        float* __restrict__ lse, int N, int m,
                                                        int dv, int causal, float scale) {
-    __shared__ __attribute__((aligned(16))) float Ks[kKeys * MM];
-    __shared__ __attribute__((aligned(16))) float Vs[kKeys * kMaxDv];
-    __shared__ float Ps[kKeys * kQ];
-    __shared__ float red[kParts * kQ];
+    constexpr int KS = MM + 1;               // LDS row stride of the key tile (floats)
+    constexpr int VS = kKeys + 4;            // LDS row stride of the transposed value tile
+    constexpr int KPT = kKeys * MM / 256;    // key-tile floats per thread (at most)
+    constexpr int VPT = kKeys * 64 * DVC / 256;  // value-tile floats per thread (at most)
+    // (one spare float after each tile takes the loads that fall past it)
+    __shared__ __attribute__((aligned(16))) float Ks[kKeys * KS + 4];
+    __shared__ __attribute__((aligned(16))) float Vs[64 * DVC * VS + 4];
 
-    const int nqb = (N + kQ - 1) / kQ;
+    const int nqb = (N + kQW - 1) / kQW;
     const int bh = blockIdx.x / nqb;
-    const int q0 = (blockIdx.x % nqb) * kQ;
-    const int tid = threadIdx.x;
-    const int qi = tid % kQ, part = tid / kQ;
-    const int q = q0 + qi;
-    const int c0 = part * kOC;  // first owned output column
+    const int q0 = (blockIdx.x % nqb) * kQW;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int q = q0 + wave;
     const float* Qh = Qt + (size_t)bh * N * m;
     const float* Kh = Kt + (size_t)bh * N * m;
     const float* Vh = V + (size_t)bh * N * dv;
 
+    // Columns m .. MM-1 of the key tile stay zero (the query row is zero there too).
+    for (int e = tid; e < kKeys * KS; e += 256) Ks[e] = 0.0f;
     float qr[MM];
 #pragma unroll
-    for (int c = 0; c < MM; ++c) qr[c] = (q < N && c < m) ? Qh[(size_t)q * m + c] : 0.0f;
-    float o[kOC];
-#pragma unroll
-    for (int i = 0; i < kOC; ++i) o[i] = 0.0f;
-    float mx = -INFINITY, lpart = 0.0f;
+    for (int c = 0; c < MM; ++c) qr[c] = (q < N && c < m) ? Qh[(size_t)q * m + c] * scale : 0.0f;
 
-    const int kend = causal ? min(N, q0 + kQ) : N;
-    for (int k0 = 0; k0 < kend; k0 += kKeys) {
-        __syncthreads();
-        for (int e = tid; e < kKeys * MM; e += 256) {
-            const int j = e / MM, c = e % MM;
-            Ks[e] = (k0 + j < N && c < m) ? Kh[(size_t)(k0 + j) * m + c] : 0.0f;
-        }
-        for (int e = tid; e < kKeys * kMaxDv; e += 256) {
-            const int j = e / kMaxDv, c = e % kMaxDv;
-            Vs[e] = (k0 + j < N && c < dv) ? Vh[(size_t)(k0 + j) * dv + c] : 0.0f;
-        }
-        __syncthreads();
-        float s[kKP];
-        float pmax = -INFINITY;
+    // The tile [k0, k0 + 64) of K~ (64 m floats) and of V (64 dv floats) is contiguous in
+    // memory; thread tid loads elements tid, tid + 256, ... of each into registers.
+    const int kend = causal ? min(N, q0 + kQW) : N;
+    const int ntiles = (kend + kKeys - 1) / kKeys;
+    // Buffer resources over the head's rows: loads past its end read as zero, with no branch.
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, N * m * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, N * dv * 4, 0x00020000);
+    // Two register sets of tile loads: the loads of tile t + 2 go out while tile t is
+    // computed, and tile t + 1 is staged from the other set after it.
+    struct TileRegs {
+        float k[KPT], v[VPT];
+    };
+    TileRegs ra, rb;
+    auto load = [&](TileRegs& r, int t) __attribute__((always_inline)) {
+        const int kb = t * kKeys * m * 4, vb = t * kKeys * dv * 4;  // byte offsets of the tile
 #pragma unroll
-        for (int jj = 0; jj < kKP; ++jj) {
-            const int j = part * kKP + jj, key = k0 + j;
-            float acc = 0.0f;
+        for (int i = 0; i < KPT; ++i)
+            r.k[i] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(krs, 4 * (tid + 256 * i), kb, 0));
 #pragma unroll
-            for (int c = 0; c < MM; c += 4) {
-                const float4 k4 = *reinterpret_cast<const float4*>(&Ks[j * MM + c]);
-                acc = fmaf(qr[c], k4.x, acc);
-                acc = fmaf(qr[c + 1], k4.y, acc);
-                acc = fmaf(qr[c + 2], k4.z, acc);
-                acc = fmaf(qr[c + 3], k4.w, acc);
-            }
-            s[jj] = (key >= N || (causal && key > q)) ? -INFINITY : acc * scale;
-            pmax = fmaxf(pmax, s[jj]);
-        }
-        red[part * kQ + qi] = pmax;
-        __syncthreads();
-        float tmax = -INFINITY;
+        for (int i = 0; i < VPT; ++i)
+            r.v[i] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(vrs, 4 * (tid + 256 * i), vb, 0));
+    };
+    // LDS slots of those elements (the same for every tile; past the tile: the spare float).
+    int kslot[KPT], vslot[VPT];
 #pragma unroll
-        for (int p = 0; p < kParts; ++p) tmax = fmaxf(tmax, red[p * kQ + qi]);
-        const float mnew = fmaxf(mx, tmax);
+    for (int i = 0; i < KPT; ++i) {
+        const int e = tid + 256 * i;
+        kslot[i] = e < kKeys * m ? (e / m) * KS + e % m : kKeys * KS;
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int e = tid + 256 * i;
+        vslot[i] = e < kKeys * dv ? (e % dv) * VS + e / dv : 64 * DVC * VS;
+    }
+    auto stage = [&](const TileRegs& r) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) Ks[kslot[i]] = r.k[i];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) Vs[vslot[i]] = r.v[i];
+    };
+
+    float o[DVC];
+#pragma unroll
+    for (int j = 0; j < DVC; ++j) o[j] = 0.0f;
+    float mx = -INFINITY, lpart = 0.0f;
+    load(ra, 0);
+    if (ntiles > 1) load(rb, 1);
+    __syncthreads();  // the zeroed key tile before it is staged over
+    stage(ra);
+    __syncthreads();
+    // Tile t from LDS; `cur` held its loads (now free), `nxt` holds tile t + 1's.
+    auto step = [&](int t, TileRegs& cur, const TileRegs& nxt) __attribute__((always_inline)) {
+        if (t + 2 < ntiles) load(cur, t + 2);
+        const int key = t * kKeys + lane;
+        float sc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < MM; ++c) sc = fmaf(qr[c], Ks[lane * KS + c], sc);
+        if (key >= N || (causal && key > q)) sc = -INFINITY;
+        const float mnew = fmaxf(mx, wave_max(sc));
         // every key so far masked (only for queries past N): nothing to add
         const bool none = mnew == -INFINITY;
         const float corr = none ? 1.0f : expf(mx - mnew);  // 0 on the first contributing tile
-        lpart *= corr;
-#pragma unroll
-        for (int jj = 0; jj < kKP; ++jj) {
-            const float p = none ? 0.0f : expf(s[jj] - mnew);
-            lpart += p;
-            Ps[(part * kKP + jj) * kQ + qi] = p;
-        }
+        const float p = none ? 0.0f : expf(sc - mnew);
+        lpart = fmaf(lpart, corr, p);
         mx = mnew;
 #pragma unroll
-        for (int i = 0; i < kOC; ++i) o[i] *= corr;
-        __syncthreads();
-        if (c0 < dv) {
-#pragma unroll 4
-            for (int j = 0; j < kKeys; ++j) {
-                const float p = Ps[j * kQ + qi];
+        for (int j = 0; j < DVC; ++j) o[j] *= corr;
+        const float* vrow[DVC];
 #pragma unroll
-                for (int i = 0; i < kOC; i += 4) {
-                    const float4 v4 = *reinterpret_cast<const float4*>(&Vs[j * kMaxDv + c0 + i]);
-                    o[i] = fmaf(p, v4.x, o[i]);
-                    o[i + 1] = fmaf(p, v4.y, o[i + 1]);
-                    o[i + 2] = fmaf(p, v4.z, o[i + 2]);
-                    o[i + 3] = fmaf(p, v4.w, o[i + 3]);
-                }
+        for (int j = 0; j < DVC; ++j) vrow[j] = Vs + (lane + 64 * j) * VS;
+#pragma unroll 4
+        for (int k = 0; k < kKeys; k += 4) {
+            float pk[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                pk[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), k + u));
+#pragma unroll
+            for (int j = 0; j < DVC; ++j) {
+                const float4 v4 = *reinterpret_cast<const float4*>(vrow[j] + k);
+                o[j] = fmaf(pk[0], v4.x, o[j]);
+                o[j] = fmaf(pk[1], v4.y, o[j]);
+                o[j] = fmaf(pk[2], v4.z, o[j]);
+                o[j] = fmaf(pk[3], v4.w, o[j]);
             }
         }
+        if (t + 1 < ntiles) {
+            __syncthreads();  // every wave is done with this tile
+            stage(nxt);
+            __syncthreads();
+        }
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, ra, rb);
+        if (t + 1 < ntiles) step(t + 1, rb, ra);
     }
-    __syncthreads();
-    red[part * kQ + qi] = lpart;
-    __syncthreads();
-    float l = 0.0f;
-#pragma unroll
-    for (int p = 0; p < kParts; ++p) l += red[p * kQ + qi];
+    const float l = wave_sum(lpart);
     if (q >= N) return;
     const float inv = 1.0f / l;
 #pragma unroll
-    for (int i = 0; i < kOC; ++i)
-        if (c0 + i < dv) O[((size_t)bh * N + q) * dv + c0 + i] = o[i] * inv;
-    if (lse && part == 0) lse[(size_t)bh * N + q] = mx + logf(l);
+    for (int j = 0; j < DVC; ++j)
+        if (lane + 64 * j < dv) O[((size_t)bh * N + q) * dv + lane + 64 * j] = o[j] * inv;
+    if (lse && lane == 0) lse[(size_t)bh * N + q] = mx + logf(l);
 }
 
 }  // namespace
@@ -175,15 +213,19 @@ hipError_t launch_attn_f32(const float* Qt, const float* Kt, const float* V, flo
                            float* lse, int BH, int N, int m, int dv, bool causal, float scale,
                            hipStream_t stream) {
     if (dv > kMaxDv) return hipErrorInvalidValue;
-    const long long blocks = (long long)((N + kQ - 1) / kQ) * BH;
+    const long long blocks = (long long)((N + kQW - 1) / kQW) * BH;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
     const int c = causal ? 1 : 0;
-    if (m <= 16) attn_f32_kernel<16><<<grid, 256, 0, stream>>>(Qt, Kt, V, O, lse, N, m, dv, c, scale);
-    else if (m <= 32) attn_f32_kernel<32><<<grid, 256, 0, stream>>>(Qt, Kt, V, O, lse, N, m, dv, c, scale);
-    else if (m <= 64) attn_f32_kernel<64><<<grid, 256, 0, stream>>>(Qt, Kt, V, O, lse, N, m, dv, c, scale);
-    else if (m <= 128) attn_f32_kernel<128><<<grid, 256, 0, stream>>>(Qt, Kt, V, O, lse, N, m, dv, c, scale);
+#define SPA_F32_LAUNCH(MMV)                                                                  \
+    (dv <= 64 ? (attn_f32_kernel<MMV, 1><<<grid, 256, 0, stream>>>(Qt, Kt, V, O, lse, N, m, dv, c, scale), 0) \
+              : (attn_f32_kernel<MMV, 2><<<grid, 256, 0, stream>>>(Qt, Kt, V, O, lse, N, m, dv, c, scale), 0))
+    if (m <= 16) (void)SPA_F32_LAUNCH(16);
+    else if (m <= 32) (void)SPA_F32_LAUNCH(32);
+    else if (m <= 64) (void)SPA_F32_LAUNCH(64);
+    else if (m <= 128) (void)SPA_F32_LAUNCH(128);
     else return hipErrorInvalidValue;
+#undef SPA_F32_LAUNCH
     return hipGetLastError();
 }
 
