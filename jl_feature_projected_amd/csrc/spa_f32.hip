@@ -93,27 +93,30 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float* __restrict__
     // memory; thread tid loads elements tid, tid + 256, ... of each into registers.
     const int kend = causal ? min(N, q0 + kQW) : N;
     const int ntiles = (kend + kKeys - 1) / kKeys;
-    // Buffer resources over the head's rows: loads past its end read as zero, with no branch.
-    const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, N * m * 4, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, N * dv * 4, 0x00020000);
     // Two register sets of tile loads: the loads of tile t + 2 go out while tile t is
     // computed, and tile t + 1 is staged from the other set after it.
     struct TileRegs {
         float k[KPT], v[VPT];
     };
     TileRegs ra, rb;
+    // Buffer resources from the tile's first row to the head's end: loads past it read as
+    // zero, with no branch (at most N * 128 * 4 <= 2^31 bytes, a 32-bit record count).
     auto load = [&](TileRegs& r, int t) __attribute__((always_inline)) {
-        const int kb = t * kKeys * m * 4, vb = t * kKeys * dv * 4;  // byte offsets of the tile
+        const int r0 = t * kKeys;
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Kh + (size_t)r0 * m), (short)0, (int)((unsigned)(N - r0) * (unsigned)m * 4u),
+            0x00020000);
+        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(Vh + (size_t)r0 * dv), (short)0, (int)((unsigned)(N - r0) * (unsigned)dv * 4u),
+            0x00020000);
 #pragma unroll
         for (int i = 0; i < KPT; ++i)
             r.k[i] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(krs, 4 * (tid + 256 * i), kb, 0));
+                float, __builtin_amdgcn_raw_buffer_load_b32(krs, 4 * (tid + 256 * i), 0, 0));
 #pragma unroll
         for (int i = 0; i < VPT; ++i)
             r.v[i] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(vrs, 4 * (tid + 256 * i), vb, 0));
+                float, __builtin_amdgcn_raw_buffer_load_b32(vrs, 4 * (tid + 256 * i), 0, 0));
     };
     // LDS slots of those elements (the same for every tile; past the tile: the spare float).
     int kslot[KPT], vslot[VPT];
