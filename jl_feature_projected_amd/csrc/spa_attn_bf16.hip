@@ -114,12 +114,29 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
     // Workgroup -> (head, query block). Workgroups are handed to the 8 XCDs round-robin;
     // when the grid divides evenly, XCD x gets a contiguous range of (head, block) pairs so
     // a head's projected keys and values stay in one XCD's L2. Causal blocks run heaviest
-    // (last) first.
+    // (last) first: head by head, or, when the range is whole heads whose keys and values
+    // fit in the XCD's L2 together, across those heads (every head's heaviest block, then
+    // every head's next one, ...), which balances the CUs' loads better.
     const int total = gridDim.x;
     int li = blockIdx.x;
-    if ((total & 7) == 0) li = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-    const int bh = li / nqb;
-    const int qbi = li - bh * nqb;
+    int bh, qbi;
+    if ((total & 7) == 0) {
+        const int per_xcd = total >> 3, x = blockIdx.x & 7, j = blockIdx.x >> 3;
+        const int hpx = per_xcd / nqb;  // whole heads per XCD (0: not whole heads)
+        constexpr long long kRowBytes = MP * 2 + DV * 2;  // projected key + value row
+        if (CAUSAL && hpx > 0 && hpx * nqb == per_xcd &&
+            (long long)hpx * N * kRowBytes <= (3ll << 20)) {
+            bh = x * hpx + j % hpx;
+            qbi = j / hpx;
+        } else {
+            li = x * per_xcd + j;
+            bh = li / nqb;
+            qbi = li - bh * nqb;
+        }
+    } else {
+        bh = li / nqb;
+        qbi = li - bh * nqb;
+    }
     const int qb_ = CAUSAL ? (nqb - 1 - qbi) : qbi;
     const int q0 = qb_ * kBR;
 
