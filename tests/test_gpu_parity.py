@@ -337,6 +337,34 @@ def test_identity_values_expose_the_weights(dev, oracle_mod, N, causal):
         assert float(O.triu(1).abs().max()) == 0.0  # masked weights are exactly zero
 
 
+def test_longest_supported_sequence(dev, oracle_mod):
+    """N = 2^22, the largest sequence the library accepts, as one causal head in the
+    benchmark's layout (d = 128, m = 32, dv = 128): rows at the first and last tiles, the
+    256-query block edges and the middle, plus random rows, against the oracle; every output
+    finite; row 0 sees only key 0. Buffer sizes reach 2^30 bytes per tensor here, so 32-bit
+    offset arithmetic anywhere on the path would show."""
+    N = 1 << 22
+    w = inputs.Workload("longest-n4194304-d128-m32-causal", 1, 1, N, 128, 32, 128, True,
+                        seed=4242)
+    note(f"{w.name}: drawing inputs")
+    x = inputs.draw(w)
+    note(f"{w.name}: GPU run")
+    O, lse = run(x, dev, return_lse=True)
+    assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(lse).all())
+    v0 = x.V[0, 0, 0].float().to(dev)
+    assert torch.all(torch.abs(O[0, 0, 0] - v0) <= 2.0 ** -22 * torch.abs(v0))
+    rng = np.random.default_rng(9)
+    rows = sorted(set([0, 1, 63, 64, 255, 256, 257, N // 2, N - 257, N - 256, N - 65, N - 2,
+                       N - 1] + rng.integers(0, N, 5).tolist()))
+    bh = np.zeros(len(rows), dtype=np.int64)
+    ri = np.array(rows, dtype=np.int64)
+    note(f"{w.name}: oracle on {len(rows)} rows")
+    Or, lr = oracle_mod.attn_rows(x.Q, x.K, x.V, x.P, w.scale, True, bh, ri, with_lse=True)
+    Og = O[0, 0][torch.from_numpy(ri).to(dev)]
+    assert_bf16_close(np64(Og), Or, what=w.name)
+    assert np.max(np.abs(np64(lse[0, 0][torch.from_numpy(ri).to(dev)]) - lr)) <= TOL_BF16
+
+
 def test_large_magnitude_inputs(dev, oracle_mod):
     """Keys 1000x longer and queries 1000x shorter: the projected keys reach the
     thousands (inside fp16, whose largest finite value is 65504, the limit the library
