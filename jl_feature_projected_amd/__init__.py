@@ -442,3 +442,47 @@ def profile_end() -> tuple[float, float, int]:
     p, a, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
     check(lib().spa_profile_end(ctypes.byref(p), ctypes.byref(a), ctypes.byref(n)))
     return p.value, a.value, n.value
+
+
+_attention_fn = None
+
+
+def _attention_function():
+    """The torch.autograd.Function over spa_attn_fwd / spa_attn_bwd (built on first use, so
+    importing this module does not import torch)."""
+    global _attention_fn
+    if _attention_fn is not None:
+        return _attention_fn
+    torch = _torch()
+
+    class SpaAttentionFunction(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, Q, K, V, P, scale, causal):
+            O, lse = spa_attn_fwd(Q, K, V, P, scale, causal, return_lse=True)
+            ctx.save_for_backward(Q, K, V, P, O, lse)
+            ctx.scale, ctx.causal = scale, causal
+            return O
+
+        @staticmethod
+        def backward(ctx, dO):
+            Q, K, V, P, O, lse = ctx.saved_tensors
+            # autograd may hand over a strided view (the expanded ones of a plain sum); the
+            # library reads dense rows
+            dO = dO.contiguous()
+            dQ, dK, dV, dP = spa_attn_bwd(Q, K, V, P, O, dO, lse, ctx.scale, ctx.causal,
+                                          grad_dtype=Q.dtype)
+            return dQ, dK, dV, dP, None, None
+
+    _attention_fn = SpaAttentionFunction
+    return _attention_fn
+
+
+def spa_attention(Q, K, V, P, scale: float | None = None, causal: bool = False):
+    """O = spa_attn_fwd(Q, K, V, P, scale, causal) recorded for autograd: the backward runs
+    spa_attn_bwd from the saved inputs, output and log-sum-exp, so Q, K, V and the projection
+    P (trained by its gradient as in SPA, Sec. 3.4.1 Gradient Flow and Algorithm 2) all
+    receive gradients. dQ, dK and dV come out of the library in the inputs' dtype; dP comes
+    out in fp32 and autograd casts it to P's dtype. O is in the inputs' dtype."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(Q.shape[-1])
+    return _attention_function().apply(Q, K, V, P, float(scale), bool(causal))
