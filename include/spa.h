@@ -26,7 +26,11 @@
  *   - Errors are reported only through the returned status; nothing aborts or throws.
  *     Arguments are validated on the host before any HIP call, so an invalid call touches
  *     neither the device nor the stream. spa_last_error() gives a readable reason.
- *   - Non-finite values in the tensors are not checked; they propagate to the outputs.
+ *   - Non-finite values in the tensors are not checked; they propagate to the outputs. In the
+ *     forward, a NaN in a query row reaches that output row (and its lse) only, and a NaN in
+ *     a key row only the rows whose scores include that key; every other row is unchanged.
+ *     A non-finite value of V also reaches rows of its 64-key tile that the causal mask
+ *     excludes (their zero weights meet it in the products).
  *   - The library is reentrant. Concurrent calls must use distinct outputs and workspaces.
  */
 #ifndef SPA_H

@@ -1048,7 +1048,10 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void attn_bf16_kernel(
             const float l0 = __shfl(lacc[b][0], src, 64), l1 = __shfl(lacc[b][1], src, 64);
             ltot[b] += col < 16 ? l0 : l1;
         }
-        low = low || (myq[b] < N && ltot[b] < 0x1p-64f);
+        // A NaN normaliser takes the exact path too: the matrix-core sum multiplies the
+        // weights of the query 16 rows away by zero, so a NaN score (from a NaN input) would
+        // reach that query's normaliser as well; the exact path sums every row on its own.
+        low = low || (myq[b] < N && !(ltot[b] >= 0x1p-64f));
     }
     if (__syncthreads_or(low)) {
         const float zero[QB] = {};

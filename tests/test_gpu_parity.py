@@ -382,6 +382,42 @@ def test_large_magnitude_inputs(dev, oracle_mod):
     assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
 
 
+# A NaN in a query row reaches only that row; a NaN in a key row only the rows whose scores
+# include that key (every row without the mask, rows from that key on with it). The score
+# bound ignores it (the key-norm maxima and the offset are maxima that skip NaN), so no
+# other row changes. Small shapes (two waves per SIMD) and 512 workgroups of 256 queries
+# (one wave per SIMD, two queries per lane sharing an offset).
+NAN_CASES = [  # B, H, N, d, m, dv, causal
+    (1, 4, 300, 128, 32, 128, True),
+    (1, 4, 300, 64, 16, 64, False),
+    (1, 128, 1024, 128, 32, 128, True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,m,dv,causal", NAN_CASES)
+def test_nan_inputs_reach_only_their_rows(dev, oracle_mod, B, H, N, d, m, dv, causal):
+    w = inputs.Workload(f"nan-b{B}h{H}-n{N}", B, H, N, d, m, dv, causal, seed=2700 + H)
+    x = inputs.draw(w)
+    note(w.name)
+    Q, K = x.Q.clone(), x.K.clone()
+    kj, qi = N * 2 // 3, N // 4
+    K[0, 1, kj, 5] = float("nan")
+    Q[0, 2, qi, 3] = float("nan")
+    x = inputs.Inputs(w, Q, K, x.V, x.P)
+    O, lse = run(x, dev, return_lse=True)
+    Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, causal, with_lse=True)
+    nan_rows = np.zeros((B, H, N), dtype=bool)
+    nan_rows[0, 1, kj if causal else 0:] = True
+    nan_rows[0, 2, qi] = True
+    On, ln = np64(O), np64(lse)
+    assert np.array_equal(np.isnan(Or).all(axis=-1), nan_rows)  # the oracle agrees
+    assert np.array_equal(np.isnan(On).all(axis=-1), nan_rows)
+    assert np.array_equal(np.isnan(ln), nan_rows)
+    assert np.isfinite(On[~nan_rows]).all() and np.isfinite(ln[~nan_rows]).all()
+    assert_bf16_close(On[~nan_rows], Or[~nan_rows], what=w.name)
+    assert np.max(np.abs(ln[~nan_rows] - lr[~nan_rows])) <= TOL_BF16
+
+
 def test_identity_projection_matches_exact_attention(dev):
     """m = d with P = I: the path computes exact softmax(Q K^T / sqrt(d)) V."""
     w = inputs.WORKLOADS["c5_identity"].replace(H=2, N=1500)
