@@ -113,28 +113,40 @@ def time_backward(w, x, Q, K, V, P, steps, warmup, dev) -> dict:
     ws = torch.empty(spa.spa_attn_bwd_workspace_bytes(w.B, w.H, w.N, w.d, w.m, w.dv, Q.dtype),
                      dtype=torch.uint8, device=dev)
 
-    def bstep():
-        spa.spa_attn_bwd(Q, K, V, P, O, dO, lse, w.scale, w.causal, workspace=ws)
+    def timed(grad_dtype) -> float:
+        def bstep():
+            spa.spa_attn_bwd(Q, K, V, P, O, dO, lse, w.scale, w.causal, grad_dtype=grad_dtype,
+                             workspace=ws)
 
-    for _ in range(warmup):
-        bstep()
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        bstep()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+        for _ in range(warmup):
+            bstep()
+        stream = torch.cuda.current_stream(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            bstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
     bw = accounting.bwd_work(w.B, w.H, w.N, w.d, w.m, w.dv, w.causal)
-    tf = bw.total_flops / (ms * 1e-3) / 1e12
     peak = accounting.PEAK_FP32_VECTOR_TFLOPS if f32 else accounting.PEAK_BF16_DENSE_TFLOPS
-    return {"ms_per_call": round(ms, 5), "value": round(tf, 3), "unit": "TFLOP/s",
-            "dtype": "f32" if f32 else "bf16",
-            "pct_of_peak": round(100.0 * tf / peak, 2),
-            "peak": peak, "flops_per_call": bw.total_flops,
-            "executed_n2_flops_per_call": bw.executed_n2_flops, "grad_dtype": "f32"}
+    ms = timed(torch.float32)
+    tf = bw.total_flops / (ms * 1e-3) / 1e12
+    res = {"ms_per_call": round(ms, 5), "value": round(tf, 3), "unit": "TFLOP/s",
+           "dtype": "f32" if f32 else "bf16",
+           "pct_of_peak": round(100.0 * tf / peak, 2),
+           "peak": peak, "flops_per_call": bw.total_flops,
+           "executed_n2_flops_per_call": bw.executed_n2_flops, "grad_dtype": "f32"}
+    if not f32:
+        # the same calls writing dQ, dK and dV in bf16, the inputs' dtype (what spa_attention
+        # hands to autograd); the arithmetic is the same, only the stores are narrower
+        ms16 = timed(torch.bfloat16)
+        tf16 = bw.total_flops / (ms16 * 1e-3) / 1e12
+        res["bf16_grads"] = {"ms_per_call": round(ms16, 5), "value": round(tf16, 3),
+                             "pct_of_peak": round(100.0 * tf16 / peak, 2)}
+    return res
 
 
 def time_decode(w, x, P, steps, warmup, dev, nq: int = 1) -> dict:
