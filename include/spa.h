@@ -143,6 +143,11 @@ int spa_attn_fwd_plan(int B, int H, int N, int d, int m, int dv, spa_dtype_t dty
  * normaliser sums those rounded weights). Each row's exponent offset is the Cauchy-Schwarz
  * bound |q| * max |k| rather than a running maximum; rows for which that bound is so loose
  * that the normaliser would fall below 2^-64 are recomputed with an exact online maximum.
+ * Accuracy of the bf16 path: rounding the two projected operands to fp16 moves a score
+ * s_ij by at most 2^-10 * |scale| * sum_c |(QP)[i,c]| |(KP)[j,c]|, and an output row by at
+ * most that times max_j |V[j,:] - O[i,:]| (first order); at the magnitudes of unit-norm
+ * heads with m >= 8 the outputs stay within 2e-2 of the exact result for V entries of
+ * order one, while very small m (large projected scores) loosens it by that bound.
  * Supported: d in {64, 128}, dv in {64, 128}, 1 <= m <= 128. Input range of the bf16
  * path: every projected key entry (K P)[j,c] and every scaled projected query entry
  * scale * log2(e) * (Q P)[i,c] must lie inside the fp16 range, |x| <= 65504 (bf16 inputs of

@@ -233,6 +233,83 @@ def test_fp32_path_other_shapes(dev, oracle_mod, N, m, dv, causal):
     assert np.max(np.abs(np64(lse) - lr)) <= TOL_F32_REL * max(1.0, np.max(np.abs(lr)))
 
 
+# ---- seeded random shapes ------------------------------------------------------------------
+# Shapes drawn once from a fixed generator (the list is the same on every run): batch,
+# heads, ragged N up to 1500, m from 8 to 128 on the bf16 path (smaller m below) and from 1
+# on the fp32 path (also above d), both masks, both output dtypes on the bf16 path and
+# arbitrary d, dv on the fp32 path; plus two grids of 512 or
+# more 256-query workgroups with m <= 32, which take the one-wave variant. Every output and
+# the lse against the oracle.
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        f32 = i % 4 == 3
+        d = int(rng.integers(1, 257)) if f32 else int(rng.choice([64, 128]))
+        dv = int(rng.integers(1, 129)) if f32 else int(rng.choice([64, 128]))
+        out.append((int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 1501)),
+                    d, int(rng.integers(1 if f32 else 8, 129)), dv, bool(rng.integers(0, 2)),
+                    "f32" if f32 else "bf16", bool(rng.integers(0, 2))))
+    for causal in (False, True):
+        out.append((1, 128, int(rng.integers(1025, 1300)), int(rng.choice([64, 128])),
+                    int(rng.integers(1, 33)), int(rng.choice([64, 128])), causal, "bf16",
+                    bool(rng.integers(0, 2))))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(24, 20261202)
+
+
+@pytest.mark.parametrize("shape", RANDOM_SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_random_shapes(dev, oracle_mod, shape):
+    B, H, N, d, m, dv, causal, dt, out_bf16 = shape
+    w = inputs.Workload(f"random-{'-'.join(map(str, shape))}", B, H, N, d, m, dv, causal,
+                        dtype=dt, seed=7000 + RANDOM_SHAPES.index(shape))
+    x = inputs.draw(w)
+    note(w.name)
+    odt = torch.bfloat16 if (dt == "bf16" and out_bf16) else torch.float32
+    O, lse = run(x, dev, out_dtype=odt, return_lse=True)
+    Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, causal, with_lse=True)
+    if dt == "f32":
+        assert np.max(np.abs(np64(O) - Or)) / np.max(np.abs(Or)) <= TOL_F32_REL
+        assert np.max(np.abs(np64(lse) - lr)) <= TOL_F32_REL * max(1.0, np.max(np.abs(lr)))
+    else:
+        assert_bf16_close(np64(O), Or, out_bf16=out_bf16, what=w.name)
+        assert np.max(np.abs(np64(lse) - lr)) <= TOL_BF16
+
+
+# Very few projected features (m = 1 .. 3 with N(0, 1/m) entries) make the projected scores
+# several times larger than at the workloads' m, and the bf16 path's error grows with them:
+# the fp16 rounding of both projected operands moves a score s_ij by at most
+# 2^-10 * scale * sum_c |q~_ic| |k~_jc|, and a score perturbation delta moves output row i by
+# at most max_j |delta_ij| * max_j |v_j - O_i| <= max_j |delta_ij| * 2 max |V| (first order).
+# Each row is held to 2e-2 plus that bound.
+@pytest.mark.parametrize("m", [1, 2, 3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_few_features_within_operand_rounding_bound(dev, oracle_mod, m, causal):
+    w = inputs.Workload(f"few-features-m{m}", 2, 2, 700, 64, m, 128, causal, seed=7400 + m)
+    x = inputs.draw(w)
+    note(w.name)
+    O, lse = run(x, dev, out_dtype=torch.bfloat16, return_lse=True)
+    Or, lr = oracle_mod.attn_fwd(x.Q, x.K, x.V, x.P, w.scale, causal, with_lse=True)
+    Q, K, V, P = x.f64("Q"), x.f64("K"), x.f64("V"), x.f64("P")
+    aq = np.abs(np.einsum("bhnd,hdm->bhnm", Q, P))
+    ak = np.abs(np.einsum("bhnd,hdm->bhnm", K, P))
+    S = abs(w.scale) * aq @ ak.swapaxes(-1, -2)  # [B,H,N,N]: sum_c |q~_ic| |k~_jc|
+    if causal:
+        S = np.where(np.tril(np.ones((w.N, w.N), dtype=bool)), S, 0.0)
+    vmax = np.abs(V).max(axis=(-2, -1), keepdims=True)  # [B,H,1,1]
+    allow = TOL_BF16 + 2.0 ** -10 * S.max(axis=-1, keepdims=True) * 2.0 * vmax
+    err = np.abs(np64(O) - Or)
+    allow = allow + bf16_half_ulp(Or)
+    note(f"{w.name}: max-abs {err.max():.3e}, largest share of its row's allowance "
+         f"{(err / allow).max():.2f}")
+    assert np.all(err <= allow)
+    # lse carries the score scale itself: 2e-2 plus the rounding bound of its largest score
+    lallow = TOL_BF16 + 2.0 ** -10 * S.max(axis=-1)
+    assert np.all(np.abs(np64(lse) - lr) <= lallow)
+
+
 # ---- full-size workloads: stratified row samples ----------------------------------------
 
 FULL = {  # workload -> (random rows per head, heads compared in full)
